@@ -39,7 +39,13 @@ from .nf4_dq import f64_from_bf16_bits
 
 
 def lora_scale(alpha: float, r: int) -> float:
-    """s = fp32(alpha / r) as a Python float."""
+    """s = fp32(alpha / r) as a Python float.
+
+    Rank 0 means there is no adapter at all, so its (empty) term contributes
+    nothing; s is then 0 rather than alpha / 0.
+    """
+    if r == 0:
+        return 0.0
     return float(np.float32(alpha) / np.float32(r))
 
 

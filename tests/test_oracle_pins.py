@@ -350,6 +350,18 @@ def test_forward_equals_merged_weight():
     assert np.max(np.abs(Y - Ym)) <= 1e-12 * np.max(np.abs(Ym))
 
 
+def test_forward_rank_zero_is_plain_product():
+    W, X, _, _, dY = _tiny(M=3, N=4, K=64, r=1)
+    A0 = np.zeros((0, 64))
+    B0 = np.zeros((4, 0))
+    Y, U = oracle.linear_fwd(W, X, A0, B0, 16.0, 0)
+    assert U.shape == (3, 0)
+    np.testing.assert_array_equal(Y, X @ W.T)
+    dX, dA, dB = oracle.linear_bwd(W, X, dY, A0, B0, 16.0, 0)
+    np.testing.assert_array_equal(dX, dY @ W)
+    assert dA.shape == (0, 64) and dB.shape == (4, 0)
+
+
 def test_forward_adapter_term_scales_with_alpha():
     W, X, A, B, _ = _tiny()
     Y0, _ = oracle.linear_fwd(W, X, A, np.zeros_like(B), 4.0, 2)
