@@ -1,0 +1,101 @@
+// NF4 + double-quantization codec kernels ([P1] "The mechanism in brief";
+// [P4] "NF4 and double quantisation").
+//
+// Quantize: one 256-thread workgroup per group of 256 blocks.  A wave takes
+// one 64-weight block at a time (one weight per lane): absmax by a wave
+// max-reduction, x = w / absmax (IEEE fp32 division), code = number of
+// decision thresholds below x (the nearest level, exact ties to the lower
+// level), two codes per byte.  The block absmaxes stay in LDS; the group max
+// gives the fp32 step s2 = max / 255 and each block's 8-bit code
+// q8 = round-half-even(absmax / s2).  No workspace.
+//
+// Dequant: a streaming decode, 8 weights (one code dword -> 16 bytes of bf16)
+// per thread per iteration; HBM-bound (2.516 bytes moved per weight).
+#include <algorithm>
+
+#include "common.h"
+
+namespace qlora {
+namespace {
+
+__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, uint32_t nb,
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ q8,
+                                                  float* __restrict__ s2, Nf4Consts c) {
+  __shared__ float s_amax[kGroup];
+  __shared__ float s_red[4];
+  const uint32_t g = blockIdx.x, b0 = g * kGroup;
+  const uint32_t nblk = min((uint32_t)kGroup, nb - b0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  for (uint32_t bl = wave; bl < (uint32_t)kGroup; bl += 4) {
+    float am = 0.f;
+    if (bl < nblk) {
+      const uint32_t b = b0 + bl;
+      const float w = W[(size_t)b * kBlock + lane];
+      float m = fabsf(w);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      am = m;
+      const float x = am > 0.f ? w / am : 0.f;
+      uint32_t code = 0;
+#pragma unroll
+      for (int i = 0; i < 15; ++i) code += (x > c.thr[i]) ? 1u : 0u;
+      const uint32_t hi = __shfl_down(code, 1);
+      if ((lane & 1) == 0) codes[(size_t)b * (kBlock / 2) + (lane >> 1)] = (uint8_t)(code | (hi << 4));
+    }
+    if (lane == 0) s_amax[bl] = am;
+  }
+  __syncthreads();
+  float m = s_amax[tid];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) s_red[wave] = m;
+  __syncthreads();
+  const float gmax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  const float step = gmax / 255.0f;
+  if ((uint32_t)tid < nblk) {
+    uint32_t q = 0;
+    if (step > 0.f) {
+      const float t = rintf(s_amax[tid] / step);  // round half to even
+      q = (uint32_t)fminf(fmaxf(t, 0.f), 255.f);
+    }
+    q8[b0 + tid] = (uint8_t)q;
+  }
+  if (tid == 0) s2[g] = step;
+}
+
+__global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ codes, const uint8_t* __restrict__ q8,
+                                                 const float* __restrict__ s2, uint32_t ndw,
+                                                 uint4* __restrict__ out, Nf4Consts c) {
+  __shared__ float lv[16];
+  if (threadIdx.x < 16) lv[threadIdx.x] = c.level[threadIdx.x];
+  __syncthreads();
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < ndw; i += stride) {
+    const uint32_t d = codes[i];
+    out[i] = decode8(d, block_scale(q8, s2, i >> 3), lv);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const float* W, int64_t nweights, uint8_t* codes, uint8_t* q8, float* s2,
+                           hipStream_t st) {
+  const uint32_t nb = (uint32_t)(nweights / kBlock);
+  const uint32_t ng = (nb + kGroup - 1) / kGroup;
+  if (ng == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quantize, dim3(ng), dim3(256), 0, st, W, nb, codes, q8, s2, nf4_consts());
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* q8, const float* s2, int64_t nweights,
+                          uint16_t* out, hipStream_t st) {
+  const uint32_t ndw = (uint32_t)(nweights / 8);
+  if (ndw == 0) return hipSuccess;
+  const uint32_t blocks = std::min<uint32_t>((ndw + 255) / 256, 256u * 64u);
+  hipLaunchKernelGGL(k_dequant, dim3(blocks), dim3(256), 0, st, reinterpret_cast<const uint32_t*>(codes), q8,
+                     s2, ndw, reinterpret_cast<uint4*>(out), nf4_consts());
+  return hipGetLastError();
+}
+
+}  // namespace qlora

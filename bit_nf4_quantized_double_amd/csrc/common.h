@@ -1,0 +1,65 @@
+// Device-side types and helpers shared by the gfx950 kernels of libqlora.
+//
+// Page legend for citations in csrc/:
+//   [P1] "QLoRA, in depth: when a 4-bit base is worth it for small language
+//        models, and how to ship the result"
+//   [P4] "QLoRA and Fine-Tuning on One Consumer GPU"
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlora {
+
+constexpr int kBlock = 64;    // weights per absmax block
+constexpr int kGroup = 256;   // blocks per second-level scale
+constexpr int kMaxRank = 64;
+
+// NF4 levels and decision thresholds, built on the host and passed to every
+// codec kernel by value (kernel arguments live in SGPRs; no device globals).
+struct Nf4Consts {
+  float level[16];  // ascending NF4 levels
+  float thr[15];    // thr[i] = largest fp32 <= (level[i] + level[i+1]) / 2
+};
+
+const Nf4Consts& nf4_consts();  // host, built once
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+// Decode 8 packed NF4 codes (one dword, element 0 in the low nibble) with
+// block scale a into 4 dwords of bf16 pairs: w = bf16(level[c] * a).
+// `lv` is the 16-entry level table in LDS (16 distinct banks: conflict-free).
+__device__ __forceinline__ uint4 decode8(uint32_t d, float a, const float* lv) {
+  uint4 o;
+  o.x = pack_bf16x2(lv[d & 15u] * a, lv[(d >> 4) & 15u] * a);
+  o.y = pack_bf16x2(lv[(d >> 8) & 15u] * a, lv[(d >> 12) & 15u] * a);
+  o.z = pack_bf16x2(lv[(d >> 16) & 15u] * a, lv[(d >> 20) & 15u] * a);
+  o.w = pack_bf16x2(lv[(d >> 24) & 15u] * a, lv[d >> 28] * a);
+  return o;
+}
+
+// Block scale of block b: a' = fp32(q8[b] * s2[b / 256]).
+__device__ __forceinline__ float block_scale(const uint8_t* q8, const float* s2, uint32_t b) {
+  return (float)q8[b] * s2[b >> 8];
+}
+
+// 16-byte chunk swizzle inside a 64-element (128-byte) bf16 LDS row: keeps
+// ds_read_b128 / ds_write_b128 conflict-free for row-consecutive and for
+// 8-row-strided access patterns.
+__device__ __forceinline__ uint32_t swz(uint32_t row) { return (row ^ (row >> 3)) & 7u; }
+
+}  // namespace qlora

@@ -1,0 +1,26 @@
+// Launch arguments of the fused NF4-dequant GEMMs (see gemm.hip).
+#pragma once
+
+#include "common.h"
+
+namespace qlora {
+
+struct GemmArgs {
+  const uint16_t* act;       // X [M x R] (forward) or dY [M x R] (dX), row-major bf16
+  int64_t ld_act;            // row pitch of act in elements (= R)
+  int M;                     // rows (tokens)
+  int R;                     // reduction length: k_in (forward) or n_out (dX)
+  int C;                     // output columns: n_out (forward) or k_in (dX)
+  const uint8_t* codes;      // packed NF4 codes of W [n_out x k_in]
+  const uint8_t* q8;         // 8-bit block absmax codes
+  const float* s2;           // fp32 step per group of 256 blocks
+  int K;                     // W row length (k_in)
+  const uint16_t* lora_act;  // U~ or V~ [M x r] bf16 (unused when r == 0)
+  const uint16_t* lora_w;    // forward: B [n_out x r]; dX: A [r x k_in]
+  int r;                     // adapter rank, 0..64
+  uint16_t* out;             // Y [M x n_out] or dX [M x k_in], bf16
+  int64_t ld_out;
+  Nf4Consts nf4;
+};
+
+}  // namespace qlora

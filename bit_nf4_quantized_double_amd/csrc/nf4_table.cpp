@@ -1,0 +1,68 @@
+// Host construction of the NF4 levels and decision thresholds.
+//
+// The levels sit at quantiles of the standard normal distribution ([P1] "The
+// mechanism in brief"; [P4] "NF4 and double quantisation"): 8 positive
+// quantiles at probabilities 0.5 + (d - 0.5) * j / 8 (j = 1..8), 7 negative at
+// 0.5 + (d - 0.5) * j / 7 (j = 1..7) mirrored, and an exact zero; everything is
+// divided by the quantile at d, so the extremes are exactly -1 and +1.  The
+// tail offset d = ((1 - 1/30) + (1 - 1/32)) / 2 is not given by the pages; it
+// is the offset of the construction in the paper they cite.
+//
+// The inverse normal here is bisection on Phi(x) = erfc(-x / sqrt 2) / 2 in
+// double precision, to adjacent doubles: accurate to ~1e-15 relative, far
+// inside the smallest fp32 rounding margin of any level.
+#include <cmath>
+#include <mutex>
+
+#include "common.h"
+
+namespace qlora {
+namespace {
+
+double normal_cdf(double x) { return 0.5 * std::erfc(-x / std::sqrt(2.0)); }
+
+double normal_quantile(double p) {
+  double lo = -40.0, hi = 40.0;
+  for (int it = 0; it < 4000; ++it) {
+    double mid = 0.5 * (lo + hi);
+    if (mid <= lo || mid >= hi) break;
+    if (normal_cdf(mid) < p) lo = mid; else hi = mid;
+  }
+  double elo = std::fabs(normal_cdf(lo) - p), ehi = std::fabs(normal_cdf(hi) - p);
+  return elo < ehi ? lo : hi;
+}
+
+float round_down_f32(double x) {
+  float f = (float)x;  // round to nearest even
+  if ((double)f > x) f = std::nextafterf(f, -INFINITY);
+  return f;
+}
+
+Nf4Consts build() {
+  const double d = 0.5 * ((1.0 - 1.0 / 30.0) + (1.0 - 1.0 / 32.0));
+  const double step = d - 0.5;
+  const double top = normal_quantile(d);
+  double lv[16];
+  // ascending: 7 negatives (most negative first), zero, 8 positives
+  for (int j = 7; j >= 1; --j) lv[7 - j] = -normal_quantile(0.5 + step * (j / 7.0)) / top;
+  lv[7] = 0.0;
+  for (int j = 1; j <= 8; ++j) lv[7 + j] = normal_quantile(0.5 + step * (j / 8.0)) / top;
+  Nf4Consts c;
+  for (int i = 0; i < 16; ++i) c.level[i] = (float)lv[i];
+  for (int i = 0; i < 15; ++i) {
+    double mid = ((double)c.level[i] + (double)c.level[i + 1]) * 0.5;  // exact
+    c.thr[i] = round_down_f32(mid);
+  }
+  return c;
+}
+
+}  // namespace
+
+const Nf4Consts& nf4_consts() {
+  static std::once_flag once;
+  static Nf4Consts consts;
+  std::call_once(once, [] { consts = build(); });
+  return consts;
+}
+
+}  // namespace qlora

@@ -1,0 +1,255 @@
+"""ctypes binding over libqlora.so (the C ABI in include/qlora.h).
+
+Argument marshalling only: PyTorch supplies device memory (``data_ptr()``) and
+the current HIP stream; every step of the computation runs in the library's
+gfx950 kernels.  There is no CPU or PyTorch fallback -- a missing library, a
+CPU tensor or a wrong dtype raises.
+
+bf16 tensors are passed as their raw bits (the ABI takes uint16_t).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlora.so")
+
+QLORA_OK = 0
+QLORA_OP_FWD = 1
+QLORA_OP_BWD = 2
+MAX_RANK = 64
+
+_c_i64 = ctypes.c_int64
+_c_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+
+
+class _CWeight(ctypes.Structure):
+    _fields_ = [("n_out", _c_i64), ("k_in", _c_i64), ("codes", _vp),
+                ("absmax_q8", _vp), ("absmax_scale", _vp)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqlora.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -m bit_nf4_quantized_double_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    W = ctypes.POINTER(_CWeight)
+    sig = {
+        "qlora_quantize_nf4_dq": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
+        "qlora_dequant": (ctypes.c_int, [W, _vp, _vp]),
+        "qlora_linear_fwd": (ctypes.c_int, [W, _vp, _c_i64, _vp, _vp, _c_i32, ctypes.c_float,
+                                            _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+        "qlora_linear_bwd": (ctypes.c_int, [W, _vp, _vp, _c_i64, _vp, _vp, _c_i32, ctypes.c_float,
+                                            _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+        "qlora_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i32]),
+        "qlora_nf4_table": (None, [ctypes.POINTER(ctypes.c_float)]),
+        "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "qlora_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str) -> None:
+    if status != QLORA_OK:
+        L = lib()
+        raise RuntimeError(f"{what}: {L.qlora_status_string(status).decode()} "
+                           f"({L.qlora_last_error().decode()})")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _opt(t, dtype, name):
+    return None if t is None else _dev(t, dtype, name)
+
+
+@dataclass
+class NF4Weight:
+    """A frozen weight in NF4 with double-quantized block scales."""
+    codes: torch.Tensor         # uint8 [n_out*k_in/2]
+    absmax_q8: torch.Tensor     # uint8 [nb]
+    absmax_scale: torch.Tensor  # float32 [ng]
+    n_out: int
+    k_in: int
+
+    def _c(self) -> _CWeight:
+        return _CWeight(self.n_out, self.k_in,
+                        _dev(self.codes, torch.uint8, "codes"),
+                        _dev(self.absmax_q8, torch.uint8, "absmax_q8"),
+                        _dev(self.absmax_scale, torch.float32, "absmax_scale"))
+
+    def nbytes(self) -> int:
+        return self.codes.numel() + self.absmax_q8.numel() + 4 * self.absmax_scale.numel()
+
+
+def nf4_table() -> list:
+    buf = (ctypes.c_float * 16)()
+    lib().qlora_nf4_table(buf)
+    return list(buf)
+
+
+def workspace_bytes(op: int, M: int, n_out: int, k_in: int, r: int) -> int:
+    return int(lib().qlora_workspace_bytes(op, M, n_out, k_in, r))
+
+
+def _empty_u8(n, device):
+    # 16-byte aligned even when n == 0
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)[:n]
+
+
+def quantize(W: torch.Tensor) -> NF4Weight:
+    """fp32 [n_out, k_in] GPU tensor -> NF4Weight (codes, q8, s2)."""
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [n_out, k_in]")
+    n_out, k_in = W.shape
+    nw = n_out * k_in
+    nb = nw // 64
+    ng = (nb + 255) // 256
+    dev = W.device
+    codes = _empty_u8(nw // 2, dev)
+    q8 = _empty_u8(nb, dev)
+    s2 = torch.empty(max(ng, 4), dtype=torch.float32, device=dev)[:ng]
+    st = lib().qlora_quantize_nf4_dq(_dev(W, torch.float32, "W"), n_out, k_in, codes.data_ptr(),
+                                     q8.data_ptr(), s2.data_ptr(), _stream())
+    _check(st, "qlora_quantize_nf4_dq")
+    return NF4Weight(codes, q8, s2, n_out, k_in)
+
+
+def dequant(w: NF4Weight, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Whole weight as a bf16 [n_out, k_in] GPU tensor."""
+    if out is None:
+        out = torch.empty((w.n_out, w.k_in), dtype=torch.bfloat16, device=w.codes.device)
+    cw = w._c()
+    st = lib().qlora_dequant(ctypes.byref(cw), _dev(out, torch.bfloat16, "out"), _stream())
+    _check(st, "qlora_dequant")
+    return out
+
+
+def _ws(nbytes: int, device, ws: torch.Tensor | None):
+    if nbytes == 0:
+        return None, 0
+    if ws is not None and ws.numel() >= nbytes:
+        return ws, ws.numel()
+    t = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return t, nbytes
+
+
+def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None,
+               r: int, alpha: float, *, Y: torch.Tensor | None = None,
+               U: torch.Tensor | None = None, return_u: bool = True,
+               ws: torch.Tensor | None = None):
+    """Y = X W^T + U~ B^T with U~ = bf16((alpha/r) X A^T).  Returns (Y, U~)."""
+    M = X.shape[0]
+    dev = X.device
+    if Y is None:
+        Y = torch.empty((M, w.n_out), dtype=torch.bfloat16, device=dev)
+    if return_u and r > 0 and U is None:
+        U = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+    wsb = 0 if U is not None else workspace_bytes(QLORA_OP_FWD, M, w.n_out, w.k_in, r)
+    wst, wsn = _ws(wsb, dev, ws)
+    cw = w._c()
+    st = lib().qlora_linear_fwd(
+        ctypes.byref(cw), _dev(X, torch.bfloat16, "X"), M,
+        _opt(A, torch.bfloat16, "A"), _opt(B, torch.bfloat16, "B"), r, float(alpha),
+        _dev(Y, torch.bfloat16, "Y"), _opt(U, torch.bfloat16, "U"),
+        None if wst is None else wst.data_ptr(), wsn, _stream())
+    _check(st, "qlora_linear_fwd")
+    return Y, U
+
+
+def linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor | None,
+               B: torch.Tensor | None, r: int, alpha: float, U: torch.Tensor | None = None, *,
+               dX: torch.Tensor | None = None, dA: torch.Tensor | None = None,
+               dB: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """Returns (dX bf16 [M,K], dA fp32 [r,K], dB fp32 [N,r]); never dW."""
+    M = X.shape[0]
+    dev = X.device
+    if dX is None:
+        dX = torch.empty((M, w.k_in), dtype=torch.bfloat16, device=dev)
+    if r > 0 and dA is None:
+        dA = torch.empty((r, w.k_in), dtype=torch.float32, device=dev)
+    if r > 0 and dB is None:
+        dB = torch.empty((w.n_out, r), dtype=torch.float32, device=dev)
+    wsb = workspace_bytes(QLORA_OP_BWD, M, w.n_out, w.k_in, r)
+    wst, wsn = _ws(wsb, dev, ws)
+    cw = w._c()
+    st = lib().qlora_linear_bwd(
+        ctypes.byref(cw), _dev(X, torch.bfloat16, "X"), _dev(dY, torch.bfloat16, "dY"), M,
+        _opt(A, torch.bfloat16, "A"), _opt(B, torch.bfloat16, "B"), r, float(alpha),
+        _opt(U, torch.bfloat16, "U"), _dev(dX, torch.bfloat16, "dX"),
+        _opt(dA, torch.float32, "dA"), _opt(dB, torch.float32, "dB"),
+        None if wst is None else wst.data_ptr(), wsn, _stream())
+    _check(st, "qlora_linear_bwd")
+    return dX, dA, dB
+
+
+class QLoRALinearFunction(torch.autograd.Function):
+    """Autograd wrapper: forward saves U~ for the backward; no grad for W."""
+
+    @staticmethod
+    def forward(ctx, X, A, B, w: NF4Weight, r: int, alpha: float):
+        X2 = X.reshape(-1, w.k_in).contiguous()
+        Y, U = linear_fwd(w, X2, A, B, r, alpha)
+        ctx.save_for_backward(X2, A, B, U)
+        ctx.w, ctx.r, ctx.alpha, ctx.xshape = w, r, alpha, X.shape
+        return Y.reshape(*X.shape[:-1], w.n_out)
+
+    @staticmethod
+    def backward(ctx, dY):
+        X2, A, B, U = ctx.saved_tensors
+        dY2 = dY.reshape(-1, ctx.w.n_out).contiguous().to(torch.bfloat16)
+        dX, dA, dB = linear_bwd(ctx.w, X2, dY2, A, B, ctx.r, ctx.alpha, U)
+        gA = dA.to(A.dtype) if (A is not None and ctx.needs_input_grad[1]) else None
+        gB = dB.to(B.dtype) if (B is not None and ctx.needs_input_grad[2]) else None
+        return dX.reshape(ctx.xshape), gA, gB, None, None, None
+
+
+class QLoRALinear(torch.nn.Module):
+    """nn.Linear replacement: frozen NF4 weight + trainable bf16 adapter."""
+
+    def __init__(self, weight_fp32: torch.Tensor, r: int = 16, alpha: float = 32.0,
+                 A: torch.Tensor | None = None, B: torch.Tensor | None = None):
+        super().__init__()
+        n_out, k_in = weight_fp32.shape
+        self.w = quantize(weight_fp32.contiguous())
+        self.r, self.alpha = r, float(alpha)
+        dev = weight_fp32.device
+        if A is None:
+            A = torch.randn(r, k_in, device=dev) / (k_in ** 0.5)
+        if B is None:
+            B = torch.zeros(n_out, r, device=dev)
+        self.A = torch.nn.Parameter(A.to(torch.bfloat16).contiguous())
+        self.B = torch.nn.Parameter(B.to(torch.bfloat16).contiguous())
+
+    def forward(self, X):
+        return QLoRALinearFunction.apply(X, self.A, self.B, self.w, self.r, self.alpha)

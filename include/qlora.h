@@ -1,0 +1,176 @@
+/*
+ * qlora.h -- C ABI of the MI355X (gfx950) NF4 double-quantized QLoRA linear.
+ *
+ * Page legend for the citations below:
+ *   [P1] "QLoRA, in depth: when a 4-bit base is worth it for small language
+ *        models, and how to ship the result"
+ *   [P2] "What is QLoRA, and how does 4-bit training make consumer-hardware
+ *        fine-tuning possible?"
+ *   [P4] "QLoRA and Fine-Tuning on One Consumer GPU"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Device pointers unless stated otherwise; all buffers are caller-owned.
+ *   The library never allocates, frees or retains memory.
+ * - Row-major storage.  bf16 values are passed as their uint16_t bit
+ *   patterns.
+ * - W is the frozen weight in nn.Linear layout: n_out rows by k_in columns.
+ *   k_in must be a multiple of 64 (a block never straddles a row) and n_out
+ *   a multiple of 8 (16-byte aligned rows of Y and dY).
+ * - Every device pointer must be 16-byte aligned.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *   the call returns without waiting for it.  Nothing is synchronised.  Calls
+ *   are re-entrant: no state is written between calls (the NF4 table is
+ *   computed once on the host under std::call_once and passed to kernels by
+ *   value).
+ * - Inputs are never written.  Outputs are fully overwritten (never
+ *   accumulated into).
+ * - Return value: QLORA_OK or a negative status; qlora_last_error() gives a
+ *   thread-local message for the most recent failure on the calling thread.
+ *   Arguments are checked on the host before anything is enqueued, so an
+ *   argument error leaves every buffer untouched.
+ *
+ * Stored weight format (NF4 with double-quantized block scales; [P1] "The
+ * mechanism in brief", [P2] "The three QLoRA ideas", [P4] "NF4 and double
+ * quantisation"):
+ *   nw = n_out*k_in weights, nb = nw/64 blocks, ng = ceil(nb/256) groups,
+ *   flattened row-major.
+ *   codes        uint8[nw/2]  two 4-bit level indices per byte; element 2j in
+ *                              the low nibble, 2j+1 in the high nibble.
+ *   absmax_q8    uint8[nb]     8-bit code of each block's absmax.
+ *   absmax_scale float[ng]     fp32 step of the 8-bit absmax code for each
+ *                              group of 256 consecutive blocks.
+ *   Decode: a' = fp32(q8[b] * s2[b/256]);  w = fp32(T[code] * a');
+ *           W_bf16 = round-to-nearest-even bf16 of w.
+ *   T is the 16-level NF4 table from qlora_nf4_table().
+ *   Cost: 4 + 8/64 + 32/16384 = 4.126953125 bits per weight.
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  QLORA_OK = 0,
+  QLORA_ERR_INVALID_ARG = -1, /* NULL required pointer, negative size, r < 0 */
+  QLORA_ERR_SHAPE = -2,       /* k_in % 64 != 0, n_out % 8 != 0, r > 64, size overflow */
+  QLORA_ERR_ALIGN = -3,       /* a device pointer not 16-byte aligned */
+  QLORA_ERR_WORKSPACE = -4,   /* workspace pointer NULL or ws_bytes too small */
+  QLORA_ERR_HIP = -5          /* a HIP launch or runtime error */
+};
+
+/* Largest adapter rank the kernels accept (the pages use 8 to 32). */
+#define QLORA_MAX_RANK 64
+
+/* Operation ids for qlora_workspace_bytes. */
+enum { QLORA_OP_FWD = 1, QLORA_OP_BWD = 2 };
+
+/* The frozen weight: borrowed device pointers, never written. */
+typedef struct {
+  int64_t n_out;              /* rows of W (output features) */
+  int64_t k_in;               /* columns of W (input features), % 64 == 0 */
+  const uint8_t *codes;       /* [n_out*k_in/2] */
+  const uint8_t *absmax_q8;   /* [n_out*k_in/64] */
+  const float *absmax_scale;  /* [ceil(n_out*k_in/64/256)] */
+} qlora_nf4_weight;
+
+/*
+ * Quantize an fp32 weight into the stored format above
+ * ([P1] "The mechanism in brief"; [P4] "NF4 and double quantisation").
+ *   W            device fp32 [n_out, k_in], read only.
+ *   codes        device uint8 [n_out*k_in/2], written.
+ *   absmax_q8    device uint8 [nb], written.
+ *   absmax_scale device fp32 [ng], written.
+ * Per block of 64: a = max|w| (fp32); x = fp32(w / a) (IEEE division;
+ * a == 0 gives x = 0); code = nearest NF4 level to x, exact ties to the lower
+ * level.  Codes use the fp32 absmax before double quantization.
+ * Per group of 256 blocks (the last one may be partial): s2 = fp32(max a / 255);
+ * q8 = round-half-even(fp32(a / s2)) clamped to [0, 255]; a zero group gives
+ * s2 = 0 and q8 = 0.  Non-finite weights give unspecified codes.
+ * Needs no workspace.  n_out == 0 is a no-op.
+ */
+int qlora_quantize_nf4_dq(const float *W, int64_t n_out, int64_t k_in,
+                          uint8_t *codes, uint8_t *absmax_q8, float *absmax_scale,
+                          hipStream_t stream);
+
+/*
+ * Dequantize the whole weight to bf16 ([P1] "The mechanism in brief": the
+ * layer dequantizes W to the compute dtype, usually bf16).
+ *   W_bf16  device uint16 [n_out, k_in], written.
+ * Bit-exact with the decode rule above.
+ */
+int qlora_dequant(const qlora_nf4_weight *w, uint16_t *W_bf16, hipStream_t stream);
+
+/*
+ * Forward of the adapted linear ([P1] "The mechanism in brief": W x plus
+ * (alpha / r) B A x; [P4] "The idea in one line": each weight tile is
+ * dequantized to bf16 only for the matmul that uses it).
+ *   X      device bf16 [M, k_in].
+ *   A      device bf16 [r, k_in]     (LoRA down-projection).
+ *   B      device bf16 [n_out, r]    (LoRA up-projection).
+ *   Y      device bf16 [M, n_out], written:
+ *            Y = X W_bf16^T + U~ B^T,  U~ = bf16(s * X A^T),  s = fp32(alpha / r)
+ *          accumulated in fp32, rounded once to bf16.
+ *   U_out  optional device bf16 [M, r]: receives U~ (the scaled adapter
+ *          activation) for the backward pass; NULL to discard.
+ *   ws     device workspace of at least qlora_workspace_bytes(QLORA_OP_FWD,...)
+ *          bytes (may be NULL when that is 0).
+ * r == 0 (or A/B NULL with r == 0) gives Y = X W_bf16^T.  M == 0 is a no-op.
+ * The dequantized weight is never written to memory.
+ */
+int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M,
+                     const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
+                     uint16_t *Y, uint16_t *U_out, void *ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/*
+ * Backward of the adapted linear: gradients for the activations and the
+ * adapter, never for the frozen weight ([P1] "The mechanism in brief";
+ * [P4] "The idea in one line").
+ *   X, A, B  as in the forward.   dY device bf16 [M, n_out].
+ *   U        optional device bf16 [M, r]: the U~ the forward returned in
+ *            U_out; NULL recomputes it from X and A.
+ *   dX       device bf16 [M, k_in], written:
+ *              dX = dY W_bf16 + V~ A,  V~ = bf16(s * dY B)
+ *   dA       device fp32 [r, k_in], written:  dA = V~^T X   (= s V^T X)
+ *   dB       device fp32 [n_out, r], written: dB = dY^T U~  (= s dY^T U)
+ *   ws       device workspace of qlora_workspace_bytes(QLORA_OP_BWD, ...).
+ * Token reductions are deterministic (fixed-order partial sums, no float
+ * atomics): repeated calls give bitwise-identical results.
+ * r == 0 gives dX = dY W_bf16 and touches neither dA nor dB.  M == 0 writes
+ * zeros to dA and dB (when r > 0) and nothing else.
+ */
+int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_t *dY,
+                     int64_t M, const uint16_t *A, const uint16_t *B, int32_t r,
+                     float alpha, const uint16_t *U, uint16_t *dX, float *dA, float *dB,
+                     void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes needed by qlora_linear_fwd (op = QLORA_OP_FWD) or
+ * qlora_linear_bwd (op = QLORA_OP_BWD) for these sizes; the bwd figure assumes
+ * U == NULL (the worst case).  Returns 0 for invalid arguments. */
+size_t qlora_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, int32_t r);
+
+/* Host function: copies the 16 fp32 NF4 levels the kernels use into out[16]
+ * (ascending; 7 negative, an exact 0, 8 positive, extremes -1 and +1: 16
+ * levels at normal quantiles, [P1] "The mechanism in brief"). */
+void qlora_nf4_table(float out[16]);
+
+/* Host function: static description of a status code. */
+const char *qlora_status_string(int status);
+
+/* Host function: thread-local detail of the last failure on this thread
+ * ("" if none). */
+const char *qlora_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H */

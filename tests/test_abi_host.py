@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI (CPU only, no GPU work).
+
+The library must load, export every function include/qlora.h declares, build
+the same NF4 table as the oracle, size workspaces, and reject bad arguments
+on the host before anything is enqueued.  The bad-argument calls below pass
+fake (never dereferenced) device pointers: each returns an error before any
+HIP call.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_nf4_quantized_double_amd import qlora
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora.h")
+
+OK, INVALID, SHAPE, ALIGN, WORKSPACE = 0, -1, -2, -3, -4
+FAKE = 0x10000  # aligned, never dereferenced
+FAKE_MIS = 0x10002
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(qlora.LIB_PATH):
+        from bit_nf4_quantized_double_amd import build
+        build.build(verbose=False)
+    return qlora.lib()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported(L):
+    names = _declared_functions()
+    assert {"qlora_quantize_nf4_dq", "qlora_dequant", "qlora_linear_fwd", "qlora_linear_bwd"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_library_table_matches_oracle_bitwise(L):
+    t = np.array(qlora.nf4_table(), dtype=np.float32)
+    assert np.array_equal(t.view(np.uint32), oracle.nf4_table().view(np.uint32))
+
+
+def test_status_strings(L):
+    for s in (OK, INVALID, SHAPE, ALIGN, WORKSPACE, -5):
+        assert L.qlora_status_string(s).decode().startswith("QLORA_")
+
+
+def _w(n_out=64, k_in=64, codes=FAKE, q8=FAKE, s2=FAKE):
+    return qlora._CWeight(n_out, k_in, codes, q8, s2)
+
+
+def test_weight_validation(L):
+    s = 0
+    assert L.qlora_dequant(None, FAKE, s) == INVALID
+    assert L.qlora_dequant(ctypes.byref(_w(k_in=100)), FAKE, s) == SHAPE
+    assert L.qlora_dequant(ctypes.byref(_w(n_out=12)), FAKE, s) == SHAPE
+    assert L.qlora_dequant(ctypes.byref(_w(n_out=-8)), FAKE, s) == INVALID
+    assert L.qlora_dequant(ctypes.byref(_w(codes=None)), FAKE, s) == INVALID
+    assert L.qlora_dequant(ctypes.byref(_w(codes=FAKE_MIS)), FAKE, s) == ALIGN
+    assert L.qlora_dequant(ctypes.byref(_w()), None, s) == INVALID
+    assert L.qlora_dequant(ctypes.byref(_w()), FAKE_MIS, s) == ALIGN
+    assert b"aligned" in L.qlora_last_error()
+    # empty weight is a no-op
+    assert L.qlora_dequant(ctypes.byref(_w(n_out=0)), None, s) == OK
+    # more than 2^32 weights
+    assert L.qlora_dequant(ctypes.byref(_w(n_out=1 << 20, k_in=1 << 13)), FAKE, s) == SHAPE
+
+
+def test_quantize_validation(L):
+    assert L.qlora_quantize_nf4_dq(None, 64, 64, FAKE, FAKE, FAKE, 0) == INVALID
+    assert L.qlora_quantize_nf4_dq(FAKE, 64, 96, FAKE, FAKE, FAKE, 0) == SHAPE
+    assert L.qlora_quantize_nf4_dq(FAKE_MIS, 64, 64, FAKE, FAKE, FAKE, 0) == ALIGN
+    assert L.qlora_quantize_nf4_dq(FAKE, 0, 64, None, None, None, 0) == OK
+
+
+def test_forward_validation(L):
+    w = ctypes.byref(_w())
+    f = L.qlora_linear_fwd
+    assert f(w, FAKE, 16, FAKE, FAKE, -1, 2.0, FAKE, FAKE, None, 0, 0) == INVALID
+    assert f(w, FAKE, 16, FAKE, FAKE, 65, 2.0, FAKE, FAKE, None, 0, 0) == SHAPE
+    assert f(w, FAKE, 16, None, FAKE, 8, 2.0, FAKE, FAKE, None, 0, 0) == INVALID
+    assert f(w, FAKE, -1, FAKE, FAKE, 8, 2.0, FAKE, FAKE, None, 0, 0) == INVALID
+    assert f(w, None, 16, FAKE, FAKE, 8, 2.0, FAKE, FAKE, None, 0, 0) == INVALID
+    assert f(w, FAKE_MIS, 16, FAKE, FAKE, 8, 2.0, FAKE, FAKE, None, 0, 0) == ALIGN
+    assert f(w, FAKE, 16, FAKE, FAKE_MIS, 8, 2.0, FAKE, FAKE, None, 0, 0) == ALIGN
+    # no U_out and no workspace
+    assert f(w, FAKE, 16, FAKE, FAKE, 8, 2.0, FAKE, None, None, 0, 0) == WORKSPACE
+    need = L.qlora_workspace_bytes(1, 16, 64, 64, 8)
+    assert need >= 16 * 8 * 2
+    assert f(w, FAKE, 16, FAKE, FAKE, 8, 2.0, FAKE, None, FAKE, need - 1, 0) == WORKSPACE
+    # M == 0 is a no-op
+    assert f(w, None, 0, FAKE, FAKE, 8, 2.0, None, None, None, 0, 0) == OK
+
+
+def test_backward_validation(L):
+    w = ctypes.byref(_w())
+    b = L.qlora_linear_bwd
+    args = dict(X=FAKE, dY=FAKE, M=16, A=FAKE, B=FAKE, r=8, alpha=2.0, U=None, dX=FAKE, dA=FAKE,
+                dB=FAKE, ws=None, wsb=0)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return b(w, a["X"], a["dY"], a["M"], a["A"], a["B"], a["r"], a["alpha"], a["U"], a["dX"],
+                 a["dA"], a["dB"], a["ws"], a["wsb"], 0)
+
+    assert call() == WORKSPACE
+    need = L.qlora_workspace_bytes(2, 16, 64, 64, 8)
+    assert call(ws=FAKE, wsb=need - 1) == WORKSPACE
+    assert call(dA=None) == INVALID
+    assert call(dX=None) == INVALID
+    assert call(dY=None) == INVALID
+    assert call(dB=FAKE_MIS) == ALIGN
+    assert call(r=99) == SHAPE
+    assert call(U=FAKE_MIS, ws=FAKE, wsb=need) == ALIGN
+
+
+def test_workspace_sizes(L):
+    ws = L.qlora_workspace_bytes
+    assert ws(1, 2048, 4096, 4096, 0) == 0
+    assert ws(1, 2048, 4096, 4096, 16) >= 2048 * 16 * 2
+    b = ws(2, 2048, 11008, 4096, 16)
+    assert b >= 2 * 2048 * 16 * 2 + 8 * 16 * 11008 * 4
+    assert ws(2, 2048, 4096, 4096, 0) == 0
+    assert ws(9, 1, 1, 64, 1) == 0
+    assert ws(1, 16, 64, 64, 65) == 0
