@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused NF4 double-quantized QLoRA linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one pass of the whole hot path over one batch: forward and backward
+(dX, dA, dB; never dW) of all seven linears of a 7B-class decoder layer
+(q/k/v/o 4096->4096, gate/up 4096->11008, down 11008->4096) at 2048 tokens,
+rank 16, alpha 32, with every weight stored as NF4 with double-quantized
+block scales and dequantized to bf16 inside the GEMMs.  Inputs are seeded
+synthetic tensors already resident in HBM; the one-time quantization runs
+before the timed region.
+
+Prints one JSON line: whole-step TFLOP/s (algorithmic flops
+4MNK + 6Mr(N+K) per linear), the roofline of the dominant kernel (measured
+per launch with HIP events recorded around that kernel inside the timed
+region), the CPU oracle timed on a bounded sample, and secondary HBM-bound
+figures (standalone dequant and few-token forward on 70B shapes).
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused NF4-QLoRA linear fwd+bwd TFLOP/s, % bf16 MFMA peak, 7B shapes"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PACKED_B_PER_W = (4 + 8 / 64 + 32 / 16384) / 8  # 0.51587 bytes per weight
+
+
+def flops_linear(m, n, k, r):
+    return 4 * m * n * k + 6 * m * r * (n + k)
+
+
+class HipEvents:
+    """Raw HIP events (the library records them on the stream it launches on)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev
+
+    def ms(self, a, b):
+        self.hip.hipEventSynchronize(b)
+        out = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_nf4_quantized_double_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key):
+    """HBM bytes per launch from committed rocprofv3 --pmc runs, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    ent = d.get(kernel_key)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the path is single-GPU: no sharding, no collectives)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_nf4_quantized_double_amd import qlora, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    qlora.lib()  # fails loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---------------------------------------------------------- inputs ----
+    wl = "7b"
+    M, r, alpha = synth.TOKENS[wl], synth.RANK[wl], synth.ALPHA[wl]
+    lins = []
+    host = []
+    for i, lin in enumerate(synth.LAYERS[wl]):
+        d = synth.workload_linear(wl, i)
+        host.append(d)
+        w = qlora.quantize(torch.from_numpy(d["W"]).to(dev))
+        e = dict(name=lin.name, n=lin.n_out, k=lin.k_in, w=w,
+                 X=to_dev(d["X"]), A=to_dev(d["A"]), B=to_dev(d["B"]), dY=to_dev(d["dY"]))
+        e["Y"] = torch.empty((M, lin.n_out), dtype=torch.bfloat16, device=dev)
+        e["U"] = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+        e["dX"] = torch.empty((M, lin.k_in), dtype=torch.bfloat16, device=dev)
+        e["dA"] = torch.empty((r, lin.k_in), dtype=torch.float32, device=dev)
+        e["dB"] = torch.empty((lin.n_out, r), dtype=torch.float32, device=dev)
+        e["ws"] = torch.empty(max(1, qlora.workspace_bytes(qlora.QLORA_OP_BWD, M, lin.n_out, lin.k_in, r)),
+                              dtype=torch.uint8, device=dev)
+        lins.append(e)
+    torch.cuda.synchronize()
+    step_flops = sum(flops_linear(M, e["n"], e["k"], r) for e in lins)
+    L = qlora.lib()
+    evs = HipEvents()
+
+    # events for every GEMM launch of the timed region, created up front
+    pool = [evs.create() for _ in range(4 * len(lins) * args.steps)]
+
+    def step(timing=None):
+        for e in lins:
+            if timing is not None:
+                a, b = pool.pop(), pool.pop()
+                timing["fwd"].append((a, b, e))
+                L.qlora_time_next_gemm(a, b)
+            qlora.linear_fwd(e["w"], e["X"], e["A"], e["B"], r, alpha, Y=e["Y"], U=e["U"])
+            if timing is not None:
+                a, b = pool.pop(), pool.pop()
+                timing["dx"].append((a, b, e))
+                L.qlora_time_next_gemm(a, b)
+            qlora.linear_bwd(e["w"], e["X"], e["dY"], e["A"], e["B"], r, alpha, e["U"],
+                             dX=e["dX"], dA=e["dA"], dB=e["dB"], ws=e["ws"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timing = {"fwd": [], "dx": []}
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step(timing)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_per_step = total_ms / max(1, args.steps)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    # ---- per-kernel roofline from the events recorded inside the timed region
+    per = {}
+    for kind, lst in timing.items():
+        tot_ms, tot_fl, n = 0.0, 0.0, 0
+        for a, b, e in lst:
+            tot_ms += evs.ms(a, b)
+            c = e["n"] if kind == "fwd" else e["k"]
+            tot_fl += 2.0 * M * e["n"] * e["k"] + 2.0 * M * r * c
+            n += 1
+            evs.destroy(a)
+            evs.destroy(b)
+        per[kind] = dict(avg_us=1e3 * tot_ms / max(1, n), launches=n,
+                         avg_flops=tot_fl / max(1, n), total_ms=tot_ms)
+    dom = max(per, key=lambda k: per[k]["total_ms"])
+    dk = per[dom]
+    achieved = dk["avg_flops"] / (dk["avg_us"] * 1e-6) / 1e12
+    kname = {"fwd": "k_gemm_nf4<128,128,NT> (fused forward GEMM)",
+             "dx": "k_gemm_nf4<128,128,NN> (dX GEMM)"}[dom]
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": load_traffic("gemm_" + dom + "_7b"),
+                "kernel": kname, "avg_launch_us": round(dk["avg_us"], 2),
+                "flops_per_launch": dk["avg_flops"]}
+    other = {k: {"avg_launch_us": round(v["avg_us"], 2),
+                 "tflops": round(v["avg_flops"] / (v["avg_us"] * 1e-6) / 1e12, 2)}
+             for k, v in per.items()}
+
+    # ------------------------------------------------------- secondary ----
+    secondary = None
+    if not args.no_secondary:
+        secondary = bench_secondary(torch, qlora, synth, dev, evs)
+
+    # ---------------------------------------------------- cpu baseline ----
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = bench_cpu(host, r, alpha)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "7B-class decoder layer, 7 NF4-DQ QLoRA linears fwd+bwd "
+                               "(q/k/v/o 4096->4096, gate/up 4096->11008, down 11008->4096)",
+                   "tokens": M, "rank": r, "alpha": alpha, "block": 64, "dq_group": 256,
+                   "parallelism": "single GPU"},
+        "pct_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "step_gflop": round(step_flops / 1e9, 2),
+        "roofline": roofline,
+        "gemm_kernels": other,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(out))
+
+
+def bench_secondary(torch, qlora, synth, dev, evs, reps=10):
+    """70B bandwidth-bound shapes: standalone dequant and few-token forward.
+    Three copies of each packed weight are rotated so the 256 MB on-die cache
+    cannot hold the weight between calls."""
+    res = {}
+    for idx in (0, 1):
+        lin = synth.LAYERS["70b"][idx]
+        rng = synth.rng_for("70b", idx)
+        W = torch.from_numpy(synth.draw(rng, (lin.n_out, lin.k_in), 0.02)).to(dev)
+        w0 = qlora.quantize(W)
+        del W
+        copies = [w0] + [qlora.NF4Weight(w0.codes.clone(), w0.absmax_q8.clone(), w0.absmax_scale.clone(),
+                                          w0.n_out, w0.k_in) for _ in range(2)]
+        out = torch.empty((lin.n_out, lin.k_in), dtype=torch.bfloat16, device=dev)
+        nw = lin.n_out * lin.k_in
+        for c in copies:
+            qlora.dequant(c, out)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps * 3):
+            qlora.dequant(copies[i % 3], out)
+        b.record()
+        torch.cuda.synchronize()
+        us = 1e3 * a.elapsed_time(b) / (reps * 3)
+        gbs = (PACKED_B_PER_W + 2.0) * nw / (us * 1e-6) / 1e9
+        res[f"dequant_70b_{lin.name}"] = {"us": round(us, 2), "GB/s": round(gbs, 1),
+                                          "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        del out
+        if idx == 0:
+            rr, alpha = synth.RANK["70b"], synth.ALPHA["70b"]
+            for m in (1, 4, 16):
+                d = synth.linear_inputs(lin.n_out, lin.k_in, m, rr, synth.rng_for("70b", 10 + m),
+                                        with_grad=False)
+                X = torch.from_numpy(d["X"].view(np.int16)).view(torch.bfloat16).to(dev)
+                A = torch.from_numpy(d["A"].view(np.int16)).view(torch.bfloat16).to(dev)
+                B = torch.from_numpy(d["B"].view(np.int16)).view(torch.bfloat16).to(dev)
+                Y = torch.empty((m, lin.n_out), dtype=torch.bfloat16, device=dev)
+                U = torch.empty((m, rr), dtype=torch.bfloat16, device=dev)
+                for c in copies:
+                    qlora.linear_fwd(c, X, A, B, rr, alpha, Y=Y, U=U)
+                torch.cuda.synchronize()
+                a.record()
+                for i in range(reps * 3):
+                    qlora.linear_fwd(copies[i % 3], X, A, B, rr, alpha, Y=Y, U=U)
+                b.record()
+                torch.cuda.synchronize()
+                us = 1e3 * a.elapsed_time(b) / (reps * 3)
+                byts = (nw * PACKED_B_PER_W + 2 * m * (lin.k_in + lin.n_out)
+                        + 2 * rr * (lin.k_in + lin.n_out) + 2 * m * rr)
+                gbs = byts / (us * 1e-6) / 1e9
+                res[f"fwd_70b_gate_M{m}"] = {"us": round(us, 2), "GB/s": round(gbs, 1),
+                                             "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        del copies, w0
+        torch.cuda.empty_cache()
+    return res
+
+
+def bench_cpu(host, r, alpha, m_sample=2048):
+    """The CPU oracle as it stands on a bounded sample of the same step:
+    dequant + forward + backward of all seven linears for the first
+    `m_sample` tokens.  The oracle quantizes each weight itself first
+    (untimed, like the GPU's one-time quantization)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    qs = [oracle.quantize_nf4_dq(d["W"]) for d in host]
+    t = time.perf_counter()
+    fl = 0
+    for d, q in zip(host, qs):
+        n, k = d["n_out"], d["k_in"]
+        _, wb = oracle.dequant(q["codes"], q["absmax_q8"], q["absmax_scale"], n, k)
+        oracle.linear_fwd(wb, d["X"][:m_sample], d["A"], d["B"], alpha, r)
+        oracle.linear_bwd(wb, d["X"][:m_sample], d["dY"][:m_sample], d["A"], d["B"], alpha, r)
+        fl += flops_linear(m_sample, n, k, r)
+    sec = time.perf_counter() - t
+    return {"value": round(fl / sec / 1e12, 4), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"all 7 linears of the 7B layer at {m_sample} of 2048 tokens: oracle dequant + "
+                      f"fwd + bwd in fp64 numpy, one pass, {sec:.1f} s",
+            "seconds": round(sec, 2), "cpu": platform.processor() or platform.machine()}
+
+
+if __name__ == "__main__":
+    main()

@@ -16,6 +16,7 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* q8, const float* 
                           uint16_t* out, hipStream_t st);
 hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_dx(const GemmArgs& a, hipStream_t st);
+void time_next_gemm(hipEvent_t start, hipEvent_t stop);
 hipError_t launch_lora_down(const uint16_t* X, int M, int K, const uint16_t* A, int r, float s, uint16_t* U,
                             hipStream_t st);
 hipError_t launch_lora_vt(const uint16_t* dY, int M, int N, const uint16_t* B, int r, float s, uint16_t* V,
@@ -118,6 +119,8 @@ const char* qlora_status_string(int status) {
 }
 
 const char* qlora_last_error(void) { return g_last_error.c_str(); }
+
+void qlora_time_next_gemm(hipEvent_t start, hipEvent_t stop) { qlora::time_next_gemm(start, stop); }
 
 void qlora_nf4_table(float out[16]) {
   if (!out) return;

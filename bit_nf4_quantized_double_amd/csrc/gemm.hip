@@ -281,22 +281,31 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nf4(GemmArgs a) {
     }
 }
 
+thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
 template <int BM, int BN, bool NN>
 hipError_t launch(const GemmArgs& a, hipStream_t st) {
   auto kern = k_gemm_nf4<BM, BN, NN>;
   constexpr int bytes = Smem<BM, BN, NN>::kBytes;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  hipEvent_t ev0 = t_ev_start, ev1 = t_ev_stop;
+  t_ev_start = t_ev_stop = nullptr;
+  if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
   dim3 grid((a.C + BN - 1) / BN, (a.M + BM - 1) / BM);
   hipLaunchKernelGGL(kern, grid, dim3(kThreads), bytes, st, a);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
 }  // namespace
+
+void time_next_gemm(hipEvent_t start, hipEvent_t stop) {
+  if (start && stop) { t_ev_start = start; t_ev_stop = stop; }
+  else { t_ev_start = t_ev_stop = nullptr; }
+}
 
 hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st) { return launch<128, 128, false>(a, st); }
 hipError_t launch_gemm_dx(const GemmArgs& a, hipStream_t st) { return launch<128, 128, true>(a, st); }

@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
         "qlora_nf4_table": (None, [ctypes.POINTER(ctypes.c_float)]),
         "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "qlora_last_error": (ctypes.c_char_p, []),
+        "qlora_time_next_gemm": (None, [_vp, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)

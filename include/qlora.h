@@ -157,6 +157,15 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_
  * U == NULL (the worst case).  Returns 0 for invalid arguments. */
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, int32_t r);
 
+/* Measurement aid.  The next fused-GEMM kernel launch made by the calling
+ * thread (the forward GEMM inside qlora_linear_fwd or the dX GEMM inside
+ * qlora_linear_bwd) is bracketed by hipEventRecord(start) and
+ * hipEventRecord(stop) on that call's stream, so hipEventElapsedTime gives
+ * the duration of that one kernel.  The request is then cleared.  Passing
+ * NULL for either event clears a pending request.  Events are caller-owned;
+ * the setting is thread-local, so concurrent threads do not interfere. */
+void qlora_time_next_gemm(hipEvent_t start, hipEvent_t stop);
+
 /* Host function: copies the 16 fp32 NF4 levels the kernels use into out[16]
  * (ascending; 7 negative, an exact 0, 8 positive, extremes -1 and +1: 16
  * levels at normal quantiles, [P1] "The mechanism in brief"). */
