@@ -78,7 +78,8 @@ int check_rows(int64_t M, int64_t n_out, int64_t k_in) {
   if (M < 0) return fail(QLORA_ERR_INVALID_ARG, "M < 0");
   if (M > INT_MAX) return fail(QLORA_ERR_SHAPE, "M exceeds INT_MAX");
   const int64_t widest = n_out > k_in ? n_out : k_in;
-  if (widest > 0 && M > (int64_t)INT_MAX / widest) return fail(QLORA_ERR_SHAPE, "M * width exceeds 2^31");
+  // every activation / output buffer stays within 2^31 bytes (32-bit buffer offsets)
+  if (widest > 0 && M > ((int64_t)1 << 30) / widest) return fail(QLORA_ERR_SHAPE, "M * width exceeds 2^30 elements");
   return QLORA_OK;
 }
 

@@ -57,6 +57,24 @@ __device__ __forceinline__ float block_scale(const uint8_t* q8, const float* s2,
   return (float)q8[b] * s2[b >> 8];
 }
 
+// ---- raw buffer loads: an offset at or past the buffer size reads zeros ----
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+constexpr uint32_t kOOB = 0x80000000u;  // callers keep every buffer <= 2^31 bytes
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
 // 16-byte chunk swizzle inside a 64-element (128-byte) bf16 LDS row: keeps
 // ds_read_b128 / ds_write_b128 conflict-free for row-consecutive and for
 // 8-row-strided access patterns.

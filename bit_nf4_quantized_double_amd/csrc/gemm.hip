@@ -5,295 +5,509 @@
 // dX (backward for the activations):
 //     dX[m][c] = sum_n dY[m][n] * Wbf[n][c] +  sum_j V~[m][j] * A[j][c]
 //
-// Wbf is never materialised: each 64-deep reduction step the workgroup reads
-// the packed codes of the W tile it needs, decodes them to bf16 (level * block
-// scale, round to nearest even) and stores them in LDS, where they feed
-// v_mfma_f32_32x32x16_bf16.  The rank-r adapter term runs as one extra
-// reduction step over the r adapter columns, into the same accumulators.
+// Wbf is never materialised.  Each 64-deep reduction step a workgroup reads
+// the packed codes of the W tile it needs, decodes them to bf16
+// (round-to-nearest-even of level * block scale) in registers and stores the
+// tile in LDS, where all four waves read it as the MFMA B operand.  The rank-r
+// adapter term is one extra reduction step into the same accumulators.
 //
-// Tile: BM x BN outputs per 256-thread workgroup, 2 x 2 waves, each wave
-// (BM/2) x (BN/2) as (BM/64) x (BN/64) MFMA tiles of 32 x 32.
-//   NT (forward): W tile = BN rows n x 64 k, stored [n][k] (k contiguous),
-//                 read with ds_read_b128 like the activation tile.
-//   NN (dX):      W tile = 64 rows n x BN columns c, stored [n][c] (c
-//                 contiguous) exactly as decoded; the MFMA B operand needs 8
-//                 consecutive n per lane and gets them with gfx950's
-//                 transposing LDS read ds_read_b64_tr_b16.
+// Workgroup tile 256 (rows) x 128 (columns), 4 waves stacked along the rows;
+// each wave owns 64 rows x 128 columns = 2 x 4 tiles of
+// v_mfma_f32_32x32x16_bf16.  A wave's activation rows are private to it: it
+// copies them with coalesced buffer_load ... lds (8 lanes per 128-byte row
+// slice, straight into a wave-private LDS ring, no VGPR round trip) and reads
+// them back in MFMA operand layout.  The decoded W tile is double-buffered
+// and shared by the four waves (one barrier per step).
+//
+//   NT (forward): W tile = 128 rows n x 64 k, stored [n][k], read with
+//                 ds_read_b128.
+//   NN (dX):      W tile = 64 rows n x 128 columns c, stored [n][c] as
+//                 decoded; the B operand needs 8 consecutive n per lane and
+//                 gets them with gfx950's transposing ds_read_b64_tr_b16.
+// Rows of 64 bf16 (128 B) keep their 16-byte chunks XOR-swizzled by swz(row)
+// so row-consecutive operand reads are bank-conflict-free.
+//
+// Decode: each thread decodes 32 consecutive weights of one 64-weight block
+// (one block scale).  The 16 values bf16(level[c] * scale) form a per-block
+// lookup table held as byte planes in registers and indexed with v_perm_b32;
+// the two lanes sharing a block each build half the table and swap halves
+// with one DPP move.  No LDS traffic for the lookup.
 #include "gemm_args.h"
 
 namespace qlora {
-
-
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int BM = 256, BN = 128;
 
 typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// ---- shared-memory tile geometry ------------------------------------------
-// Activation tile / NT weight tile: rows of 64 bf16 (128 B), 16-byte chunks
-// XOR-swizzled by swz(row).
+// ---- LDS tile geometry -----------------------------------------------------
+// NT W tile: rows of 64 bf16 (128 B), 16-byte chunks XOR-swizzled by swz(row).
 __device__ __forceinline__ uint32_t kt_off(uint32_t row, uint32_t chunk) {
   return row * 64u + ((chunk ^ swz(row)) << 3);
 }
-// NN weight tile: 64 rows (n) of BN bf16, padded by 16 elements so the 4 rows
-// touched by one transposing read land in different banks.
-template <int BN>
-__device__ __forceinline__ uint32_t nn_off(uint32_t row, uint32_t col) {
-  return row * (uint32_t)(BN + 16) + col;
+// NN W tile: 64 rows of BN bf16, padded by 16 elements.
+constexpr int kNNPitch = BN + 16;
+__device__ __forceinline__ uint32_t nn_off(uint32_t row, uint32_t col) { return row * kNNPitch + col; }
+
+template <bool NN>
+struct Tile {
+  static constexpr int kElems = NN ? 64 * kNNPitch : BN * 64;  // bf16 per buffer
+};
+
+// ---- per-block lookup-table decode ----------------------------------------
+struct Lut {
+  uint32_t alo0, alo1, ahi0, ahi1;  // my 8 entries (byte planes)
+  uint32_t blo0, blo1, bhi0, bhi1;  // partner's 8 entries
+};
+
+// Lane parity p: even lanes hold levels 0..7, odd lanes 8..15 (th[]).
+__device__ __forceinline__ Lut build_lut(const float th[8], float a) {
+  const uint32_t p0 = pack_bf16x2(th[0] * a, th[1] * a);
+  const uint32_t p1 = pack_bf16x2(th[2] * a, th[3] * a);
+  const uint32_t p2 = pack_bf16x2(th[4] * a, th[5] * a);
+  const uint32_t p3 = pack_bf16x2(th[6] * a, th[7] * a);
+  Lut L;
+  L.alo0 = __builtin_amdgcn_perm(p1, p0, 0x06040200u);
+  L.ahi0 = __builtin_amdgcn_perm(p1, p0, 0x07050301u);
+  L.alo1 = __builtin_amdgcn_perm(p3, p2, 0x06040200u);
+  L.ahi1 = __builtin_amdgcn_perm(p3, p2, 0x07050301u);
+  // swap with the partner lane (lane ^ 1): DPP quad_perm [1,0,3,2]
+  L.blo0 = __builtin_amdgcn_mov_dpp(L.alo0, 0xB1, 0xF, 0xF, false);
+  L.bhi0 = __builtin_amdgcn_mov_dpp(L.ahi0, 0xB1, 0xF, 0xF, false);
+  L.blo1 = __builtin_amdgcn_mov_dpp(L.alo1, 0xB1, 0xF, 0xF, false);
+  L.bhi1 = __builtin_amdgcn_mov_dpp(L.ahi1, 0xB1, 0xF, 0xF, false);
+  return L;
 }
 
-template <int BM, int BN, bool NN>
-struct Smem {
-  static constexpr int kAct = BM * 64;                         // elements per buffer
-  static constexpr int kW = NN ? 64 * (BN + 16) : BN * 64;
-  static constexpr int kBytes = 2 * 2 * (kAct + kW);            // double-buffered bf16
+// Per-lane constants of the lookup: lanes of odd parity own levels 8..15.
+struct LaneMask {
+  uint32_t s;    // xor for my-half indices: 0 (even) or 0x08080808 (odd)
+  uint32_t x;    // xor for partner-half indices: s ^ 0x08080808
+  uint32_t sel;  // base byte selector 0x03020100, bit 2 flipped on odd lanes
 };
 
-// ---- activation tile: BM rows x 64 reduction columns ----------------------
-template <int BM>
-struct ActLoader {
-  static constexpr int kChunks = BM * 8 / kThreads;  // 16-byte chunks per thread
-  uint4 v[kChunks];
+// t: bytes hold (code_i | code_{i+1} << 4); the low nibble of byte i is the
+// code of output element i.  Index < 8 after the xor: my half of the table;
+// >= 8: the partner's half.  Returns {w0,w1}, {w2,w3} as bf16 pairs.
+__device__ __forceinline__ void lookup4(const Lut& L, uint32_t t, const LaneMask& lm, uint32_t& o01,
+                                        uint32_t& o23) {
+  const uint32_t s = (t & 0x0F0F0F0Fu) ^ lm.s;
+  const uint32_t x = (t & 0x0F0F0F0Fu) ^ lm.x;
+  const uint32_t sel = ((t >> 1) & 0x04040404u) ^ lm.sel;
+  const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(L.blo1, L.blo0, x),
+                                            __builtin_amdgcn_perm(L.alo1, L.alo0, s), sel);
+  const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(L.bhi1, L.bhi0, x),
+                                            __builtin_amdgcn_perm(L.ahi1, L.ahi0, s), sel);
+  o01 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+  o23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+}
 
-  __device__ __forceinline__ void load(const GemmArgs& a, int m0, int r0, int tid) {
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      int q = tid + i * kThreads;
-      int row = q >> 3, ch = q & 7;
-      int m = m0 + row, rr = r0 + ch * 8;
-      if (m < a.M && rr < a.R)
-        v[i] = *reinterpret_cast<const uint4*>(a.act + (int64_t)m * a.ld_act + rr);
-      else
-        v[i] = make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* s, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      int q = tid + i * kThreads;
-      *reinterpret_cast<uint4*>(s + kt_off(q >> 3, q & 7)) = v[i];
-    }
-  }
+// 8 codes (one dword, element 0 in the low nibble) -> 4 dwords of bf16 pairs.
+__device__ __forceinline__ uint4 decode8_lut(const Lut& L, uint32_t d, const LaneMask& lm) {
+  const uint32_t sh = d >> 4;
+  uint4 o;
+  lookup4(L, __builtin_amdgcn_perm(sh, d, 0x05010400u), lm, o.x, o.y);
+  lookup4(L, __builtin_amdgcn_perm(sh, d, 0x07030602u), lm, o.z, o.w);
+  return o;
+}
+
+// ---- global -> register loads (raw buffer loads: out of range reads 0) ----
+struct Srcs {
+  __amdgpu_buffer_rsrc_t act, codes, q8, s2;
 };
 
-// ---- W tile: each thread decodes 32 consecutive weights of one W row ------
-// NT: BN rows (n = c0 + row) x 64 k starting at r0.
-// NN: 64 rows (n = r0 + row) x BN columns starting at c0.
-template <int BN, bool NN>
-struct WLoader {
-  static constexpr int kRows = NN ? 64 : BN;
-  static constexpr int kSegs = (NN ? BN : 64) / 32;            // 32-weight segments per row
-  static constexpr int kPer = kRows * kSegs / kThreads;         // segments per thread
-  static_assert(kRows * kSegs % kThreads == 0, "tile/thread mismatch");
-  uint4 code[kPer];
-  float scale[kPer];
+template <bool NN>
+__device__ __forceinline__ Srcs make_srcs(const GemmArgs& a) {
+  Srcs s;
+  // W is [n_out x k_in]: n_out = C (forward) or R (dX)
+  const uint64_t wn = (uint64_t)a.K * (uint64_t)(NN ? a.R : a.C);
+  const uint32_t nb = (uint32_t)(wn >> 6);
+  s.act = make_rsrc(a.act, (uint32_t)((uint64_t)a.M * a.ld_act * 2));
+  s.codes = make_rsrc(a.codes, (uint32_t)(wn >> 1));
+  s.q8 = make_rsrc(a.q8, nb);
+  s.s2 = make_rsrc(a.s2, ((nb + 255) >> 8) * 4);
+  return s;
+}
 
-  __device__ __forceinline__ void load(const GemmArgs& a, int c0, int r0, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      int s = tid + i * kThreads;
-      int row = s / kSegs, seg = s % kSegs;
-      int n, k;
-      bool ok;
-      if (NN) { n = r0 + row; k = c0 + seg * 32; ok = n < a.R && k < a.C; }
-      else    { n = c0 + row; k = r0 + seg * 32; ok = n < a.C; }
-      if (ok) {
-        uint32_t e = (uint32_t)n * (uint32_t)a.K + (uint32_t)k;   // weight index
-        code[i] = *reinterpret_cast<const uint4*>(a.codes + (e >> 1));
-        scale[i] = block_scale(a.q8, a.s2, e >> 6);
-      } else {
-        code[i] = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);  // level 0.0
-        scale[i] = 0.f;
-      }
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* s, int tid, const float* lv) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      int sg = tid + i * kThreads;
-      int row = sg / kSegs, seg = sg % kSegs;
-      uint4 w0 = decode8(code[i].x, scale[i], lv);
-      uint4 w1 = decode8(code[i].y, scale[i], lv);
-      uint4 w2 = decode8(code[i].z, scale[i], lv);
-      uint4 w3 = decode8(code[i].w, scale[i], lv);
-      if (NN) {
-        uint16_t* p = s + nn_off<BN>(row, seg * 32);
-        reinterpret_cast<uint4*>(p)[0] = w0;
-        reinterpret_cast<uint4*>(p)[1] = w1;
-        reinterpret_cast<uint4*>(p)[2] = w2;
-        reinterpret_cast<uint4*>(p)[3] = w3;
-      } else {
-        *reinterpret_cast<uint4*>(s + kt_off(row, seg * 4 + 0)) = w0;
-        *reinterpret_cast<uint4*>(s + kt_off(row, seg * 4 + 1)) = w1;
-        *reinterpret_cast<uint4*>(s + kt_off(row, seg * 4 + 2)) = w2;
-        *reinterpret_cast<uint4*>(s + kt_off(row, seg * 4 + 3)) = w3;
-      }
-    }
-  }
+// Codes of the 32 weights this thread decodes for the step starting at r0.
+struct CodeSeg {
+  uint4 code;
+  uint32_t q;  // 8-bit block absmax code
+  float s2;    // second-level scale of its group
 };
 
-// B operand (W side) for one 32 x 32 x 16 MFMA: output columns col0..col0+31,
-// reduction rows 16*ks .. 16*ks+15 of the current step.
-template <int BN, bool NN>
-__device__ __forceinline__ bf16x8 load_bfrag(const uint16_t* s, int col0, int ks, int lane) {
-  if (!NN) {
-    uint4 v = *reinterpret_cast<const uint4*>(s + kt_off(col0 + (lane & 31), ks * 2 + (lane >> 5)));
-    return __builtin_bit_cast(bf16x8, v);
+template <bool NN>
+__device__ __forceinline__ CodeSeg load_codes(const GemmArgs& a, const Srcs& src, int c0, int r0, int tid) {
+  int n, k;
+  bool ok;
+  if (NN) { n = r0 + (tid >> 2); k = c0 + (tid & 3) * 32; ok = n < a.R && k < a.C; }
+  else    { n = c0 + (tid >> 1); k = r0 + (tid & 1) * 32; ok = n < a.C && k < a.R; }
+  const uint32_t e = (uint32_t)n * (uint32_t)a.K + (uint32_t)k;  // weight index
+  CodeSeg cs;  // out of range: all zero, which decodes to zeros
+  cs.code = buf_load16(src.codes, ok ? (e >> 1) : kOOB);
+  cs.q = buf_load1(src.q8, ok ? (e >> 6) : kOOB);
+  cs.s2 = __builtin_bit_cast(float, buf_load4(src.s2, ok ? ((e >> 14) << 2) : kOOB));
+  return cs;
+}
+
+template <bool NN>
+__device__ __forceinline__ void decode_store(uint16_t* s, const CodeSeg& cs, const float th[8],
+                                             const LaneMask& lm, int tid) {
+  const Lut L = build_lut(th, (float)cs.q * cs.s2);  // a' = fp32(q8 * s2)
+  const uint4 w0 = decode8_lut(L, cs.code.x, lm);
+  const uint4 w1 = decode8_lut(L, cs.code.y, lm);
+  const uint4 w2 = decode8_lut(L, cs.code.z, lm);
+  const uint4 w3 = decode8_lut(L, cs.code.w, lm);
+  if (NN) {
+    uint16_t* p = s + nn_off(tid >> 2, (tid & 3) * 32);
+    reinterpret_cast<uint4*>(p)[0] = w0;
+    reinterpret_cast<uint4*>(p)[1] = w1;
+    reinterpret_cast<uint4*>(p)[2] = w2;
+    reinterpret_cast<uint4*>(p)[3] = w3;
   } else {
-    // lane (within its 16-lane group g) = p + 4q addresses row k0 + q, columns
-    // cb + 4p..4p+3; it receives column cb + (lane & 15), rows k0..k0+3.
-    int g = lane >> 4, i = lane & 15;
-    int p = i & 3, q = i >> 2;
-    int cb = col0 + (g & 1) * 16 + 4 * p;
-    int k0 = ks * 16 + (g >> 1) * 8;
-    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(s + nn_off<BN>(k0 + q, cb)));
-    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(s + nn_off<BN>(k0 + 4 + q, cb)));
-    typedef __attribute__((ext_vector_type(8))) short i16x8;
-    i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, v);
+    const int row = tid >> 1, c = (tid & 1) * 4;
+    *reinterpret_cast<uint4*>(s + kt_off(row, c + 0)) = w0;
+    *reinterpret_cast<uint4*>(s + kt_off(row, c + 1)) = w1;
+    *reinterpret_cast<uint4*>(s + kt_off(row, c + 2)) = w2;
+    *reinterpret_cast<uint4*>(s + kt_off(row, c + 3)) = w3;
   }
 }
 
-template <int BM>
-__device__ __forceinline__ bf16x8 load_afrag(const uint16_t* s, int row0, int ks, int lane) {
-  uint4 v = *reinterpret_cast<const uint4*>(s + kt_off(row0 + (lane & 31), ks * 2 + (lane >> 5)));
+// ---- activations: coalesced copies into a wave-private LDS ring ----------
+// One stage = the wave's 64 rows x 64 reduction columns (8 KB), row r at
+// byte r * 128 with chunk lc stored at physical chunk lc ^ swz(r).
+constexpr uint32_t kActStage = 64 * 128;
+constexpr int kActStages = 3;
+
+// Byte offsets of the 8 rows this lane copies (row 8j + (lane >> 3) of the
+// wave's 64 rows for copy instruction j; kOOB past the last row).
+struct ActRows {
+  uint32_t off[8];
+};
+
+__device__ __forceinline__ ActRows act_rows(const GemmArgs& a, int row0, int lane) {
+  ActRows ar;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int m = row0 + 8 * j + (lane >> 3);
+    ar.off[j] = m < a.M ? (uint32_t)m * (uint32_t)a.ld_act * 2u : kOOB;
+  }
+  return ar;
+}
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Issue the 8 coalesced copies of one step (reduction columns r0..r0+63) into
+// the LDS stage at byte offset `stage`.  Lane l of copy j lands at stage +
+// 1024 j + 16 l = row (8j + l / 8), physical chunk l % 8.
+__device__ __forceinline__ void copy_act(const GemmArgs& a, const Srcs& src, const ActRows& rows, lds_u8* stage,
+                                         int r0, int lane) {
+  const uint32_t pc = lane & 7, rl = lane >> 3;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t lc = pc ^ ((rl ^ (uint32_t)j) & 7u);  // logical chunk = pc ^ swz(8j + rl)
+    const int k = r0 + 8 * (int)lc;
+    const uint32_t off = k < a.R ? rows.off[j] + 2u * (uint32_t)k : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.act, stage + 1024u * j, 16, off, 0, 0, 0);
+  }
+}
+
+// A operand for MFMA sub-step ks, rows 32 i .. 32 i + 31 of the wave's slice.
+__device__ __forceinline__ bf16x8 load_afrag(const uint16_t* st, int i, int ks, int lane) {
+  const uint32_t r = 32 * i + (lane & 31);
+  const uint4 v = *reinterpret_cast<const uint4*>(st + r * 64u + (((2u * ks + (lane >> 5)) ^ swz(r)) << 3));
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int BM, int BN, bool NN>
-__global__ __launch_bounds__(kThreads) void k_gemm_nf4(GemmArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  using S = Smem<BM, BN, NN>;
-  constexpr int TM = BM / 64, TN = BN / 64;  // MFMA tiles per wave
-  // buffer b: activations at smem + b*kAct, W tile at smem + 2*kAct + b*kW
-  auto s_act = [&](int b) { return smem + b * S::kAct; };
-  auto s_w = [&](int b) { return smem + 2 * S::kAct + b * S::kW; };
-  __shared__ float s_lv[16];
+// B operand for MFMA sub-step ks, columns col0..col0+31.
+template <bool NN>
+__device__ __forceinline__ bf16x8 load_bfrag(const uint16_t* s, int col0, int ks, int lane) {
+  if (!NN) {
+    const uint4 v = *reinterpret_cast<const uint4*>(s + kt_off(col0 + (lane & 31), 2 * ks + (lane >> 5)));
+    return __builtin_bit_cast(bf16x8, v);
+  } else {
+    // 16-lane group g: lanes 0-31 are half 0 (rows 16 ks .. +7), 32-63 half 1
+    // (rows 16 ks + 8 .. +15); odd groups take columns 16..31.  Lane p + 4q addresses row nb + q, columns cb + 4p and
+    // receives column cb + (lane & 15), rows nb .. nb + 3.
+    const int g = lane >> 4, i = lane & 15;
+    const int cb = col0 + (g & 1) * 16 + 4 * (i & 3);
+    const int nb = 16 * ks + 8 * (g >> 1) + (i >> 2);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(s + nn_off(nb, cb)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(s + nn_off(nb + 4, cb)));
+    const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+  }
+}
 
+// One reduction step of MFMAs: A operand from the wave's activation stage,
+// B operand from the shared W tile.  If cs is given, the next W tile is
+// decoded into s_next alongside: MFMA sub-step ks is paired with code dword ks
+// of this thread's 32 weights, so the decode VALU work issues while the matrix
+// core runs (sub-steps are fenced so the compiler keeps that pairing).  B
+// operands of sub-step ks + 1 are read during sub-step ks.
+template <bool NN>
+__device__ __forceinline__ void store_w8(uint16_t* s_next, const uint4& w, int q, int tid) {
+  if (NN) *reinterpret_cast<uint4*>(s_next + nn_off(tid >> 2, (tid & 3) * 32 + 8 * q)) = w;
+  else *reinterpret_cast<uint4*>(s_next + kt_off(tid >> 1, (tid & 1) * 4 + q)) = w;
+}
+
+template <bool NN, bool DECODE>
+__device__ __forceinline__ void mma_step(f32x16 (&acc)[2][4], const uint16_t* act, const uint16_t* sw,
+                                         uint16_t* s_next, const CodeSeg& cs, const float th[8],
+                                         const LaneMask& lm, int tid, int lane) {
+  bf16x8 nb[4], na[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) nb[j] = load_bfrag<NN>(sw, 32 * j, 0, lane);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) na[i] = load_afrag(act, i, 0, lane);
+  Lut L;
+  if (DECODE) L = build_lut(th, (float)cs.q * cs.s2);  // a' = fp32(q8 * s2)
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    bf16x8 bf[4], af[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[j] = nb[j];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) af[i] = na[i];
+    if (ks < 3) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) nb[j] = load_bfrag<NN>(sw, 32 * j, ks + 1, lane);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) na[i] = load_afrag(act, i, ks + 1, lane);
+    }
+    if (DECODE) {
+      const uint32_t d = ks == 0 ? cs.code.x : ks == 1 ? cs.code.y : ks == 2 ? cs.code.z : cs.code.w;
+      store_w8<NN>(s_next, decode8_lut(L, d, lm), ks, tid);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    if (DECODE) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // then up to 4 VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// s_waitcnt with only a vmcnt limit (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their "no wait" maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Step hand-off barrier of the main loop.  A plain __syncthreads() carries a
+// workgroup release fence, which would also drain the activation copies
+// still in flight for later steps; here each wave first waits only for its
+// own LDS operations (lgkmcnt(0): decoded-tile stores, operand reads), and
+// producers additionally wait for the copies the next step needs before
+// calling this (wait_vmcnt).
+__device__ __forceinline__ void step_barrier() {
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+}
+
+// XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
+// give each XCD a contiguous run of tiles (row-major over column tiles): the
+// workgroups resident on one XCD then share activation rows in its L2.
+__device__ __forceinline__ void tile_coords(int& tm, int& tn) {
+  const int nt = gridDim.x, total = gridDim.x * gridDim.y;
+  const int lin = blockIdx.x + blockIdx.y * gridDim.x;
+  int t = lin;
+  if (total % 8 == 0) t = (lin % 8) * (total / 8) + lin / 8;
+  tm = t / nt;
+  tn = t % nt;
+}
+
+// Wave-specialised workgroup of 8 waves, two per SIMD:
+//   waves 0-3 (consumers) run only the MFMAs of their 64 x 128 output slice;
+//   waves 4-7 (producers) copy activations for consumer (wave - 4) into its
+//   LDS ring, load codes and decode the next W tile.
+// The SIMD co-issues a producer's VALU work with its consumer's MFMAs, so the
+// decode runs in the matrix core's shadow without hand interleaving.  One
+// barrier per 64-deep step hands tile s + 1 (and activation stage s + 1) from
+// producers to consumers.
+//
+// Producer pipeline at step s: load codes of step s + 2 (2-slot register
+// ring), copy activations of step s + 2 (3-stage LDS ring), decode codes of
+// step s + 1 into W buffer (s + 1) % 2, then wait for the copies of step s + 1.
+template <bool NN>
+__global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
+  // Two distinct LDS objects: the compiler can then tell that the producers'
+  // stores of decoded W tiles never alias the activation copies in flight
+  // (otherwise it drains every copy before each such store).
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[2 * Tile<NN>::kElems];
+  __shared__ __attribute__((aligned(16))) uint8_t s_act[4 * kActStages * kActStage];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM, c0 = blockIdx.x * BN;
-  if (tid < 16) s_lv[tid] = a.nf4.level[tid];
+  const bool producer = wave >= 4;
+  const int slice = wave & 3;               // consumer slice this wave works on / feeds
+  const int ptid = tid & (kThreads - 1);    // producer thread index 0..255
+  int tm, tn;
+  tile_coords(tm, tn);
+  const int m0 = tm * BM, c0 = tn * BN;
+  const int row0 = m0 + 64 * slice;
+  uint16_t* const w_buf0 = s_w;
+  uint16_t* const w_buf1 = s_w + Tile<NN>::kElems;
+  auto act_lds = [&](int st) {
+    return (lds_u8*)s_act + ((uint32_t)slice * kActStages + st) * kActStage;
+  };
+  auto act_ptr = [&](int st) {
+    return reinterpret_cast<uint16_t*>(s_act + ((uint32_t)slice * kActStages + st) * kActStage);
+  };
 
-  f32x16 acc[TM][TN];
+  const int nsteps = (a.R + 63) / 64;
+  // step count rounded up to even (an all-zero step adds nothing)
+  const int nst = (nsteps + 1) & ~1;
+  // Each column tile starts its reduction at a different step (rotation by
+  // the tile index) so the workgroups of one XCD do not all read the same
+  // column slice at the same time.  The per-tile summation order stays fixed,
+  // so results are deterministic.
+  const int rot = nst > 0 ? (tn * 5) % nst : 0;
+  auto kofs = [&](int step) {  // reduction offset of logical step; >= R past the end
+    if (step >= nst) return nst * 64;
+    int p = step + rot;
+    p -= p >= nst ? nst : 0;
+    return p * 64;
+  };
+  auto stage_of = [](int step) { return step % kActStages; };
+
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  ActLoader<BM> al;
-  WLoader<BN, NN> wl;
-  const int nsteps = (a.R + 63) / 64;
+  if (producer) {
+    const bool odd = lane & 1;
+    float th[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) th[i] = odd ? a.nf4.level[8 + i] : a.nf4.level[i];
+    LaneMask lm;
+    lm.s = odd ? 0x08080808u : 0u;
+    lm.x = lm.s ^ 0x08080808u;
+    lm.sel = odd ? 0x07060504u : 0x03020100u;
+    const Srcs src = make_srcs<NN>(a);
+    const ActRows rows = act_rows(a, row0, lane);
 
-  al.load(a, m0, 0, tid);
-  wl.load(a, c0, 0, tid);
-  __syncthreads();  // s_lv visible
-  al.store(s_act(0), tid);
-  wl.store(s_w(0), tid, s_lv);
-  __syncthreads();
-
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
-    const bool more = step + 1 < nsteps;
-    if (more) {
-      al.load(a, m0, (step + 1) * 64, tid);
-      wl.load(a, c0, (step + 1) * 64, tid);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = load_afrag<BM>(s_act(buf), wm * (BM / 2) + 32 * i, ks, lane);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = load_bfrag<BN, NN>(s_w(buf), wn * (BN / 2) + 32 * j, ks, lane);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      al.store(s_act(buf ^ 1), tid);
-      wl.store(s_w(buf ^ 1), tid, s_lv);
-    }
+    // Issue order inside a step: code loads first, then activation copies,
+    // so that waiting for the codes of step s + 1 (decoded at step s) never
+    // waits for the copies issued after them (vmcnt retires in order).
+    CodeSeg c0s = load_codes<NN>(a, src, c0, kofs(0), ptid);
+    copy_act(a, src, rows, act_lds(stage_of(0)), kofs(0), lane);
+    CodeSeg c1s = load_codes<NN>(a, src, c0, kofs(1), ptid);
+    copy_act(a, src, rows, act_lds(stage_of(1)), kofs(1), lane);
+    decode_store<NN>(w_buf0, c0s, th, lm, ptid);
+    // copies of step 0 done: younger are the codes (3) and copies (8) of step 1
+    wait_vmcnt<11>();
     __syncthreads();
+
+    auto body = [&](int step, CodeSeg& load_slot, const CodeSeg& dec, uint16_t* w_next) {
+      load_slot = load_codes<NN>(a, src, c0, kofs(step + 2), ptid);
+      __builtin_amdgcn_sched_barrier(0);  // keep all code loads ahead of the copies
+      copy_act(a, src, rows, act_lds(stage_of(step + 2)), kofs(step + 2), lane);
+      decode_store<NN>(w_next, dec, th, lm, ptid);
+      // copies of step s + 1 done: younger are the codes (3) and copies (8)
+      // of step s + 2
+      wait_vmcnt<11>();
+      step_barrier();
+    };
+    for (int step = 0; step < nst; step += 2) {
+      body(step, c0s, c1s, w_buf1);
+      body(step + 1, c1s, c0s, w_buf0);
+    }
+    wait_vmcnt<0>();  // nothing left in flight into the activation ring
+  } else {
+    __syncthreads();  // tile 0 and activations of step 0 are ready
+    const CodeSeg none{};
+    const float th0[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const LaneMask lm0{0, 0, 0};
+    for (int step = 0; step < nst; step += 2) {
+      mma_step<NN, false>(acc, act_ptr(stage_of(step)), w_buf0, w_buf1, none, th0, lm0, 0, lane);
+      step_barrier();
+      mma_step<NN, false>(acc, act_ptr(stage_of(step + 1)), w_buf1, w_buf0, none, th0, lm0, 0, lane);
+      step_barrier();
+    }
   }
 
-  // ---- adapter step: r extra reduction columns ---------------------------
+  // ---- adapter step: r extra reduction columns j = 16 ks + 8 h + e --------
   if (a.r > 0) {
-    const int buf = nsteps & 1;
-    const int rp = (a.r + 15) & ~15;
-    uint16_t* sa = s_act(buf);
-    uint16_t* sw = s_w(buf);
-    for (int idx = tid; idx < BM * rp; idx += kThreads) {
-      int row = idx / rp, j = idx % rp;
-      int m = m0 + row;
-      uint16_t v = (m < a.M && j < a.r) ? a.lora_act[(int64_t)m * a.r + j] : (uint16_t)0;
-      sa[kt_off(row, j >> 3) + (j & 7)] = v;
-    }
-    for (int idx = tid; idx < BN * rp; idx += kThreads) {
-      if (!NN) {
-        int col = idx / rp, j = idx % rp;
-        int n = c0 + col;
-        uint16_t v = (n < a.C && j < a.r) ? a.lora_w[(int64_t)n * a.r + j] : (uint16_t)0;
-        sw[kt_off(col, j >> 3) + (j & 7)] = v;
-      } else {
-        int j = idx / BN, col = idx % BN;
-        int c = c0 + col;
-        uint16_t v = (c < a.C && j < a.r) ? a.lora_w[(int64_t)j * a.K + c] : (uint16_t)0;
-        sw[nn_off<BN>(j, col)] = v;
+    // W buffer 0 and activation stage stage_of(nst) are no longer read.
+    __syncthreads();
+    uint16_t* sw = w_buf0;
+    uint16_t* sa = act_ptr(stage_of(nst));
+    if (producer) {
+      for (int idx = ptid; idx < BN * 64; idx += kThreads) {
+        if (!NN) {
+          const int col = idx >> 6, j = idx & 63;
+          const int n = c0 + col;
+          const uint16_t v = (n < a.C && j < a.r) ? a.lora_w[(int64_t)n * a.r + j] : (uint16_t)0;
+          sw[kt_off(col, j >> 3) + (j & 7)] = v;
+        } else {
+          const int j = idx / BN, col = idx % BN;
+          const int c = c0 + col;
+          const uint16_t v = (c < a.C && j < a.r) ? a.lora_w[(int64_t)j * a.K + c] : (uint16_t)0;
+          sw[nn_off(j, col)] = v;
+        }
+      }
+      for (int idx = lane; idx < 64 * 64; idx += 64) {
+        const uint32_t r = idx >> 6, j = idx & 63;
+        const int m = row0 + (int)r;
+        const uint16_t v = (m < a.M && (int)j < a.r) ? a.lora_act[(int64_t)m * a.r + j] : (uint16_t)0;
+        sa[r * 64u + (((j >> 3) ^ swz(r)) << 3) + (j & 7)] = v;
       }
     }
     __syncthreads();
-    for (int ks = 0; ks < rp / 16; ++ks) {
-      bf16x8 af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = load_afrag<BM>(sa, wm * (BM / 2) + 32 * i, ks, lane);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = load_bfrag<BN, NN>(sw, wn * (BN / 2) + 32 * j, ks, lane);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    if (!producer) {
+      const CodeSeg none{};
+      const float th0[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      const LaneMask lm0{0, 0, 0};
+      mma_step<NN, false>(acc, sa, sw, sw, none, th0, lm0, 0, lane);
     }
   }
 
   // ---- epilogue: fp32 -> bf16 (round to nearest even) ---------------------
+  if (!producer) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = c0 + wn * (BN / 2) + 32 * j + (lane & 31);
+      for (int j = 0; j < 4; ++j) {
+        const int col = c0 + 32 * j + (lane & 31);
+        if (col >= a.C) continue;
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        const int row = m0 + wm * (BM / 2) + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        uint32_t pk = pack_bf16x2(acc[i][j][v], acc[i][j][v + 1]);
-        if (col < a.C) {
+        for (int v = 0; v < 16; v += 2) {
+          const int row = row0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const uint32_t pk = pack_bf16x2(acc[i][j][v], acc[i][j][v + 1]);
           if (row < a.M) a.out[(int64_t)row * a.ld_out + col] = (uint16_t)(pk & 0xFFFFu);
           if (row + 1 < a.M) a.out[(int64_t)(row + 1) * a.ld_out + col] = (uint16_t)(pk >> 16);
         }
       }
-    }
+  }
 }
 
 thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
 
-template <int BM, int BN, bool NN>
+template <bool NN>
 hipError_t launch(const GemmArgs& a, hipStream_t st) {
-  auto kern = k_gemm_nf4<BM, BN, NN>;
-  constexpr int bytes = Smem<BM, BN, NN>::kBytes;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e != hipSuccess) return e;
+  auto kern = k_gemm_nf4<NN>;
+  hipError_t e;
   hipEvent_t ev0 = t_ev_start, ev1 = t_ev_stop;
   t_ev_start = t_ev_stop = nullptr;
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
   dim3 grid((a.C + BN - 1) / BN, (a.M + BM - 1) / BM);
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), bytes, st, a);
+  hipLaunchKernelGGL(kern, grid, dim3(2 * kThreads), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
@@ -307,7 +521,7 @@ void time_next_gemm(hipEvent_t start, hipEvent_t stop) {
   else { t_ev_start = t_ev_stop = nullptr; }
 }
 
-hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st) { return launch<128, 128, false>(a, st); }
-hipError_t launch_gemm_dx(const GemmArgs& a, hipStream_t st) { return launch<128, 128, true>(a, st); }
+hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st) { return launch<false>(a, st); }
+hipError_t launch_gemm_dx(const GemmArgs& a, hipStream_t st) { return launch<true>(a, st); }
 
 }  // namespace qlora

@@ -60,7 +60,7 @@ extern "C" {
 enum {
   QLORA_OK = 0,
   QLORA_ERR_INVALID_ARG = -1, /* NULL required pointer, negative size, r < 0 */
-  QLORA_ERR_SHAPE = -2,       /* k_in % 64 != 0, n_out % 8 != 0, r > 64, size overflow */
+  QLORA_ERR_SHAPE = -2,       /* k_in % 64 != 0, n_out % 8 != 0, r > 64, n_out*k_in >= 2^32, M*max(n_out,k_in) > 2^30 */
   QLORA_ERR_ALIGN = -3,       /* a device pointer not 16-byte aligned */
   QLORA_ERR_WORKSPACE = -4,   /* workspace pointer NULL or ws_bytes too small */
   QLORA_ERR_HIP = -5          /* a HIP launch or runtime error */
