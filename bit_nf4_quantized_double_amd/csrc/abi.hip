@@ -1,6 +1,7 @@
 // extern "C" entry points of libqlora: argument checks on the host, workspace
 // layout, and the launch sequence of each operation on the caller's stream.
 // Declarations and the contract of every entry point: include/qlora.h.
+#include <algorithm>
 #include <climits>
 #include <cstring>
 #include <string>
@@ -18,9 +19,10 @@ hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_dx(const GemmArgs& a, hipStream_t st);
 void time_next_gemm(hipEvent_t start, hipEvent_t stop);
 hipError_t launch_lora_down(const uint16_t* X, int M, int K, const uint16_t* A, int r, float s, uint16_t* U,
-                            hipStream_t st);
+                            float* part, hipStream_t st);
 hipError_t launch_lora_vt(const uint16_t* dY, int M, int N, const uint16_t* B, int r, float s, uint16_t* V,
-                          hipStream_t st);
+                          float* part, hipStream_t st);
+size_t rowdot_part_bytes(int64_t M, int64_t Kd, int r);
 int coldot_chunk_rows();
 hipError_t launch_coldot(const uint16_t* v, int r, const uint16_t* in, int M, int C, float* part,
                          hipStream_t st);
@@ -99,7 +101,12 @@ BwdLayout bwd_layout(int64_t M, int64_t n_out, int64_t k_in, int32_t r) {
   L.u = 0;
   L.v = L.u + round_up((size_t)M * r * 2);
   L.part = L.v + round_up((size_t)M * r * 2);
-  L.total = L.part + round_up((size_t)L.nmc * r * widest * 4);
+  // the partial-sum region is reused, in stream order, by the U~ and V~
+  // split-K reductions and by the dA / dB token reductions
+  size_t part = (size_t)L.nmc * r * widest * 4;
+  part = std::max(part, qlora::rowdot_part_bytes(M, k_in, r));
+  part = std::max(part, qlora::rowdot_part_bytes(M, n_out, r));
+  L.total = L.part + round_up(part);
   return L;
 }
 
@@ -131,7 +138,8 @@ void qlora_nf4_table(float out[16]) {
 
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, int32_t r) {
   if (M < 0 || n_out < 0 || k_in < 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
-  if (op == QLORA_OP_FWD) return r > 0 ? round_up((size_t)M * r * 2) : 0;
+  if (op == QLORA_OP_FWD)
+    return r > 0 && M > 0 ? round_up((size_t)M * r * 2) + round_up(qlora::rowdot_part_bytes(M, k_in, r)) : 0;
   if (op == QLORA_OP_BWD) return bwd_layout(M, n_out, k_in, r).total;
   return 0;
 }
@@ -171,20 +179,23 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, co
   if (!aligned16(X) || !aligned16(Y)) return fail(QLORA_ERR_ALIGN, "X and Y must be 16-byte aligned");
   if (U_out && !aligned16(U_out)) return fail(QLORA_ERR_ALIGN, "U_out must be 16-byte aligned");
   uint16_t* U = nullptr;
+  float* part = nullptr;
   if (r > 0) {
-    if (U_out) {
-      U = U_out;
-    } else {
-      const size_t need = qlora_workspace_bytes(QLORA_OP_FWD, M, w->n_out, w->k_in, r);
-      if (!ws || ws_bytes < need) return fail(QLORA_ERR_WORKSPACE, "forward workspace too small");
+    // workspace: [U~ when U_out is NULL][split-K partials of U~]
+    const size_t ubytes = U_out ? 0 : round_up((size_t)M * r * 2);
+    const size_t pbytes = qlora::rowdot_part_bytes(M, w->k_in, r);
+    if (ubytes + pbytes > 0) {
+      if (!ws || ws_bytes < ubytes + pbytes) return fail(QLORA_ERR_WORKSPACE, "forward workspace too small");
       if (!aligned16(ws)) return fail(QLORA_ERR_ALIGN, "workspace must be 16-byte aligned");
-      U = static_cast<uint16_t*>(ws);
     }
+    char* base = static_cast<char*>(ws);
+    U = U_out ? U_out : reinterpret_cast<uint16_t*>(base);
+    if (pbytes) part = reinterpret_cast<float*>(base + ubytes);
   }
   const float s = lora_scale(alpha, r);
   hipError_t e;
   if (r > 0 && w->k_in > 0) {
-    e = qlora::launch_lora_down(X, (int)M, (int)w->k_in, A, r, s, U, stream);
+    e = qlora::launch_lora_down(X, (int)M, (int)w->k_in, A, r, s, U, part, stream);
     if (e != hipSuccess) return hip_fail(e, "lora_down launch");
   } else if (r > 0) {
     // k_in == 0: X A^T is an empty sum
@@ -253,11 +264,11 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_
       Ut = const_cast<uint16_t*>(U);
     } else {
       Ut = reinterpret_cast<uint16_t*>(base + L.u);
-      if ((e = qlora::launch_lora_down(X, (int)M, (int)K, A, r, s, Ut, stream)) != hipSuccess)
+      if ((e = qlora::launch_lora_down(X, (int)M, (int)K, A, r, s, Ut, part, stream)) != hipSuccess)
         return hip_fail(e, "lora_down launch");
     }
     // V~ = bf16(s dY B)
-    if ((e = qlora::launch_lora_vt(dY, (int)M, (int)N, B, r, s, Vt, stream)) != hipSuccess)
+    if ((e = qlora::launch_lora_vt(dY, (int)M, (int)N, B, r, s, Vt, part, stream)) != hipSuccess)
       return hip_fail(e, "lora V launch");
     // dB = dY^T U~  (stored [N x r])
     if ((e = qlora::launch_coldot(Ut, r, dY, (int)M, (int)N, part, stream)) != hipSuccess)

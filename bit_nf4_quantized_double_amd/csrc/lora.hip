@@ -13,6 +13,26 @@
 #include "common.h"
 
 namespace qlora {
+
+// K split of the rowdot kernel: enough (row block, split) workgroups to fill
+// the GPU (>= 512), splits of whole 256-wide sub-chunks.
+void rowdot_split(int M, int Kd, int* nsplit, int* kchunk) {
+  const int rb = (M + 63) / 64;
+  const int nsub = std::max(1, (Kd + 255) / 256);
+  int ns = std::min(nsub, std::max(1, (512 + rb - 1) / rb));
+  const int per = (nsub + ns - 1) / ns;
+  ns = (nsub + per - 1) / per;
+  *nsplit = ns;
+  *kchunk = per * 256;
+}
+
+// fp32 partial bytes the rowdot kernel needs for these sizes (0 if unsplit).
+size_t rowdot_part_bytes(int64_t M, int64_t Kd, int r) {
+  int ns, kc;
+  rowdot_split((int)M, (int)Kd, &ns, &kc);
+  return ns > 1 ? (size_t)ns * (size_t)M * (size_t)r * 4u : 0;
+}
+
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) short i16x8;
@@ -20,66 +40,136 @@ typedef __attribute__((ext_vector_type(8))) short i16x8;
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ---------------------------------------------------------------- rowdot ----
-// One 256-thread workgroup per 16 rows; the 4 waves split the reduction in
-// 32-wide chunks and are summed in LDS in a fixed order.
-// w(j, k) = wt[j * ldw + k] if CONTIG (A is [r x K]), else wt[k * ldw + j]
-// (B is [N x r], read down its columns).
+// out[m][j] = bf16(scale * sum_k in[m][k] * w(j, k)), j < r.
+// w(j, k) = wt[j * Kd + k] when CONTIG (A is [r x K]), else wt[k * r + j]
+// (B is [N x r]).
+//
+// Grid (row blocks of 64, K splits).  Each 256-thread workgroup covers 64
+// rows (16 per wave) and one K range, walked in 256-wide sub-chunks: the
+// sub-chunk of w is staged in LDS (A as [j][k], read with ds_read_b128; B as
+// [k][j] -- its rows are contiguous in memory -- read with the transposing
+// ds_read_b64_tr_b16), the activations go straight from global memory into
+// MFMA A-operand registers, eight 16-byte loads in flight per lane.  With
+// one K split the result is rounded and stored directly; otherwise fp32
+// partials [split][m][j] are summed in a fixed order by k_rowdot_finalize.
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kRowdotSub = 256;  // reduction columns per LDS sub-chunk
+
+template <bool CONTIG, int RT>
+struct RowdotLds {
+  // CONTIG: [RT*16][kRowdotSub + 8]; else [kRowdotSub][RT*16 + 8]
+  static constexpr int kPitch = CONTIG ? kRowdotSub + 8 : RT * 16 + 8;
+  static constexpr int kElems = CONTIG ? RT * 16 * kPitch : kRowdotSub * kPitch;
+};
+
 template <bool CONTIG, int RT>
 __global__ __launch_bounds__(256) void k_rowdot(const uint16_t* __restrict__ in, int M, int Kd,
-                                                const uint16_t* __restrict__ wt, int ldw, int r,
-                                                float scale, uint16_t* __restrict__ out) {
-  __shared__ f32x4 red[4][RT][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m0 = blockIdx.x * 16;
+                                                const uint16_t* __restrict__ wt, int r, int kchunk,
+                                                float scale, uint16_t* __restrict__ out,
+                                                float* __restrict__ part) {
+  using Ly = RowdotLds<CONTIG, RT>;
+  __shared__ __attribute__((aligned(16))) uint16_t sw[Ly::kElems];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.x * 64 + 16 * wave;
+  const int split = blockIdx.y;
+  const int k_lo = split * kchunk, k_hi = min(Kd, k_lo + kchunk);
   const int row = lane & 15, kg = lane >> 4;
+  const __amdgpu_buffer_rsrc_t rin = make_rsrc(in, (uint32_t)((uint64_t)M * Kd * 2));
+  const uint32_t row_off = (m0 + row < M) ? (uint32_t)(m0 + row) * (uint32_t)Kd * 2u : kOOB;
+
   f32x4 acc[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nchunks = (Kd + 31) / 32;
-  const bool row_ok = m0 + row < M;
-  for (int ch = wave; ch < nchunks; ch += 4) {
-    const int k = ch * 32 + kg * 8;
-    uint4 av = make_uint4(0, 0, 0, 0);
-    if (row_ok && k < Kd) av = *reinterpret_cast<const uint4*>(in + (int64_t)(m0 + row) * Kd + k);
+
+  for (int k0 = k_lo; k0 < k_hi; k0 += kRowdotSub) {
+    // activations of this sub-chunk: 8 MFMA steps of 32, lane k-group kg
+    uint4 av[8];
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const int j = 16 * t + row;
-      uint4 bv = make_uint4(0, 0, 0, 0);
-      if (j < r && k < Kd) {
-        if (CONTIG) {
-          bv = *reinterpret_cast<const uint4*>(wt + (int64_t)j * ldw + k);
-        } else {
-          uint16_t e[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) e[i] = wt[(int64_t)(k + i) * ldw + j];
-          bv.x = e[0] | ((uint32_t)e[1] << 16);
-          bv.y = e[2] | ((uint32_t)e[3] << 16);
-          bv.z = e[4] | ((uint32_t)e[5] << 16);
-          bv.w = e[6] | ((uint32_t)e[7] << 16);
-        }
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + 32 * u + 8 * kg;
+      av[u] = buf_load16(rin, k < k_hi ? row_off + 2u * (uint32_t)k : kOOB);
+    }
+    // stage w for k0 .. k0 + 255 (zero past r / k_hi)
+    __syncthreads();  // previous sub-chunk's reads of sw are done
+    if (CONTIG) {
+      for (int idx = tid; idx < RT * 16 * (kRowdotSub / 8); idx += 256) {
+        const int j = idx / (kRowdotSub / 8), ch = idx % (kRowdotSub / 8);
+        const int k = k0 + 8 * ch;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (j < r && k < k_hi) v = *reinterpret_cast<const uint4*>(wt + (int64_t)j * Kd + k);
+        *reinterpret_cast<uint4*>(sw + j * Ly::kPitch + 8 * ch) = v;
       }
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc[t], 0, 0, 0);
+    } else if ((r & 7) == 0) {
+      // rows of B are r * 2 bytes, 16-byte aligned: copy 8 ranks at a time
+      for (int idx = tid; idx < kRowdotSub * RT * 2; idx += 256) {
+        const int kk = idx / (RT * 2), c = idx % (RT * 2);
+        const int k = k0 + kk;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (8 * c < r && k < k_hi) v = *reinterpret_cast<const uint4*>(wt + (int64_t)k * r + 8 * c);
+        *reinterpret_cast<uint4*>(sw + kk * Ly::kPitch + 8 * c) = v;
+      }
+    } else {
+      for (int idx = tid; idx < kRowdotSub * RT * 16; idx += 256) {
+        const int kk = idx / (RT * 16), j = idx % (RT * 16);
+        const int k = k0 + kk;
+        sw[kk * Ly::kPitch + j] = (j < r && k < k_hi) ? wt[(int64_t)k * r + j] : (uint16_t)0;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, av[u]);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        bf16x8 b;
+        if (CONTIG) {
+          const uint4 v = *reinterpret_cast<const uint4*>(sw + (16 * t + row) * Ly::kPitch + 32 * u + 8 * kg);
+          b = __builtin_bit_cast(bf16x8, v);
+        } else {
+          // lane p + 4q of k-group kg addresses row kb + q, columns 4p..4p+3
+          // and receives column (lane & 15), rows kb .. kb + 3
+          const int p = row & 3, q = row >> 2;
+          const int kb = 32 * u + 8 * kg + q;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(sw + kb * Ly::kPitch + 16 * t + 4 * p));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(sw + (kb + 4) * Ly::kPitch + 16 * t + 4 * p));
+          const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          b = __builtin_bit_cast(bf16x8, v);
+        }
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[t], 0, 0, 0);
+      }
     }
   }
+  // D[m][j]: m = m0 + 4 * (lane >> 4) + v, j = 16 t + (lane & 15)
 #pragma unroll
-  for (int t = 0; t < RT; ++t) red[wave][t][lane] = acc[t];
-  __syncthreads();
-  if (wave == 0) {
+  for (int t = 0; t < RT; ++t) {
+    const int j = 16 * t + (lane & 15);
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      f32x4 s = red[0][t][lane];
-#pragma unroll
-      for (int w = 1; w < 4; ++w) s += red[w][t][lane];
-      const int j = 16 * t + (lane & 15);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = m0 + 4 * (lane >> 4) + v;
-        if (m < M && j < r) {
-          uint32_t pk = pack_bf16x2(scale * s[v], 0.f);
+    for (int v = 0; v < 4; ++v) {
+      const int m = m0 + 4 * (lane >> 4) + v;
+      if (m < M && j < r) {
+        if (part) {
+          part[((int64_t)split * M + m) * r + j] = acc[t][v];
+        } else {
+          const uint32_t pk = pack_bf16x2(scale * acc[t][v], 0.f);
           out[(int64_t)m * r + j] = (uint16_t)(pk & 0xFFFFu);
         }
       }
     }
+  }
+}
+
+// out[m][j] = bf16(scale * sum_{split} part[split][m][j]), fixed order.
+__global__ __launch_bounds__(256) void k_rowdot_finalize(const float* __restrict__ part, int nsplit, int64_t n,
+                                                         float scale, uint16_t* __restrict__ out) {
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    float s = 0.f;
+    for (int k = 0; k < nsplit; ++k) s += part[(int64_t)k * n + i];
+    const uint32_t pk = pack_bf16x2(scale * s, 0.f);
+    out[i] = (uint16_t)(pk & 0xFFFFu);
   }
 }
 
@@ -184,17 +274,30 @@ __global__ __launch_bounds__(256) void k_zero_u16(uint16_t* __restrict__ p, int6
   for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
 }
 
+template <bool CONTIG, int RT>
+void rowdot_launch(dim3 grid, hipStream_t st, const uint16_t* in, int M, int Kd, const uint16_t* wt, int r,
+                   int kchunk, float scale, uint16_t* out, float* part) {
+  hipLaunchKernelGGL((k_rowdot<CONTIG, RT>), grid, dim3(256), 0, st, in, M, Kd, wt, r, kchunk, scale, out, part);
+}
+
 template <bool CONTIG>
-hipError_t rowdot_dispatch(const uint16_t* in, int M, int Kd, const uint16_t* wt, int ldw, int r, float scale,
-                           uint16_t* out, hipStream_t st) {
-  dim3 grid((M + 15) / 16);
-  const int rt = (r + 15) / 16;
-  switch (rt) {
-    case 1: hipLaunchKernelGGL((k_rowdot<CONTIG, 1>), grid, dim3(256), 0, st, in, M, Kd, wt, ldw, r, scale, out); break;
-    case 2: hipLaunchKernelGGL((k_rowdot<CONTIG, 2>), grid, dim3(256), 0, st, in, M, Kd, wt, ldw, r, scale, out); break;
-    case 3: hipLaunchKernelGGL((k_rowdot<CONTIG, 3>), grid, dim3(256), 0, st, in, M, Kd, wt, ldw, r, scale, out); break;
-    default: hipLaunchKernelGGL((k_rowdot<CONTIG, 4>), grid, dim3(256), 0, st, in, M, Kd, wt, ldw, r, scale, out); break;
+hipError_t rowdot_dispatch(const uint16_t* in, int M, int Kd, const uint16_t* wt, int r, float scale,
+                           uint16_t* out, float* part, hipStream_t st) {
+  int nsplit, kchunk;
+  rowdot_split(M, Kd, &nsplit, &kchunk);
+  dim3 grid((M + 63) / 64, nsplit);
+  float* p = nsplit > 1 ? part : nullptr;
+  switch ((r + 15) / 16) {
+    case 1: rowdot_launch<CONTIG, 1>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p); break;
+    case 2: rowdot_launch<CONTIG, 2>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p); break;
+    case 3: rowdot_launch<CONTIG, 3>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p); break;
+    default: rowdot_launch<CONTIG, 4>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p); break;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit == 1) return e;
+  const int64_t n = (int64_t)M * r;
+  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 2048));
+  hipLaunchKernelGGL(k_rowdot_finalize, dim3(blocks), dim3(256), 0, st, part, nsplit, n, scale, out);
   return hipGetLastError();
 }
 
@@ -202,14 +305,14 @@ hipError_t rowdot_dispatch(const uint16_t* in, int M, int Kd, const uint16_t* wt
 
 // U~ = bf16(s X A^T): in = X [M x K], A [r x K]
 hipError_t launch_lora_down(const uint16_t* X, int M, int K, const uint16_t* A, int r, float s, uint16_t* U,
-                            hipStream_t st) {
-  return rowdot_dispatch<true>(X, M, K, A, K, r, s, U, st);
+                            float* part, hipStream_t st) {
+  return rowdot_dispatch<true>(X, M, K, A, r, s, U, part, st);
 }
 
 // V~ = bf16(s dY B): in = dY [M x N], B [N x r]
 hipError_t launch_lora_vt(const uint16_t* dY, int M, int N, const uint16_t* B, int r, float s, uint16_t* V,
-                          hipStream_t st) {
-  return rowdot_dispatch<false>(dY, M, N, B, r, r, s, V, st);
+                          float* part, hipStream_t st) {
+  return rowdot_dispatch<false>(dY, M, N, B, r, s, V, part, st);
 }
 
 int coldot_chunk_rows() { return 256; }

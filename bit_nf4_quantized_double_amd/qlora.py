@@ -176,7 +176,7 @@ def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor | None, B: torch.T
         Y = torch.empty((M, w.n_out), dtype=torch.bfloat16, device=dev)
     if return_u and r > 0 and U is None:
         U = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
-    wsb = 0 if U is not None else workspace_bytes(QLORA_OP_FWD, M, w.n_out, w.k_in, r)
+    wsb = workspace_bytes(QLORA_OP_FWD, M, w.n_out, w.k_in, r)
     wst, wsn = _ws(wsb, dev, ws)
     cw = w._c()
     st = lib().qlora_linear_fwd(

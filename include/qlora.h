@@ -120,8 +120,11 @@ int qlora_dequant(const qlora_nf4_weight *w, uint16_t *W_bf16, hipStream_t strea
  *          accumulated in fp32, rounded once to bf16.
  *   U_out  optional device bf16 [M, r]: receives U~ (the scaled adapter
  *          activation) for the backward pass; NULL to discard.
- *   ws     device workspace of at least qlora_workspace_bytes(QLORA_OP_FWD,...)
- *          bytes (may be NULL when that is 0).
+ *   ws     device workspace, 16-byte aligned, of qlora_workspace_bytes(
+ *          QLORA_OP_FWD, ...) bytes (always enough; may be NULL when that is
+ *          0).  It holds U~ when U_out is NULL, followed by fp32 split-K
+ *          partial sums of X A^T for large M * k_in; with U_out given the
+ *          partials alone are needed.
  * r == 0 (or A/B NULL with r == 0) gives Y = X W_bf16^T.  M == 0 is a no-op.
  * The dequantized weight is never written to memory.
  */
@@ -144,8 +147,10 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M,
  *   ws       device workspace of qlora_workspace_bytes(QLORA_OP_BWD, ...).
  * Token reductions are deterministic (fixed-order partial sums, no float
  * atomics): repeated calls give bitwise-identical results.
- * r == 0 gives dX = dY W_bf16 and touches neither dA nor dB.  M == 0 writes
- * zeros to dA and dB (when r > 0) and nothing else.
+ * r == 0 gives dX = dY W_bf16 and touches neither dA nor dB.  An empty
+ * token or feature dimension (M, n_out or k_in zero) makes the token
+ * reductions empty sums: dA and dB are zero-filled (when r > 0), dX is
+ * zero-filled when n_out == 0 (and M, k_in > 0), and nothing else is written.
  */
 int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_t *dY,
                      int64_t M, const uint16_t *A, const uint16_t *B, int32_t r,
@@ -153,8 +158,9 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_
                      void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes needed by qlora_linear_fwd (op = QLORA_OP_FWD) or
- * qlora_linear_bwd (op = QLORA_OP_BWD) for these sizes; the bwd figure assumes
- * U == NULL (the worst case).  Returns 0 for invalid arguments. */
+ * qlora_linear_bwd (op = QLORA_OP_BWD) for these sizes: enough for any
+ * U_out / U argument (U_out == NULL, U == NULL is the worst case).  Returns 0
+ * for invalid arguments and when no workspace is needed (r == 0 or M == 0). */
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, int32_t r);
 
 /* Measurement aid.  The next fused-GEMM kernel launch made by the calling
