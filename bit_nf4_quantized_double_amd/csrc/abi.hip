@@ -9,6 +9,7 @@
 #include "../../include/qlora.h"
 #include "common.h"
 #include "gemm_args.h"
+#include "skinny_args.h"
 
 namespace qlora {
 hipError_t launch_quantize(const float* W, int64_t nweights, uint8_t* codes, uint8_t* q8, float* s2,
@@ -200,6 +201,17 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, co
   } else if (r > 0) {
     // k_in == 0: X A^T is an empty sum
     if ((e = qlora::launch_zero_u16(U, M * r, stream)) != hipSuccess) return hip_fail(e, "zero U");
+  }
+  if (M <= qlora::skinny_max_tokens()) {
+    // few tokens: bound by reading the packed weight; decode straight into
+    // MFMA operands, no LDS tile
+    qlora::SkinnyArgs k{};
+    k.X = X; k.codes = w->codes; k.q8 = w->absmax_q8; k.s2 = w->absmax_scale;
+    k.U = U; k.B = B; k.Y = Y;
+    k.M = (int)M; k.N = (int)w->n_out; k.K = (int)w->k_in; k.r = r;
+    k.nf4 = qlora::nf4_consts();
+    e = qlora::launch_skinny_fwd(k, stream);
+    return e == hipSuccess ? QLORA_OK : hip_fail(e, "few-token forward launch");
   }
   qlora::GemmArgs g{};
   g.act = X; g.ld_act = w->k_in; g.M = (int)M; g.R = (int)w->k_in; g.C = (int)w->n_out;

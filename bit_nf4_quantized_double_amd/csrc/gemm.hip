@@ -33,6 +33,7 @@
 // the two lanes sharing a block each build half the table and swap halves
 // with one DPP move.  No LDS traffic for the lookup.
 #include "gemm_args.h"
+#include "nf4_lut.h"
 
 namespace qlora {
 namespace {
@@ -57,63 +58,6 @@ template <bool NN>
 struct Tile {
   static constexpr int kElems = NN ? 64 * kNNPitch : BN * 64;  // bf16 per buffer
 };
-
-// ---- per-block lookup-table decode ----------------------------------------
-struct Lut {
-  uint32_t alo0, alo1, ahi0, ahi1;  // my 8 entries (byte planes)
-  uint32_t blo0, blo1, bhi0, bhi1;  // partner's 8 entries
-};
-
-// Lane parity p: even lanes hold levels 0..7, odd lanes 8..15 (th[]).
-__device__ __forceinline__ Lut build_lut(const float th[8], float a) {
-  const uint32_t p0 = pack_bf16x2(th[0] * a, th[1] * a);
-  const uint32_t p1 = pack_bf16x2(th[2] * a, th[3] * a);
-  const uint32_t p2 = pack_bf16x2(th[4] * a, th[5] * a);
-  const uint32_t p3 = pack_bf16x2(th[6] * a, th[7] * a);
-  Lut L;
-  L.alo0 = __builtin_amdgcn_perm(p1, p0, 0x06040200u);
-  L.ahi0 = __builtin_amdgcn_perm(p1, p0, 0x07050301u);
-  L.alo1 = __builtin_amdgcn_perm(p3, p2, 0x06040200u);
-  L.ahi1 = __builtin_amdgcn_perm(p3, p2, 0x07050301u);
-  // swap with the partner lane (lane ^ 1): DPP quad_perm [1,0,3,2]
-  L.blo0 = __builtin_amdgcn_mov_dpp(L.alo0, 0xB1, 0xF, 0xF, false);
-  L.bhi0 = __builtin_amdgcn_mov_dpp(L.ahi0, 0xB1, 0xF, 0xF, false);
-  L.blo1 = __builtin_amdgcn_mov_dpp(L.alo1, 0xB1, 0xF, 0xF, false);
-  L.bhi1 = __builtin_amdgcn_mov_dpp(L.ahi1, 0xB1, 0xF, 0xF, false);
-  return L;
-}
-
-// Per-lane constants of the lookup: lanes of odd parity own levels 8..15.
-struct LaneMask {
-  uint32_t s;    // xor for my-half indices: 0 (even) or 0x08080808 (odd)
-  uint32_t x;    // xor for partner-half indices: s ^ 0x08080808
-  uint32_t sel;  // base byte selector 0x03020100, bit 2 flipped on odd lanes
-};
-
-// t: bytes hold (code_i | code_{i+1} << 4); the low nibble of byte i is the
-// code of output element i.  Index < 8 after the xor: my half of the table;
-// >= 8: the partner's half.  Returns {w0,w1}, {w2,w3} as bf16 pairs.
-__device__ __forceinline__ void lookup4(const Lut& L, uint32_t t, const LaneMask& lm, uint32_t& o01,
-                                        uint32_t& o23) {
-  const uint32_t s = (t & 0x0F0F0F0Fu) ^ lm.s;
-  const uint32_t x = (t & 0x0F0F0F0Fu) ^ lm.x;
-  const uint32_t sel = ((t >> 1) & 0x04040404u) ^ lm.sel;
-  const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(L.blo1, L.blo0, x),
-                                            __builtin_amdgcn_perm(L.alo1, L.alo0, s), sel);
-  const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(L.bhi1, L.bhi0, x),
-                                            __builtin_amdgcn_perm(L.ahi1, L.ahi0, s), sel);
-  o01 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
-  o23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
-}
-
-// 8 codes (one dword, element 0 in the low nibble) -> 4 dwords of bf16 pairs.
-__device__ __forceinline__ uint4 decode8_lut(const Lut& L, uint32_t d, const LaneMask& lm) {
-  const uint32_t sh = d >> 4;
-  uint4 o;
-  lookup4(L, __builtin_amdgcn_perm(sh, d, 0x05010400u), lm, o.x, o.y);
-  lookup4(L, __builtin_amdgcn_perm(sh, d, 0x07030602u), lm, o.z, o.w);
-  return o;
-}
 
 // ---- global -> register loads (raw buffer loads: out of range reads 0) ----
 struct Srcs {
@@ -157,7 +101,7 @@ __device__ __forceinline__ CodeSeg load_codes(const GemmArgs& a, const Srcs& src
 template <bool NN>
 __device__ __forceinline__ void decode_store(uint16_t* s, const CodeSeg& cs, const float th[8],
                                              const LaneMask& lm, int tid) {
-  const Lut L = build_lut(th, (float)cs.q * cs.s2);  // a' = fp32(q8 * s2)
+  const Lut L = build_lut<LutPartner::kXor1>(th, (float)cs.q * cs.s2);  // a' = fp32(q8 * s2)
   const uint4 w0 = decode8_lut(L, cs.code.x, lm);
   const uint4 w1 = decode8_lut(L, cs.code.y, lm);
   const uint4 w2 = decode8_lut(L, cs.code.z, lm);
@@ -265,7 +209,7 @@ __device__ __forceinline__ void mma_step(f32x16 (&acc)[2][4], const uint16_t* ac
 #pragma unroll
   for (int i = 0; i < 2; ++i) na[i] = load_afrag(act, i, 0, lane);
   Lut L;
-  if (DECODE) L = build_lut(th, (float)cs.q * cs.s2);  // a' = fp32(q8 * s2)
+  if (DECODE) L = build_lut<LutPartner::kXor1>(th, (float)cs.q * cs.s2);  // a' = fp32(q8 * s2)
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     bf16x8 bf[4], af[2];
@@ -393,12 +337,8 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
   if (producer) {
     const bool odd = lane & 1;
     float th[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) th[i] = odd ? a.nf4.level[8 + i] : a.nf4.level[i];
-    LaneMask lm;
-    lm.s = odd ? 0x08080808u : 0u;
-    lm.x = lm.s ^ 0x08080808u;
-    lm.sel = odd ? 0x07060504u : 0x03020100u;
+    lane_levels(a.nf4, odd, th);
+    const LaneMask lm = lane_mask(odd);
     const Srcs src = make_srcs<NN>(a);
     const ActRows rows = act_rows(a, row0, lane);
 

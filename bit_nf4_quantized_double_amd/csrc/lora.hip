@@ -167,7 +167,15 @@ __global__ __launch_bounds__(256) void k_rowdot_finalize(const float* __restrict
                                                          float scale, uint16_t* __restrict__ out) {
   for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     float s = 0.f;
-    for (int k = 0; k < nsplit; ++k) s += part[(int64_t)k * n + i];
+    int k = 0;
+    for (; k + 8 <= nsplit; k += 8) {  // 8 loads in flight, added in split order
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = part[(int64_t)(k + j) * n + i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s += v[j];
+    }
+    for (; k < nsplit; ++k) s += part[(int64_t)k * n + i];
     const uint32_t pk = pack_bf16x2(scale * s, 0.f);
     out[i] = (uint16_t)(pk & 0xFFFFu);
   }

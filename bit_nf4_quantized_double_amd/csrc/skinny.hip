@@ -1,0 +1,295 @@
+// Few-token fused forward of the QLoRA linear (M <= 16 token rows):
+//     Y[m][n] = sum_k X[m][k] * Wbf[n][k] + sum_j U~[m][j] * B[n][j]
+// ([P1] "The mechanism in brief": W x plus (alpha / r) B A x on a frozen
+// 4-bit base; [P4] "The idea in one line": W is dequantized to bf16 only for
+// the product that uses it).
+//
+// With a handful of tokens the layer is bound by reading the packed weight
+// (0.516 B per weight), and decoding it is the only real arithmetic.  Every
+// weight is decoded exactly once, from its codes straight into MFMA operand
+// registers -- no LDS tile, no barrier in the main loop.  The product uses
+// v_mfma_f32_16x16x32_bf16 with 16 W rows on one side and the (zero-padded)
+// 16 tokens on the other.
+//
+// Workgroup: 8 waves (two per SIMD, so up to 256 VGPRs per lane for deep
+// prefetch), `tiles` 16-row W tiles (a tile = 16 output features),
+// the whole reduction length.  Wave (a, b): tiles a*TPW .. a*TPW + TPW - 1
+// of the group, 128-wide reduction chunks b, b + nwk, b + 2 nwk, ...
+// Lane l: W row (l & 15) of a tile, reduction columns 32 (l >> 4) .. + 31 of
+// a chunk -- one 16-byte code load, half of a 64-weight block; lane l ^ 16
+// holds the other half and shares the block's lookup table.  The X fragment
+// of a chunk is loaded once and reused by all TPW tiles of the wave.  At the
+// end, the nwk partial tiles of each output tile are added in LDS in a fixed
+// order (deterministic); the b == 0 wave adds the adapter term first.
+//
+// The reduction index is permuted consistently in both operands (lane group
+// g, dword i of a chunk <-> columns kc + 32 g + 8 i .. + 7, and inside each
+// such group of 8 the order 0,2,4,6,1,3,5,7), which only changes the fp32
+// summation order.
+#include <algorithm>
+
+#include "nf4_lut.h"
+#include "skinny_args.h"
+
+namespace qlora {
+
+namespace {
+
+constexpr int kSkWaves = 8;
+constexpr int kSkThreads = 64 * kSkWaves;
+
+struct SkSeg {
+  uint4 code;  // 32 codes
+  uint32_t q;  // block absmax code
+  float s2;    // group scale
+};
+
+struct SkSrcs {
+  __amdgpu_buffer_rsrc_t codes, q8, s2, X;
+};
+
+template <int TPW, int RD>
+__global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float4 s_red[];  // [tiles][nwk][64]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nwk = 1 << a.nwk_log2;
+  const int wa = wave >> a.nwk_log2, wb = wave & (nwk - 1);
+  const int row = lane & 15, g = lane >> 4;
+  const int nch = (a.K + 127) >> 7;
+
+  const uint32_t nw = (uint32_t)a.N * (uint32_t)a.K;  // < 2^32 (checked on the host)
+  SkSrcs src;
+  src.codes = make_rsrc(a.codes, nw >> 1);
+  src.q8 = make_rsrc(a.q8, nw >> 6);
+  src.s2 = make_rsrc(a.s2, (((nw >> 6) + 255) >> 8) * 4);
+  src.X = make_rsrc(a.X, (uint32_t)a.M * (uint32_t)a.K * 2u);
+
+  // first W row of this lane in tile 0 of the wave; tile t adds 16 rows
+  const int n0 = (blockIdx.x * a.tiles + wa * TPW) * 16 + row;
+  const uint32_t e0 = (uint32_t)n0 * (uint32_t)a.K + 32u * (uint32_t)g;  // weight index at chunk 0
+
+  // Code loads carry no range check of their own: a row past n_out lies past
+  // the end of the codes (reads zeros, or -- if the index wraps -- some other
+  // row's finite weights, into an output row that is never stored), and
+  // columns past k_in (the tail of the last chunk, padding chunks) read the
+  // next row's finite weights, which meet X == 0 there (X loads are range
+  // checked).  Either way nothing reaches a stored output.
+  auto load = [&](int t, int i) {
+    const int c = wb + (i << a.nwk_log2);
+    const uint32_t e = e0 + (uint32_t)t * 16u * (uint32_t)a.K + (uint32_t)c * 128u;
+    SkSeg s;
+    s.code = buf_load16(src.codes, e >> 1);
+    s.q = buf_load1(src.q8, e >> 6);
+    s.s2 = __builtin_bit_cast(float, buf_load4(src.s2, (e >> 14) << 2));
+    return s;
+  };
+  // X fragment of chunk i: tokens m = lane & 15, columns kc + 32 g + 8 j
+  const bool xrow = row < a.M;
+  const uint32_t xoff0 = (uint32_t)row * (uint32_t)a.K * 2u + 64u * (uint32_t)g;
+  auto load_x = [&](int i, uint4 xf[4]) {
+    const int c = wb + (i << a.nwk_log2);
+    const bool ok = xrow && (c < nch) && (c * 128 + 32 * g < a.K);
+    const uint32_t o = xoff0 + (uint32_t)c * 256u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xf[j] = buf_load16(src.X, ok ? o + 16u * j : kOOB);
+  };
+  // The decoded W fragments come out in the element order 0,2,4,6,1,3,5,7 of
+  // each 8-column group (decode8_lut_eo); the X fragment is put in the same
+  // order once per chunk and reused by every tile.
+  auto order_x = [&](const uint4 (&xc)[4], uint4 (&xo)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xo[j] = x_order_even_odd(xc[j]);
+  };
+
+  // lanes l and l ^ 16 share a block: the even row (g even) builds the
+  // entries of the even levels, the odd row those of the odd levels
+  float th[8];
+  lane_levels_parity(a.nf4, g & 1, th);
+  const EoConsts kc = eo_consts();
+
+  f32x4 acc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Issue order is pinned with full scheduling barriers: the X fragment of
+  // chunk i + 1 is requested at the start of chunk i, and the codes of (tile
+  // t, chunk i + RD) right after tile t of chunk i is decoded, so each load
+  // has a whole chunk of decode work to arrive in.  Between two barriers the
+  // MFMAs of tile t - 1 interleave with the decode of tile t.
+  SkSeg ring[RD][TPW];
+  uint4 xa[4], xb[4];
+  load_x(0, xa);
+#pragma unroll
+  for (int d = 0; d < RD; ++d)
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) ring[d][t] = load(t, d);
+  __builtin_amdgcn_sched_barrier(0);
+
+  auto chunk = [&](int i, SkSeg (&rg)[TPW], const uint4 (&xraw)[4], uint4 (&xn)[4]) {
+    uint4 xc[4];
+    order_x(xraw, xc);
+    load_x(i + 1, xn);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const SkSeg cs = rg[t];
+      const Lut L = build_lut<LutPartner::kRows16>(th, (float)cs.q * cs.s2);  // a' = fp32(q8 * s2)
+      const uint4 w0 = decode8_lut_eo(L, cs.code.x, kc);
+      const uint4 w1 = decode8_lut_eo(L, cs.code.y, kc);
+      const uint4 w2 = decode8_lut_eo(L, cs.code.z, kc);
+      const uint4 w3 = decode8_lut_eo(L, cs.code.w, kc);
+      rg[t] = load(t, i + RD);  // the same tile, RD chunks ahead
+      __builtin_amdgcn_sched_barrier(0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w0),
+                                                      __builtin_bit_cast(bf16x8, xc[0]), acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w1),
+                                                      __builtin_bit_cast(bf16x8, xc[1]), acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w2),
+                                                      __builtin_bit_cast(bf16x8, xc[2]), acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w3),
+                                                      __builtin_bit_cast(bf16x8, xc[3]), acc[t], 0, 0, 0);
+    }
+  };
+  // unrolled by U = max(RD, 2): static ring slot (u % RD) and X buffer (u % 2)
+  constexpr int U = RD > 2 ? RD : 2;
+  for (int it = 0; it < a.nci; it += U) {
+#pragma unroll
+    for (int u = 0; u < U; u += 2) {
+      chunk(it + u, ring[u % RD], xa, xb);
+      chunk(it + u + 1, ring[(u + 1) % RD], xb, xa);
+    }
+  }
+
+  // adapter term U~ B^T, once per output tile (by the b == 0 wave): W-side
+  // operand B[n][j], token-side operand U~[m][j], 32 ranks per MFMA
+  if (wb == 0 && a.r > 0) {
+    const bool vec = (a.r & 7) == 0;
+    for (int j0 = 0; j0 < a.r; j0 += 32) {
+      const int j = j0 + 8 * g;
+      uint4 uf = make_uint4(0, 0, 0, 0);
+      if (row < a.M && j < a.r) {
+        const uint16_t* p = a.U + (int64_t)row * a.r + j;
+        if (vec) {
+          uf = *reinterpret_cast<const uint4*>(p);
+        } else {
+          uint16_t v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = j + e < a.r ? p[e] : (uint16_t)0;
+          uf = make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16,
+                          v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int n = n0 + 16 * t;
+        uint4 bf = make_uint4(0, 0, 0, 0);
+        if (n < a.N && j < a.r) {
+          const uint16_t* p = a.B + (int64_t)n * a.r + j;
+          if (vec) {
+            bf = *reinterpret_cast<const uint4*>(p);
+          } else {
+            uint16_t v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = j + e < a.r ? p[e] : (uint16_t)0;
+            bf = make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16,
+                            v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
+          }
+        }
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bf),
+                                                        __builtin_bit_cast(bf16x8, uf), acc[t], 0, 0, 0);
+      }
+    }
+  }
+
+  // partial tiles -> LDS [tile][b][lane], then a fixed-order sum over b
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int tt = wa * TPW + t;
+    s_red[((tt << a.nwk_log2) + wb) * 64 + lane] = float4{acc[t][0], acc[t][1], acc[t][2], acc[t][3]};
+  }
+  __syncthreads();
+  for (int idx = tid; idx < a.tiles * 64; idx += kSkThreads) {
+    const int tt = idx >> 6, l = idx & 63;
+    float4 s = s_red[(tt << a.nwk_log2) * 64 + l];
+    for (int b = 1; b < nwk; ++b) {
+      const float4 v = s_red[((tt << a.nwk_log2) + b) * 64 + l];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    // fragment element v of lane l: W row 4 (l >> 4) + v of the tile, token l & 15
+    const int m = l & 15;
+    const int n = (blockIdx.x * a.tiles + tt) * 16 + 4 * (l >> 4);
+    if (m < a.M && n < a.N) {  // n_out % 8 == 0: the 4 rows are all in range
+      uint2 o;
+      o.x = pack_bf16x2(s.x, s.y);
+      o.y = pack_bf16x2(s.z, s.w);
+      *reinterpret_cast<uint2*>(a.Y + (int64_t)m * a.N + n) = o;
+    }
+  }
+}
+
+template <int TPW, int RD>
+hipError_t sk_launch(const SkinnyArgs& a, int grid, size_t lds, hipStream_t st) {
+  hipLaunchKernelGGL((k_skinny_fwd<TPW, RD>), dim3(grid), dim3(kSkThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Largest M the few-token kernel handles.
+int skinny_max_tokens() { return 16; }
+
+// Work split: about one workgroup per compute unit.  A workgroup takes
+// `tiles` = nwt * TPW W tiles; its 8 waves form nwt tile groups of TPW
+// tiles, each split over nwk = 8 / nwt waves along the reduction.  The
+// prefetch depth RD (chunks ahead) keeps about 8 code loads in flight per
+// lane.  LDS: tiles * nwk KB <= 64 KB.
+hipError_t launch_skinny_fwd(SkinnyArgs a, hipStream_t st) {
+  const int ntiles = (a.N + 15) / 16;
+  const int nch = (a.K + 127) / 128;
+  int num_cu = 256;
+  {
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess) {
+      int v = 0;
+      if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) num_cu = v;
+    }
+  }
+  const int tpg = std::max(1, (ntiles + num_cu - 1) / num_cu);
+  int tpw = std::min(tpg, 8);
+  int nwt = 1;
+  while (nwt * tpw < tpg && nwt < kSkWaves) nwt *= 2;
+  tpw = std::min(8, (tpg + nwt - 1) / nwt);
+  int nwk_log2 = 0;
+  while ((nwt << (nwk_log2 + 1)) <= kSkWaves) ++nwk_log2;
+  const int nwk = 1 << nwk_log2;
+  int nci = (nch + nwk - 1) / nwk;
+  int rd = tpw >= 5 ? 1 : (tpw >= 3 ? 2 : (tpw == 2 ? 4 : 8));
+  while (rd > 2 && nci % rd) rd /= 2;
+  const int unroll = std::max(rd, 2);
+  nci = (nci + unroll - 1) / unroll * unroll;  // padding chunks read nothing and add zeros
+  a.tiles = nwt * tpw;
+  a.nwk_log2 = nwk_log2;
+  a.nci = nci;
+  const int grid = (ntiles + a.tiles - 1) / a.tiles;
+  const size_t lds = (size_t)a.tiles * nwk * 64 * sizeof(float4);
+  switch (tpw * 16 + rd) {
+    case 1 * 16 + 1: return sk_launch<1, 1>(a, grid, lds, st);
+    case 1 * 16 + 2: return sk_launch<1, 2>(a, grid, lds, st);
+    case 1 * 16 + 4: return sk_launch<1, 4>(a, grid, lds, st);
+    case 1 * 16 + 8: return sk_launch<1, 8>(a, grid, lds, st);
+    case 2 * 16 + 1: return sk_launch<2, 1>(a, grid, lds, st);
+    case 2 * 16 + 2: return sk_launch<2, 2>(a, grid, lds, st);
+    case 2 * 16 + 4: return sk_launch<2, 4>(a, grid, lds, st);
+    case 3 * 16 + 1: return sk_launch<3, 1>(a, grid, lds, st);
+    case 3 * 16 + 2: return sk_launch<3, 2>(a, grid, lds, st);
+    case 4 * 16 + 1: return sk_launch<4, 1>(a, grid, lds, st);
+    case 4 * 16 + 2: return sk_launch<4, 2>(a, grid, lds, st);
+    case 5 * 16 + 1: return sk_launch<5, 1>(a, grid, lds, st);
+    case 6 * 16 + 1: return sk_launch<6, 1>(a, grid, lds, st);
+    case 7 * 16 + 1: return sk_launch<7, 1>(a, grid, lds, st);
+    case 8 * 16 + 1: return sk_launch<8, 1>(a, grid, lds, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace qlora

@@ -1,0 +1,26 @@
+// Arguments of the few-token fused forward kernel (skinny.hip).
+#pragma once
+
+#include "common.h"
+
+namespace qlora {
+
+struct SkinnyArgs {
+  const uint16_t* X;  // [M x K] bf16 tokens
+  const uint8_t* codes;
+  const uint8_t* q8;
+  const float* s2;
+  const uint16_t* U;  // [M x r] bf16 scaled adapter activation, or null (r == 0)
+  const uint16_t* B;  // [N x r] bf16, or null (r == 0)
+  uint16_t* Y;        // [M x N] bf16, written
+  int M, N, K, r;
+  int tiles;          // W tiles per workgroup (= nwt * TPW); set by the launcher
+  int nwk_log2;       // log2 of the waves sharing one tile group; set by the launcher
+  int nci;            // chunk iterations per wave; set by the launcher
+  Nf4Consts nf4;
+};
+
+int skinny_max_tokens();
+hipError_t launch_skinny_fwd(SkinnyArgs a, hipStream_t st);
+
+}  // namespace qlora

@@ -212,6 +212,38 @@ def test_forward_parity(M, N, K, r, alpha):
     assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16))
 
 
+# Few-token forward (M <= 16 runs a dedicated kernel): partial 16-row tiles
+# (n_out % 16 == 8), half 128-wide chunks (k_in % 128 == 64), ranks that are
+# not multiples of 8, and tile counts that select every work split (1 to 8
+# tiles per wave, 1 to 8 waves per reduction).
+FEW_SHAPES = [
+    (1, 8, 64, 0, 0.0),
+    (2, 264, 192, 3, 6.0),
+    (5, 1000, 384, 16, 32.0),
+    (16, 4104, 320, 64, 128.0),
+    (7, 40000, 128, 8, 16.0),
+    (16, 28672, 64, 16, 32.0),
+    (3, 32768, 64, 5, 8.0),
+    (16, 2048, 1088, 32, 64.0),
+    (11, 512, 4096, 0, 0.0),
+]
+
+
+@pytest.mark.parametrize("M,N,K,r,alpha", FEW_SHAPES)
+def test_few_token_forward_parity(M, N, K, r, alpha):
+    _need_gpu()
+    d, q, wb = _case(M, N, K, r, seed=M * 13 + N + K)
+    w = gpu_quantize(d["W"])
+    X, A, B, _ = _dev_inputs(d, r)
+    Y, U = qlora.linear_fwd(w, X, A, B, r, alpha)
+    torch.cuda.synchronize()
+    Yr, _ = oracle.linear_fwd(wb, d["X"], d["A"], d["B"], alpha, r)
+    check_close(f64(Y), Yr, "Y")
+    Y2, _ = qlora.linear_fwd(w, X, A, B, r, alpha, return_u=False)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16))
+
+
 @pytest.mark.parametrize("M,N,K,r,alpha", SHAPES)
 def test_backward_parity(M, N, K, r, alpha):
     _need_gpu()
