@@ -36,6 +36,11 @@
 #include "nf4_lut.h"
 
 namespace qlora {
+
+// Pending measurement request of qlora_time_next_gemm (thread-local): the
+// events to record around the next fused-GEMM launch; taking clears it.
+void take_gemm_events(hipEvent_t& start, hipEvent_t& stop);
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -443,8 +448,8 @@ template <bool NN>
 hipError_t launch(const GemmArgs& a, hipStream_t st) {
   auto kern = k_gemm_nf4<NN>;
   hipError_t e;
-  hipEvent_t ev0 = t_ev_start, ev1 = t_ev_stop;
-  t_ev_start = t_ev_stop = nullptr;
+  hipEvent_t ev0, ev1;
+  take_gemm_events(ev0, ev1);
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
   dim3 grid((a.C + BN - 1) / BN, (a.M + BM - 1) / BM);
   hipLaunchKernelGGL(kern, grid, dim3(2 * kThreads), 0, st, a);
@@ -455,6 +460,12 @@ hipError_t launch(const GemmArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+void take_gemm_events(hipEvent_t& start, hipEvent_t& stop) {
+  start = t_ev_start;
+  stop = t_ev_stop;
+  t_ev_start = t_ev_stop = nullptr;
+}
 
 void time_next_gemm(hipEvent_t start, hipEvent_t stop) {
   if (start && stop) { t_ev_start = start; t_ev_stop = stop; }

@@ -33,6 +33,8 @@
 
 namespace qlora {
 
+void take_gemm_events(hipEvent_t& start, hipEvent_t& stop);  // gemm.hip
+
 namespace {
 
 constexpr int kSkWaves = 8;
@@ -229,8 +231,14 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
 
 template <int TPW, int RD>
 hipError_t sk_launch(const SkinnyArgs& a, int grid, size_t lds, hipStream_t st) {
+  hipEvent_t ev0, ev1;
+  take_gemm_events(ev0, ev1);
+  hipError_t e;
+  if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
   hipLaunchKernelGGL((k_skinny_fwd<TPW, RD>), dim3(grid), dim3(kSkThreads), lds, st, a);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
 }  // namespace

@@ -20,9 +20,10 @@
  * - Every device pointer must be 16-byte aligned.
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *   the call returns without waiting for it.  Nothing is synchronised.  Calls
- *   are re-entrant: no state is written between calls (the NF4 table is
+ *   are re-entrant: no state is kept between calls (the NF4 table is
  *   computed once on the host under std::call_once and passed to kernels by
- *   value).
+ *   value), except the thread-local measurement request of
+ *   qlora_time_next_gemm.
  * - Inputs are never written.  Outputs are fully overwritten (never
  *   accumulated into).
  * - Return value: QLORA_OK or a negative status; qlora_last_error() gives a
@@ -126,7 +127,9 @@ int qlora_dequant(const qlora_nf4_weight *w, uint16_t *W_bf16, hipStream_t strea
  *          partial sums of X A^T for large M * k_in; with U_out given the
  *          partials alone are needed.
  * r == 0 (or A/B NULL with r == 0) gives Y = X W_bf16^T.  M == 0 is a no-op.
- * The dequantized weight is never written to memory.
+ * The dequantized weight is never written to memory.  M <= 16 runs a
+ * dedicated few-token kernel (bound by reading the packed weight); the
+ * result contract is the same, only the fp32 summation order differs.
  */
 int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M,
                      const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
@@ -164,8 +167,9 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, int32_t r);
 
 /* Measurement aid.  The next fused-GEMM kernel launch made by the calling
- * thread (the forward GEMM inside qlora_linear_fwd or the dX GEMM inside
- * qlora_linear_bwd) is bracketed by hipEventRecord(start) and
+ * thread (the forward kernel inside qlora_linear_fwd -- the GEMM, or for
+ * M <= 16 the few-token kernel -- or the dX GEMM inside qlora_linear_bwd)
+ * is bracketed by hipEventRecord(start) and
  * hipEventRecord(stop) on that call's stream, so hipEventElapsedTime gives
  * the duration of that one kernel.  The request is then cleared.  Passing
  * NULL for either event clears a pending request.  Events are caller-owned;
