@@ -67,6 +67,7 @@ struct Tile {
 // ---- global -> register loads (raw buffer loads: out of range reads 0) ----
 struct Srcs {
   __amdgpu_buffer_rsrc_t act, codes, q8, s2;
+  __amdgpu_buffer_rsrc_t lora_act, lora_w;  // U~ or V~ [M x r]; B [C x r] (NT) or A [r x K] (NN)
 };
 
 template <bool NN>
@@ -79,7 +80,24 @@ __device__ __forceinline__ Srcs make_srcs(const GemmArgs& a) {
   s.codes = make_rsrc(a.codes, (uint32_t)(wn >> 1));
   s.q8 = make_rsrc(a.q8, nb);
   s.s2 = make_rsrc(a.s2, ((nb + 255) >> 8) * 4);
+  s.lora_act = make_rsrc(a.lora_act, (uint32_t)((uint64_t)a.M * a.r * 2));
+  s.lora_w = make_rsrc(a.lora_w, (uint32_t)((uint64_t)(NN ? a.K : a.C) * a.r * 2));
   return s;
+}
+
+// 8 consecutive bf16 starting at element e of a buffer, of which the first
+// `valid` (clamped to 0..8) are real and the rest read as zero; nothing at
+// all when !ok.  vec: e is a multiple of 8 (one 16-byte load); otherwise the
+// elements are loaded one by one (all loads independent).
+__device__ __forceinline__ uint4 load_bf16x8(__amdgpu_buffer_rsrc_t r, uint32_t e, bool ok, int valid,
+                                             bool vec) {
+  if (!ok || valid <= 0) return make_uint4(0, 0, 0, 0);
+  if (vec && valid >= 8) return buf_load16(r, 2u * e);
+  uint32_t h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    h[i] = i < valid ? __builtin_amdgcn_raw_buffer_load_b16(r, 2u * (e + i), 0, 0) : 0u;
+  return make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
 }
 
 // Codes of the 32 weights this thread decodes for the step starting at r0.
@@ -267,16 +285,22 @@ __device__ __forceinline__ void step_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
-// give each XCD a contiguous run of tiles (row-major over column tiles): the
-// workgroups resident on one XCD then share activation rows in its L2.
+// XCD-aware tile order.  Workgroups are dealt round-robin to the 8 XCDs, so
+// lin % 8 picks the XCD; each XCD gets a contiguous run t of the tile order
+// below.  Tiles are ordered in bands of 2 row blocks, column-major inside a
+// band: with 8 row blocks (2048 tokens) an XCD owns 2 row blocks x half the
+// column tiles, so its L2 is shared by 2 activation row blocks and half the
+// weight (instead of 1 row block and the whole weight).
 __device__ __forceinline__ void tile_coords(int& tm, int& tn) {
-  const int nt = gridDim.x, total = gridDim.x * gridDim.y;
-  const int lin = blockIdx.x + blockIdx.y * gridDim.x;
-  int t = lin;
-  if (total % 8 == 0) t = (lin % 8) * (total / 8) + lin / 8;
-  tm = t / nt;
-  tn = t % nt;
+  constexpr int RB = 2;  // row blocks per band
+  const int nt = gridDim.x, mt = gridDim.y, total = nt * mt;
+  const int lin = blockIdx.x + blockIdx.y * nt;
+  const int t = (total % 8 == 0) ? (lin % 8) * (total / 8) + lin / 8 : lin;
+  const int band = t / (RB * nt);
+  const int rows = min(RB, mt - band * RB);  // the last band may be partial
+  const int within = t - band * RB * nt;
+  tn = within / rows;
+  tm = band * RB + within % rows;
 }
 
 // Wave-specialised workgroup of 8 waves, two per SIMD:
@@ -318,16 +342,11 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
   const int nsteps = (a.R + 63) / 64;
   // step count rounded up to even (an all-zero step adds nothing)
   const int nst = (nsteps + 1) & ~1;
-  // Each column tile starts its reduction at a different step (rotation by
-  // the tile index) so the workgroups of one XCD do not all read the same
-  // column slice at the same time.  The per-tile summation order stays fixed,
-  // so results are deterministic.
-  const int rot = nst > 0 ? (tn * 5) % nst : 0;
+  // All tiles walk the reduction in the same order, so the workgroups of
+  // one XCD read the same activation / weight slices at about the same time
+  // and share them in L2.
   auto kofs = [&](int step) {  // reduction offset of logical step; >= R past the end
-    if (step >= nst) return nst * 64;
-    int p = step + rot;
-    p -= p >= nst ? nst : 0;
-    return p * 64;
+    return (step >= nst ? nst : step) * 64;
   };
   auto stage_of = [](int step) { return step % kActStages; };
 
@@ -394,24 +413,47 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
     uint16_t* sw = w_buf0;
     uint16_t* sa = act_ptr(stage_of(nst));
     if (producer) {
-      for (int idx = ptid; idx < BN * 64; idx += kThreads) {
+      const Srcs src = make_srcs<NN>(a);
+      // All loads of the fill are issued before any LDS store (16-byte
+      // chunks of 8 ranks; out of range reads zero), so the fill costs one
+      // memory latency, not one per element.
+      const bool vec = (a.r & 7) == 0;
+      // W-side operand: NT: B[n][j] -> sw[col][j]; NN: A[j][c] -> sw[j][col]
+      uint4 wv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int idx = ptid + u * kThreads;  // 0 .. 1023 chunk slots
         if (!NN) {
-          const int col = idx >> 6, j = idx & 63;
-          const int n = c0 + col;
-          const uint16_t v = (n < a.C && j < a.r) ? a.lora_w[(int64_t)n * a.r + j] : (uint16_t)0;
-          sw[kt_off(col, j >> 3) + (j & 7)] = v;
+          const int col = idx >> 3, jc = idx & 7, n = c0 + col;
+          wv[u] = load_bf16x8(src.lora_w, (uint32_t)n * (uint32_t)a.r + 8u * jc, n < a.C, a.r - 8 * jc, vec);
         } else {
-          const int j = idx / BN, col = idx % BN;
-          const int c = c0 + col;
-          const uint16_t v = (c < a.C && j < a.r) ? a.lora_w[(int64_t)j * a.K + c] : (uint16_t)0;
-          sw[nn_off(j, col)] = v;
+          const int j = idx >> 4, cc = idx & 15, c = c0 + 8 * cc;
+          wv[u] = load_bf16x8(src.lora_w, (uint32_t)j * (uint32_t)a.K + (uint32_t)c, j < a.r && c < a.C, 8, true);
         }
       }
-      for (int idx = lane; idx < 64 * 64; idx += 64) {
-        const uint32_t r = idx >> 6, j = idx & 63;
-        const int m = row0 + (int)r;
-        const uint16_t v = (m < a.M && (int)j < a.r) ? a.lora_act[(int64_t)m * a.r + j] : (uint16_t)0;
-        sa[r * 64u + (((j >> 3) ^ swz(r)) << 3) + (j & 7)] = v;
+      // token-side operand: U~ / V~ rows of this producer's consumer slice
+      uint4 av[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = lane + 64 * u;  // 0 .. 511: row idx >> 3, chunk idx & 7
+        const int rr = idx >> 3, jc = idx & 7, m = row0 + rr;
+        av[u] = load_bf16x8(src.lora_act, (uint32_t)m * (uint32_t)a.r + 8u * jc, m < a.M, a.r - 8 * jc, vec);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int idx = ptid + u * kThreads;
+        if (!NN) {
+          const int col = idx >> 3, jc = idx & 7;
+          *reinterpret_cast<uint4*>(sw + kt_off(col, jc)) = wv[u];
+        } else {
+          const int j = idx >> 4, cc = idx & 15;
+          *reinterpret_cast<uint4*>(sw + nn_off(j, 8 * cc)) = wv[u];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t idx = lane + 64u * u, rr = idx >> 3, jc = idx & 7;
+        *reinterpret_cast<uint4*>(sa + rr * 64u + ((jc ^ swz(rr)) << 3)) = av[u];
       }
     }
     __syncthreads();
