@@ -55,9 +55,15 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 __device__ __forceinline__ uint32_t kt_off(uint32_t row, uint32_t chunk) {
   return row * 64u + ((chunk ^ swz(row)) << 3);
 }
-// NN W tile: 64 rows of BN bf16, padded by 16 elements.
+// NN W tile: 64 rows of BN bf16, padded by 16 elements; the 16-byte chunks of
+// the upper half of a row have bit 0 of their index flipped.  With 32 LDS
+// banks this makes both the producers' ds_write_b128 (4 threads per row at
+// 64-byte stride) and the consumers' transposing ds_read_b64_tr_b16
+// conflict-free.
 constexpr int kNNPitch = BN + 16;
-__device__ __forceinline__ uint32_t nn_off(uint32_t row, uint32_t col) { return row * kNNPitch + col; }
+__device__ __forceinline__ uint32_t nn_off(uint32_t row, uint32_t col) {
+  return row * kNNPitch + ((((col >> 3) ^ (col >> 6)) << 3) | (col & 7));
+}
 
 template <bool NN>
 struct Tile {
@@ -130,11 +136,11 @@ __device__ __forceinline__ void decode_store(uint16_t* s, const CodeSeg& cs, con
   const uint4 w2 = decode8_lut(L, cs.code.z, lm);
   const uint4 w3 = decode8_lut(L, cs.code.w, lm);
   if (NN) {
-    uint16_t* p = s + nn_off(tid >> 2, (tid & 3) * 32);
-    reinterpret_cast<uint4*>(p)[0] = w0;
-    reinterpret_cast<uint4*>(p)[1] = w1;
-    reinterpret_cast<uint4*>(p)[2] = w2;
-    reinterpret_cast<uint4*>(p)[3] = w3;
+    const int row = tid >> 2, c = (tid & 3) * 32;
+    *reinterpret_cast<uint4*>(s + nn_off(row, c + 0)) = w0;
+    *reinterpret_cast<uint4*>(s + nn_off(row, c + 8)) = w1;
+    *reinterpret_cast<uint4*>(s + nn_off(row, c + 16)) = w2;
+    *reinterpret_cast<uint4*>(s + nn_off(row, c + 24)) = w3;
   } else {
     const int row = tid >> 1, c = (tid & 1) * 4;
     *reinterpret_cast<uint4*>(s + kt_off(row, c + 0)) = w0;
