@@ -133,8 +133,8 @@ def main():
         e["dX"] = torch.empty((M, lin.k_in), dtype=torch.bfloat16, device=dev)
         e["dA"] = torch.empty((r, lin.k_in), dtype=torch.float32, device=dev)
         e["dB"] = torch.empty((lin.n_out, r), dtype=torch.float32, device=dev)
-        e["ws"] = torch.empty(max(1, qlora.workspace_bytes(qlora.QLORA_OP_BWD, M, lin.n_out, lin.k_in, r)),
-                              dtype=torch.uint8, device=dev)
+        e["ws"] = qlora.new_workspace(qlora.QLORA_OP_BWD, M, lin.n_out, lin.k_in, r, dev)
+        e["ws_fwd"] = qlora.new_workspace(qlora.QLORA_OP_FWD, M, lin.n_out, lin.k_in, r, dev)
         lins.append(e)
     torch.cuda.synchronize()
     step_flops = sum(flops_linear(M, e["n"], e["k"], r) for e in lins)
@@ -150,7 +150,7 @@ def main():
                 a, b = pool.pop(), pool.pop()
                 timing["fwd"].append((a, b, e))
                 L.qlora_time_next_gemm(a, b)
-            qlora.linear_fwd(e["w"], e["X"], e["A"], e["B"], r, alpha, Y=e["Y"], U=e["U"])
+            qlora.linear_fwd(e["w"], e["X"], e["A"], e["B"], r, alpha, Y=e["Y"], U=e["U"], ws=e["ws_fwd"])
             if timing is not None:
                 a, b = pool.pop(), pool.pop()
                 timing["dx"].append((a, b, e))
@@ -281,12 +281,13 @@ def bench_secondary(torch, qlora, synth, dev, evs, reps=10):
                 B = torch.from_numpy(d["B"].view(np.int16)).view(torch.bfloat16).to(dev)
                 Y = torch.empty((m, lin.n_out), dtype=torch.bfloat16, device=dev)
                 U = torch.empty((m, rr), dtype=torch.bfloat16, device=dev)
+                ws = qlora.new_workspace(qlora.QLORA_OP_FWD, m, lin.n_out, lin.k_in, rr, dev)
                 for c in copies:
-                    qlora.linear_fwd(c, X, A, B, rr, alpha, Y=Y, U=U)
+                    qlora.linear_fwd(c, X, A, B, rr, alpha, Y=Y, U=U, ws=ws)
                 torch.cuda.synchronize()
                 a.record()
                 for i in range(reps * 3):
-                    qlora.linear_fwd(copies[i % 3], X, A, B, rr, alpha, Y=Y, U=U)
+                    qlora.linear_fwd(copies[i % 3], X, A, B, rr, alpha, Y=Y, U=U, ws=ws)
                 b.record()
                 torch.cuda.synchronize()
                 us = 1e3 * a.elapsed_time(b) / (reps * 3)

@@ -50,9 +50,13 @@ struct SkSrcs {
   __amdgpu_buffer_rsrc_t codes, q8, s2, X;
 };
 
-template <int TPW, int RD>
+// SL: the workgroup's block scales (absmax codes of its rows, and the
+// second-level scales they use) are staged in LDS once, with coalesced loads,
+// instead of two scattered small loads per 32 weights.
+template <int TPW, int RD, bool SL>
 __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float4 s_red[];  // [tiles][nwk][64]
+  extern __shared__ __attribute__((aligned(16))) float4 s_dyn[];
+  float4* const s_red = s_dyn;  // [tiles][nwk][64], used after the main loop
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nwk = 1 << a.nwk_log2;
   const int wa = wave >> a.nwk_log2, wb = wave & (nwk - 1);
@@ -68,6 +72,31 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
 
   // first W row of this lane in tile 0 of the wave; tile t adds 16 rows
   const int n0 = (blockIdx.x * a.tiles + wa * TPW) * 16 + row;
+
+  // staged scales: q8 of the workgroup's rows [rowbase, rowbase + 16 tiles),
+  // all blocks of each row (nbr per row), then the s2 values they refer to
+  const int nbr = a.K >> 6;
+  const uint32_t qbase = (uint32_t)blockIdx.x * (uint32_t)a.tiles * 16u * (uint32_t)nbr;  // first block
+  const uint32_t qbytes = (uint32_t)a.tiles * 16u * (uint32_t)nbr;                       // multiple of 16
+  const uint32_t g_first = qbase >> 8;
+  const uint8_t* const s_q8 = reinterpret_cast<const uint8_t*>(s_dyn);
+  const float* const s_s2 = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(s_dyn) + qbytes);
+  if (SL) {
+    uint8_t* q8w = reinterpret_cast<uint8_t*>(s_dyn);
+    float* s2w = reinterpret_cast<float*>(q8w + qbytes);
+    const uint32_t ngs = ((qbase + qbytes - 1) >> 8) - g_first + 1;
+    for (uint32_t i = tid; i < qbytes / 16; i += kSkThreads)
+      *reinterpret_cast<uint4*>(q8w + 16 * i) = buf_load16(src.q8, qbase + 16 * i);
+    for (uint32_t i = tid; i < ngs; i += kSkThreads)
+      s2w[i] = __builtin_bit_cast(float, buf_load4(src.s2, (g_first + i) * 4));
+    __syncthreads();
+  }
+  // block scale a' = fp32(q8 * s2) of tile t, chunk c for this lane
+  auto lds_scale = [&](int t, int c) {
+    const int blk = min(2 * c + (g >> 1), nbr - 1);  // padding chunks: any finite scale
+    const uint32_t bl = (uint32_t)((wa * TPW + t) * 16 + row) * (uint32_t)nbr + (uint32_t)blk;
+    return (float)s_q8[bl] * s_s2[((qbase + bl) >> 8) - g_first];
+  };
   const uint32_t e0 = (uint32_t)n0 * (uint32_t)a.K + 32u * (uint32_t)g;  // weight index at chunk 0
 
   // Code loads carry no range check of their own: a row past n_out lies past
@@ -81,8 +110,13 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
     const uint32_t e = e0 + (uint32_t)t * 16u * (uint32_t)a.K + (uint32_t)c * 128u;
     SkSeg s;
     s.code = buf_load16(src.codes, e >> 1);
-    s.q = buf_load1(src.q8, e >> 6);
-    s.s2 = __builtin_bit_cast(float, buf_load4(src.s2, (e >> 14) << 2));
+    if (!SL) {
+      s.q = buf_load1(src.q8, e >> 6);
+      s.s2 = __builtin_bit_cast(float, buf_load4(src.s2, (e >> 14) << 2));
+    } else {
+      s.q = 0;
+      s.s2 = 0.f;
+    }
     return s;
   };
   // X fragment of chunk i: tokens m = lane & 15, columns kc + 32 g + 8 j
@@ -131,11 +165,18 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
     uint4 xc[4];
     order_x(xraw, xc);
     load_x(i + 1, xn);
+    float sc[TPW];
+    if (SL) {
+      const int c = wb + (i << a.nwk_log2);
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) sc[t] = lds_scale(t, c);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       const SkSeg cs = rg[t];
-      const Lut L = build_lut<LutPartner::kRows16>(th, (float)cs.q * cs.s2);  // a' = fp32(q8 * s2)
+      const float scale = SL ? sc[t] : (float)cs.q * cs.s2;  // a' = fp32(q8 * s2)
+      const Lut L = build_lut<LutPartner::kRows16>(th, scale);
       const uint4 w0 = decode8_lut_eo(L, cs.code.x, kc);
       const uint4 w1 = decode8_lut_eo(L, cs.code.y, kc);
       const uint4 w2 = decode8_lut_eo(L, cs.code.z, kc);
@@ -203,7 +244,9 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
     }
   }
 
-  // partial tiles -> LDS [tile][b][lane], then a fixed-order sum over b
+  // partial tiles -> LDS [tile][b][lane] (over the staged scales: wait for
+  // every wave to leave the main loop), then a fixed-order sum over b
+  __syncthreads();
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int tt = wa * TPW + t;
@@ -230,12 +273,13 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
 }
 
 template <int TPW, int RD>
-hipError_t sk_launch(const SkinnyArgs& a, int grid, size_t lds, hipStream_t st) {
+hipError_t sk_launch(const SkinnyArgs& a, int grid, size_t lds, bool sl, hipStream_t st) {
   hipEvent_t ev0, ev1;
   take_gemm_events(ev0, ev1);
   hipError_t e;
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_skinny_fwd<TPW, RD>), dim3(grid), dim3(kSkThreads), lds, st, a);
+  if (sl) hipLaunchKernelGGL((k_skinny_fwd<TPW, RD, true>), dim3(grid), dim3(kSkThreads), lds, st, a);
+  else hipLaunchKernelGGL((k_skinny_fwd<TPW, RD, false>), dim3(grid), dim3(kSkThreads), lds, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
   return hipSuccess;
@@ -279,23 +323,28 @@ hipError_t launch_skinny_fwd(SkinnyArgs a, hipStream_t st) {
   a.nwk_log2 = nwk_log2;
   a.nci = nci;
   const int grid = (ntiles + a.tiles - 1) / a.tiles;
-  const size_t lds = (size_t)a.tiles * nwk * 64 * sizeof(float4);
+  const size_t red = (size_t)a.tiles * nwk * 64 * sizeof(float4);
+  // staged scales: q8 of 16 * tiles rows plus the s2 groups they span
+  const size_t qbytes = (size_t)a.tiles * 16 * (size_t)(a.K / 64);
+  const size_t sbytes = qbytes + 4 * (qbytes / 256 + 2);
+  const bool sl = a.K >= 64 && sbytes <= 60 * 1024;  // stays within the default 64 KB of dynamic LDS
+  const size_t lds = std::max(red, sl ? sbytes : (size_t)0);
   switch (tpw * 16 + rd) {
-    case 1 * 16 + 1: return sk_launch<1, 1>(a, grid, lds, st);
-    case 1 * 16 + 2: return sk_launch<1, 2>(a, grid, lds, st);
-    case 1 * 16 + 4: return sk_launch<1, 4>(a, grid, lds, st);
-    case 1 * 16 + 8: return sk_launch<1, 8>(a, grid, lds, st);
-    case 2 * 16 + 1: return sk_launch<2, 1>(a, grid, lds, st);
-    case 2 * 16 + 2: return sk_launch<2, 2>(a, grid, lds, st);
-    case 2 * 16 + 4: return sk_launch<2, 4>(a, grid, lds, st);
-    case 3 * 16 + 1: return sk_launch<3, 1>(a, grid, lds, st);
-    case 3 * 16 + 2: return sk_launch<3, 2>(a, grid, lds, st);
-    case 4 * 16 + 1: return sk_launch<4, 1>(a, grid, lds, st);
-    case 4 * 16 + 2: return sk_launch<4, 2>(a, grid, lds, st);
-    case 5 * 16 + 1: return sk_launch<5, 1>(a, grid, lds, st);
-    case 6 * 16 + 1: return sk_launch<6, 1>(a, grid, lds, st);
-    case 7 * 16 + 1: return sk_launch<7, 1>(a, grid, lds, st);
-    case 8 * 16 + 1: return sk_launch<8, 1>(a, grid, lds, st);
+    case 1 * 16 + 1: return sk_launch<1, 1>(a, grid, lds, sl, st);
+    case 1 * 16 + 2: return sk_launch<1, 2>(a, grid, lds, sl, st);
+    case 1 * 16 + 4: return sk_launch<1, 4>(a, grid, lds, sl, st);
+    case 1 * 16 + 8: return sk_launch<1, 8>(a, grid, lds, sl, st);
+    case 2 * 16 + 1: return sk_launch<2, 1>(a, grid, lds, sl, st);
+    case 2 * 16 + 2: return sk_launch<2, 2>(a, grid, lds, sl, st);
+    case 2 * 16 + 4: return sk_launch<2, 4>(a, grid, lds, sl, st);
+    case 3 * 16 + 1: return sk_launch<3, 1>(a, grid, lds, sl, st);
+    case 3 * 16 + 2: return sk_launch<3, 2>(a, grid, lds, sl, st);
+    case 4 * 16 + 1: return sk_launch<4, 1>(a, grid, lds, sl, st);
+    case 4 * 16 + 2: return sk_launch<4, 2>(a, grid, lds, sl, st);
+    case 5 * 16 + 1: return sk_launch<5, 1>(a, grid, lds, sl, st);
+    case 6 * 16 + 1: return sk_launch<6, 1>(a, grid, lds, sl, st);
+    case 7 * 16 + 1: return sk_launch<7, 1>(a, grid, lds, sl, st);
+    case 8 * 16 + 1: return sk_launch<8, 1>(a, grid, lds, sl, st);
     default: return hipErrorInvalidValue;
   }
 }

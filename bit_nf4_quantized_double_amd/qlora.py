@@ -156,7 +156,13 @@ def dequant(w: NF4Weight, out: torch.Tensor | None = None) -> torch.Tensor:
     return out
 
 
+def new_workspace(op: int, M: int, n_out: int, k_in: int, r: int, device) -> torch.Tensor:
+    """A workspace for `op` at these sizes (reusable across calls)."""
+    return torch.empty(max(1, workspace_bytes(op, M, n_out, k_in, r)), dtype=torch.uint8, device=device)
+
+
 def _ws(nbytes: int, device, ws: torch.Tensor | None):
+    """The caller's workspace when it is big enough, else a fresh one."""
     if nbytes == 0:
         return None, 0
     if ws is not None and ws.numel() >= nbytes:
