@@ -21,13 +21,13 @@ hipError_t launch_gemm_dx(const GemmArgs& a, hipStream_t st);
 void time_next_gemm(hipEvent_t start, hipEvent_t stop);
 hipError_t launch_lora_down(const uint16_t* X, int M, int K, const uint16_t* A, int r, float s, uint16_t* U,
                             float* part, hipStream_t st);
-hipError_t launch_lora_vt(const uint16_t* dY, int M, int N, const uint16_t* B, int r, float s, uint16_t* V,
-                          float* part, hipStream_t st);
 size_t rowdot_part_bytes(int64_t M, int64_t Kd, int r);
 int coldot_chunk_rows();
 hipError_t launch_coldot(const uint16_t* v, int r, const uint16_t* in, int M, int C, float* part,
                          hipStream_t st);
 hipError_t launch_finalize(const float* part, int nmc, int r, int C, float* out, bool trans, hipStream_t st);
+hipError_t launch_vt_and_db(const uint16_t* dY, int M, int N, const uint16_t* B, const uint16_t* U, int r,
+                            float s, uint16_t* V, float* vpart, float* cpart, float* dB, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_zero_u16(uint16_t* p, int64_t n, hipStream_t st);
 }  // namespace qlora
@@ -89,7 +89,7 @@ int check_rows(int64_t M, int64_t n_out, int64_t k_in) {
 float lora_scale(float alpha, int32_t r) { return r > 0 ? alpha / (float)r : 0.f; }
 
 struct BwdLayout {
-  size_t u, v, part, total;
+  size_t u, v, part, cpart, total;  // part: U~ / V~ split-K partials; cpart: dA / dB row-chunk partials
   int nmc;
 };
 
@@ -102,12 +102,11 @@ BwdLayout bwd_layout(int64_t M, int64_t n_out, int64_t k_in, int32_t r) {
   L.u = 0;
   L.v = L.u + round_up((size_t)M * r * 2);
   L.part = L.v + round_up((size_t)M * r * 2);
-  // the partial-sum region is reused, in stream order, by the U~ and V~
-  // split-K reductions and by the dA / dB token reductions
-  size_t part = (size_t)L.nmc * r * widest * 4;
-  part = std::max(part, qlora::rowdot_part_bytes(M, k_in, r));
-  part = std::max(part, qlora::rowdot_part_bytes(M, n_out, r));
-  L.total = L.part + round_up(part);
+  // U~ and V~ split-K partials share one region (stream order); the dB and
+  // dA row-chunk partials share another (dB's are produced alongside V~'s)
+  const size_t part = std::max(qlora::rowdot_part_bytes(M, k_in, r), qlora::rowdot_part_bytes(M, n_out, r));
+  L.cpart = L.part + round_up(part);
+  L.total = L.cpart + round_up((size_t)L.nmc * r * widest * 4);
   return L;
 }
 
@@ -279,18 +278,14 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_
       if ((e = qlora::launch_lora_down(X, (int)M, (int)K, A, r, s, Ut, part, stream)) != hipSuccess)
         return hip_fail(e, "lora_down launch");
     }
-    // V~ = bf16(s dY B)
-    if ((e = qlora::launch_lora_vt(dY, (int)M, (int)N, B, r, s, Vt, part, stream)) != hipSuccess)
-      return hip_fail(e, "lora V launch");
-    // dB = dY^T U~  (stored [N x r])
-    if ((e = qlora::launch_coldot(Ut, r, dY, (int)M, (int)N, part, stream)) != hipSuccess)
-      return hip_fail(e, "dB partials launch");
-    if ((e = qlora::launch_finalize(part, L.nmc, r, (int)N, dB, true, stream)) != hipSuccess)
-      return hip_fail(e, "dB finalize launch");
+    // V~ = bf16(s dY B) and dB = dY^T U~ (stored [N x r]): both read dY
+    float* cpart = reinterpret_cast<float*>(base + L.cpart);
+    if ((e = qlora::launch_vt_and_db(dY, (int)M, (int)N, B, Ut, r, s, Vt, part, cpart, dB, stream)) != hipSuccess)
+      return hip_fail(e, "V~ / dB launch");
     // dA = V~^T X  ([r x K])
-    if ((e = qlora::launch_coldot(Vt, r, X, (int)M, (int)K, part, stream)) != hipSuccess)
+    if ((e = qlora::launch_coldot(Vt, r, X, (int)M, (int)K, cpart, stream)) != hipSuccess)
       return hip_fail(e, "dA partials launch");
-    if ((e = qlora::launch_finalize(part, L.nmc, r, (int)K, dA, false, stream)) != hipSuccess)
+    if ((e = qlora::launch_finalize(cpart, L.nmc, r, (int)K, dA, false, stream)) != hipSuccess)
       return hip_fail(e, "dA finalize launch");
   }
   qlora::GemmArgs g{};

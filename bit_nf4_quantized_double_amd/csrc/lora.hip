@@ -64,16 +64,29 @@ struct RowdotLds {
   static constexpr int kElems = CONTIG ? RT * 16 * kPitch : kRowdotSub * kPitch;
 };
 
+struct RowdotArgs {
+  const uint16_t* in;  // [M x Kd]
+  int M, Kd;
+  const uint16_t* wt;  // A [r x Kd] (CONTIG) or B [Kd x r]
+  int r, kchunk, nsplit;
+  float scale;
+  uint16_t* out;       // [M x r] bf16
+  float* part;         // [nsplit][M][r] fp32, or null when nsplit == 1
+};
+
+// Workgroup (bx, by) = (64-row block, K split) of the rowdot grid.
 template <bool CONTIG, int RT>
-__global__ __launch_bounds__(256) void k_rowdot(const uint16_t* __restrict__ in, int M, int Kd,
-                                                const uint16_t* __restrict__ wt, int r, int kchunk,
-                                                float scale, uint16_t* __restrict__ out,
-                                                float* __restrict__ part) {
+__device__ __forceinline__ void rowdot_body(const RowdotArgs& ra, int bx, int by, uint16_t* sw) {
   using Ly = RowdotLds<CONTIG, RT>;
-  __shared__ __attribute__((aligned(16))) uint16_t sw[Ly::kElems];
+  const uint16_t* __restrict__ in = ra.in;
+  const uint16_t* __restrict__ wt = ra.wt;
+  const int M = ra.M, Kd = ra.Kd, r = ra.r, kchunk = ra.kchunk;
+  const float scale = ra.scale;
+  uint16_t* __restrict__ out = ra.out;
+  float* __restrict__ part = ra.part;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m0 = blockIdx.x * 64 + 16 * wave;
-  const int split = blockIdx.y;
+  const int m0 = bx * 64 + 16 * wave;
+  const int split = by;
   const int k_lo = split * kchunk, k_hi = min(Kd, k_lo + kchunk);
   const int row = lane & 15, kg = lane >> 4;
   const __amdgpu_buffer_rsrc_t rin = make_rsrc(in, (uint32_t)((uint64_t)M * Kd * 2));
@@ -162,10 +175,16 @@ __global__ __launch_bounds__(256) void k_rowdot(const uint16_t* __restrict__ in,
   }
 }
 
+template <bool CONTIG, int RT>
+__global__ __launch_bounds__(256) void k_rowdot(RowdotArgs ra) {
+  __shared__ __attribute__((aligned(16))) uint16_t sw[RowdotLds<CONTIG, RT>::kElems];
+  rowdot_body<CONTIG, RT>(ra, blockIdx.x, blockIdx.y, sw);
+}
+
 // out[m][j] = bf16(scale * sum_{split} part[split][m][j]), fixed order.
-__global__ __launch_bounds__(256) void k_rowdot_finalize(const float* __restrict__ part, int nsplit, int64_t n,
-                                                         float scale, uint16_t* __restrict__ out) {
-  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+__device__ __forceinline__ void rowdot_finalize_body(const float* __restrict__ part, int nsplit, int64_t n,
+                                                     float scale, uint16_t* __restrict__ out, int b, int nb) {
+  for (int64_t i = (int64_t)b * 256 + threadIdx.x; i < n; i += (int64_t)nb * 256) {
     float s = 0.f;
     int k = 0;
     for (; k + 8 <= nsplit; k += 8) {  // 8 loads in flight, added in split order
@@ -181,18 +200,33 @@ __global__ __launch_bounds__(256) void k_rowdot_finalize(const float* __restrict
   }
 }
 
+__global__ __launch_bounds__(256) void k_rowdot_finalize(const float* __restrict__ part, int nsplit, int64_t n,
+                                                         float scale, uint16_t* __restrict__ out) {
+  rowdot_finalize_body(part, nsplit, n, scale, out, blockIdx.x, gridDim.x);
+}
+
 // ---------------------------------------------------------------- coldot ----
 // Workgroup: 128 columns x one chunk of rows; the 4 waves take interleaved
 // 32-row steps and are summed in LDS in a fixed order.  Each lane loads an
 // 8 x 8 patch (8 rows x 16 bytes) and transposes it in registers, so column
 // c0 + 8q + jj becomes the B operand of MFMA number jj.
+struct ColdotArgs {
+  const uint16_t* v;   // [M x r] bf16 (U~ or V~)
+  int r;
+  const uint16_t* in;  // [M x C] bf16 (dY or X)
+  int M, C, mchunk;
+  float* part;         // [nmc][r][C] fp32
+};
+
+// Workgroup (bx, by) = (128-column tile, row chunk) of the coldot grid.
 template <int RT>
-__global__ __launch_bounds__(256) void k_coldot(const uint16_t* __restrict__ v, int r,
-                                                const uint16_t* __restrict__ in, int M, int C,
-                                                int mchunk, float* __restrict__ part) {
-  __shared__ f32x4 red[4][8][64];
+__device__ __forceinline__ void coldot_body(const ColdotArgs& ca, int bx, int by, f32x4 (*red)[8][64]) {
+  const uint16_t* __restrict__ v = ca.v;
+  const uint16_t* __restrict__ in = ca.in;
+  const int r = ca.r, M = ca.M, C = ca.C, mchunk = ca.mchunk;
+  float* __restrict__ part = ca.part;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c0 = blockIdx.x * 128, mc = blockIdx.y;
+  const int c0 = bx * 128, mc = by;
   const int mbeg = mc * mchunk, mend = min(M, mbeg + mchunk);
   const int g = lane >> 4, q = lane & 15;
   const bool col_ok = c0 + 8 * q < C;
@@ -261,17 +295,61 @@ __global__ __launch_bounds__(256) void k_coldot(const uint16_t* __restrict__ v, 
   }
 }
 
+template <int RT>
+__global__ __launch_bounds__(256) void k_coldot(ColdotArgs ca) {
+  __shared__ f32x4 red[4][8][64];
+  coldot_body<RT>(ca, blockIdx.x, blockIdx.y, red);
+}
+
 // out[j][c] (or out[c][j] when TRANS) = sum_{mc} part[mc][j][c], fixed order.
+template <bool TRANS>
+__device__ __forceinline__ void finalize_body(const float* __restrict__ part, int nmc, int r, int C,
+                                              float* __restrict__ out, int b, int nb) {
+  const int64_t total = (int64_t)r * C;
+  for (int64_t idx = (int64_t)b * 256 + threadIdx.x; idx < total; idx += (int64_t)nb * 256) {
+    const int j = (int)(idx / C), c = (int)(idx % C);
+    float s = 0.f;
+    int mc = 0;
+    for (; mc + 8 <= nmc; mc += 8) {  // 8 loads in flight, added in chunk order
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[((int64_t)(mc + u) * r + j) * C + c];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; mc < nmc; ++mc) s += part[((int64_t)mc * r + j) * C + c];
+    if (TRANS) out[(int64_t)c * r + j] = s; else out[idx] = s;
+  }
+}
+
 template <bool TRANS>
 __global__ __launch_bounds__(256) void k_finalize(const float* __restrict__ part, int nmc, int r, int C,
                                                   float* __restrict__ out) {
-  const int64_t total = (int64_t)r * C;
-  for (int64_t idx = blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
-    const int j = (int)(idx / C), c = (int)(idx % C);
-    float s = 0.f;
-    for (int mc = 0; mc < nmc; ++mc) s += part[((int64_t)mc * r + j) * C + c];
-    if (TRANS) out[(int64_t)c * r + j] = s; else out[idx] = s;
-  }
+  finalize_body<TRANS>(part, nmc, r, C, out, blockIdx.x, gridDim.x);
+}
+
+// ---- merged launches of the backward (independent work, one dispatch) ----
+// Blocks [0, nr) run the V~ rowdot grid (nr = row blocks x splits), blocks
+// [nr, nr + nc) the dB coldot grid: both read dY, neither needs the other.
+template <int RT>
+__global__ __launch_bounds__(256) void k_vt_and_db(RowdotArgs ra, int rb, ColdotArgs ca, int ctiles) {
+  __shared__ __attribute__((aligned(16))) uint16_t sw[RowdotLds<false, RT>::kElems];
+  __shared__ f32x4 red[4][8][64];
+  const int nr = rb * ra.nsplit;
+  const int b = blockIdx.x;
+  if (b < nr) rowdot_body<false, RT>(ra, b % rb, b / rb, sw);
+  else coldot_body<RT>(ca, (b - nr) % ctiles, (b - nr) / ctiles, red);
+}
+
+// Blocks [0, n1) finalize V~ (when it was split), blocks [n1, n1 + n2)
+// finalize dB (stored [N x r]).
+__global__ __launch_bounds__(256) void k_fin_vt_and_db(const float* __restrict__ vpart, int nsplit, int64_t nv,
+                                                       float scale, uint16_t* __restrict__ vout, int n1,
+                                                       const float* __restrict__ cpart, int nmc, int r, int C,
+                                                       float* __restrict__ dB, int n2) {
+  const int b = blockIdx.x;
+  if (b < n1) rowdot_finalize_body(vpart, nsplit, nv, scale, vout, b, n1);
+  else finalize_body<true>(cpart, nmc, r, C, dB, b - n1, n2);
 }
 
 __global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_t n) {
@@ -285,7 +363,8 @@ __global__ __launch_bounds__(256) void k_zero_u16(uint16_t* __restrict__ p, int6
 template <bool CONTIG, int RT>
 void rowdot_launch(dim3 grid, hipStream_t st, const uint16_t* in, int M, int Kd, const uint16_t* wt, int r,
                    int kchunk, float scale, uint16_t* out, float* part) {
-  hipLaunchKernelGGL((k_rowdot<CONTIG, RT>), grid, dim3(256), 0, st, in, M, Kd, wt, r, kchunk, scale, out, part);
+  const RowdotArgs ra{in, M, Kd, wt, r, kchunk, (int)grid.y, scale, out, part};
+  hipLaunchKernelGGL((k_rowdot<CONTIG, RT>), grid, dim3(256), 0, st, ra);
 }
 
 template <bool CONTIG>
@@ -317,11 +396,6 @@ hipError_t launch_lora_down(const uint16_t* X, int M, int K, const uint16_t* A, 
   return rowdot_dispatch<true>(X, M, K, A, r, s, U, part, st);
 }
 
-// V~ = bf16(s dY B): in = dY [M x N], B [N x r]
-hipError_t launch_lora_vt(const uint16_t* dY, int M, int N, const uint16_t* B, int r, float s, uint16_t* V,
-                          float* part, hipStream_t st) {
-  return rowdot_dispatch<false>(dY, M, N, B, r, s, V, part, st);
-}
 
 int coldot_chunk_rows() { return 256; }
 
@@ -330,12 +404,43 @@ hipError_t launch_coldot(const uint16_t* v, int r, const uint16_t* in, int M, in
   const int mchunk = coldot_chunk_rows();
   dim3 grid((C + 127) / 128, (M + mchunk - 1) / mchunk);
   const int rt = (r + 15) / 16;
+  const ColdotArgs ca{v, r, in, M, C, mchunk, part};
   switch (rt) {
-    case 1: hipLaunchKernelGGL((k_coldot<1>), grid, dim3(256), 0, st, v, r, in, M, C, mchunk, part); break;
-    case 2: hipLaunchKernelGGL((k_coldot<2>), grid, dim3(256), 0, st, v, r, in, M, C, mchunk, part); break;
-    case 3: hipLaunchKernelGGL((k_coldot<3>), grid, dim3(256), 0, st, v, r, in, M, C, mchunk, part); break;
-    default: hipLaunchKernelGGL((k_coldot<4>), grid, dim3(256), 0, st, v, r, in, M, C, mchunk, part); break;
+    case 1: hipLaunchKernelGGL((k_coldot<1>), grid, dim3(256), 0, st, ca); break;
+    case 2: hipLaunchKernelGGL((k_coldot<2>), grid, dim3(256), 0, st, ca); break;
+    case 3: hipLaunchKernelGGL((k_coldot<3>), grid, dim3(256), 0, st, ca); break;
+    default: hipLaunchKernelGGL((k_coldot<4>), grid, dim3(256), 0, st, ca); break;
   }
+  return hipGetLastError();
+}
+
+// Backward adapter reductions over dY in two dispatches:
+//   1. V~ split partials (or V~ itself when unsplit) and dB row-chunk partials;
+//   2. V~ finalize (when split) and dB finalize.
+hipError_t launch_vt_and_db(const uint16_t* dY, int M, int N, const uint16_t* B, const uint16_t* U, int r,
+                            float s, uint16_t* V, float* vpart, float* cpart, float* dB, hipStream_t st) {
+  int nsplit, kchunk;
+  rowdot_split(M, N, &nsplit, &kchunk);
+  const int rb = (M + 63) / 64;
+  const RowdotArgs ra{dY, M, N, B, r, kchunk, nsplit, s, V, nsplit > 1 ? vpart : nullptr};
+  const int mchunk = coldot_chunk_rows();
+  const int ctiles = (N + 127) / 128, nmc = (M + mchunk - 1) / mchunk;
+  const ColdotArgs ca{U, r, dY, M, N, mchunk, cpart};
+  const dim3 grid(rb * nsplit + ctiles * nmc);
+  switch ((r + 15) / 16) {
+    case 1: hipLaunchKernelGGL((k_vt_and_db<1>), grid, dim3(256), 0, st, ra, rb, ca, ctiles); break;
+    case 2: hipLaunchKernelGGL((k_vt_and_db<2>), grid, dim3(256), 0, st, ra, rb, ca, ctiles); break;
+    case 3: hipLaunchKernelGGL((k_vt_and_db<3>), grid, dim3(256), 0, st, ra, rb, ca, ctiles); break;
+    default: hipLaunchKernelGGL((k_vt_and_db<4>), grid, dim3(256), 0, st, ra, rb, ca, ctiles); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nv = (int64_t)M * r;
+  const int n1 = nsplit > 1 ? (int)std::max<int64_t>(1, std::min<int64_t>((nv + 255) / 256, 2048)) : 0;
+  const int64_t nc = (int64_t)r * N;
+  const int n2 = (int)std::max<int64_t>(1, std::min<int64_t>((nc + 255) / 256, 4096));
+  hipLaunchKernelGGL(k_fin_vt_and_db, dim3(n1 + n2), dim3(256), 0, st, vpart, nsplit, nv, s, V, n1, cpart, nmc, r,
+                     N, dB, n2);
   return hipGetLastError();
 }
 
