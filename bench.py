@@ -270,6 +270,36 @@ def bench_secondary(torch, qlora, synth, dev, evs, reps=10):
         gbs = (PACKED_B_PER_W + 2.0) * nw / (us * 1e-6) / 1e9
         res[f"dequant_70b_{lin.name}"] = {"us": round(us, 2), "GB/s": round(gbs, 1),
                                           "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        if idx == 0:
+            # merge the adapter into the weight (bf16 out) and re-quantize it
+            rr, alpha = synth.RANK["70b"], synth.ALPHA["70b"]
+            dm = synth.linear_inputs(lin.n_out, lin.k_in, 1, rr, synth.rng_for("70b", 30), with_grad=False)
+            Am = torch.from_numpy(dm["A"].view(np.int16)).view(torch.bfloat16).to(dev)
+            Bm = torch.from_numpy(dm["B"].view(np.int16)).view(torch.bfloat16).to(dev)
+            for c in copies:
+                qlora.merge(c, Am, Bm, rr, alpha, out)
+            torch.cuda.synchronize()
+            a.record()
+            for i in range(reps * 3):
+                qlora.merge(copies[i % 3], Am, Bm, rr, alpha, out)
+            b.record()
+            torch.cuda.synchronize()
+            us = 1e3 * a.elapsed_time(b) / (reps * 3)
+            gbs = (PACKED_B_PER_W + 2.0) * nw / (us * 1e-6) / 1e9
+            res["merge_70b_gate"] = {"us": round(us, 2), "GB/s": round(gbs, 1),
+                                     "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+            qlora.quantize(out)
+            torch.cuda.synchronize()
+            a.record()
+            for i in range(reps):
+                qlora.quantize(out)
+            b.record()
+            torch.cuda.synchronize()
+            us = 1e3 * a.elapsed_time(b) / reps
+            gbs = (PACKED_B_PER_W + 2.0) * nw / (us * 1e-6) / 1e9
+            res["requantize_70b_gate"] = {"us": round(us, 2), "GB/s": round(gbs, 1),
+                                          "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+            del Am, Bm
         del out
         if idx == 0:
             rr, alpha = synth.RANK["70b"], synth.ALPHA["70b"]

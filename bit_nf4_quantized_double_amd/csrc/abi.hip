@@ -14,8 +14,12 @@
 namespace qlora {
 hipError_t launch_quantize(const float* W, int64_t nweights, uint8_t* codes, uint8_t* q8, float* s2,
                            hipStream_t st);
+hipError_t launch_quantize_bf16(const uint16_t* W, int64_t nweights, uint8_t* codes, uint8_t* q8, float* s2,
+                                hipStream_t st);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* q8, const float* s2, int64_t nweights,
                           uint16_t* out, hipStream_t st);
+hipError_t launch_merge(const uint8_t* codes, const uint8_t* q8, const float* s2, int N, int K, const uint16_t* A,
+                        const uint16_t* B, int r, float s, uint16_t* out, hipStream_t st);
 hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_dx(const GemmArgs& a, hipStream_t st);
 void time_next_gemm(hipEvent_t start, hipEvent_t stop);
@@ -154,6 +158,37 @@ int qlora_quantize_nf4_dq(const float* W, int64_t n_out, int64_t k_in, uint8_t* 
   if (!aligned16(W)) return fail(QLORA_ERR_ALIGN, "W must be 16-byte aligned");
   hipError_t e = qlora::launch_quantize(W, n_out * k_in, codes, absmax_q8, absmax_scale, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e, "quantize launch");
+}
+
+int qlora_quantize_nf4_dq_bf16(const uint16_t* W, int64_t n_out, int64_t k_in, uint8_t* codes,
+                               uint8_t* absmax_q8, float* absmax_scale, hipStream_t stream) {
+  qlora_nf4_weight w{n_out, k_in, codes, absmax_q8, absmax_scale};
+  int st = check_weight(&w);
+  if (st) return st;
+  if (n_out * k_in == 0) return QLORA_OK;
+  if (!W) return fail(QLORA_ERR_INVALID_ARG, "W is NULL");
+  if (!aligned16(W)) return fail(QLORA_ERR_ALIGN, "W must be 16-byte aligned");
+  hipError_t e = qlora::launch_quantize_bf16(W, n_out * k_in, codes, absmax_q8, absmax_scale, stream);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e, "quantize launch");
+}
+
+int qlora_merge(const qlora_nf4_weight* w, const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                uint16_t* W_merged, hipStream_t stream) {
+  int st = check_weight(w);
+  if (st) return st;
+  if ((st = check_adapter(r, A, B))) return st;
+  if (w->n_out * w->k_in == 0) return QLORA_OK;
+  if (!W_merged) return fail(QLORA_ERR_INVALID_ARG, "W_merged is NULL");
+  if (!aligned16(W_merged)) return fail(QLORA_ERR_ALIGN, "W_merged must be 16-byte aligned");
+  hipError_t e;
+  if (r == 0) {
+    // no adapter: the merged weight is the dequantized weight
+    e = qlora::launch_dequant(w->codes, w->absmax_q8, w->absmax_scale, w->n_out * w->k_in, W_merged, stream);
+  } else {
+    e = qlora::launch_merge(w->codes, w->absmax_q8, w->absmax_scale, (int)w->n_out, (int)w->k_in, A, B, r,
+                            lora_scale(alpha, r), W_merged, stream);
+  }
+  return e == hipSuccess ? QLORA_OK : hip_fail(e, "merge launch");
 }
 
 int qlora_dequant(const qlora_nf4_weight* w, uint16_t* W_bf16, hipStream_t stream) {

@@ -7,7 +7,8 @@
 // decision thresholds below x (the nearest level, exact ties to the lower
 // level), two codes per byte.  The block absmaxes stay in LDS; the group max
 // gives the fp32 step s2 = max / 255 and each block's 8-bit code
-// q8 = round-half-even(absmax / s2).  No workspace.
+// q8 = round-half-even(absmax / s2).  No workspace.  The input is fp32 or
+// bf16 (widened exactly; used to re-quantize a merged bf16 weight).
 //
 // Dequant: a streaming decode, 8 weights (one code dword -> 16 bytes of bf16)
 // per thread per iteration; HBM-bound (2.516 bytes moved per weight).
@@ -18,7 +19,12 @@
 namespace qlora {
 namespace {
 
-__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, uint32_t nb,
+// Weight element as fp32: fp32 input as is, bf16 input widened exactly.
+__device__ __forceinline__ float load_w(const float* W, size_t i) { return W[i]; }
+__device__ __forceinline__ float load_w(const uint16_t* W, size_t i) { return bf16_to_f32(W[i]); }
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ W, uint32_t nb,
                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ q8,
                                                   float* __restrict__ s2, Nf4Consts c) {
   __shared__ float s_amax[kGroup];
@@ -31,7 +37,7 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, u
     float am = 0.f;
     if (bl < nblk) {
       const uint32_t b = b0 + bl;
-      const float w = W[(size_t)b * kBlock + lane];
+      const float w = load_w(W, (size_t)b * kBlock + lane);
       float m = fabsf(w);
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -89,7 +95,16 @@ hipError_t launch_quantize(const float* W, int64_t nweights, uint8_t* codes, uin
   const uint32_t nb = (uint32_t)(nweights / kBlock);
   const uint32_t ng = (nb + kGroup - 1) / kGroup;
   if (ng == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_quantize, dim3(ng), dim3(256), 0, st, W, nb, codes, q8, s2, nf4_consts());
+  hipLaunchKernelGGL(k_quantize<float>, dim3(ng), dim3(256), 0, st, W, nb, codes, q8, s2, nf4_consts());
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_bf16(const uint16_t* W, int64_t nweights, uint8_t* codes, uint8_t* q8, float* s2,
+                                hipStream_t st) {
+  const uint32_t nb = (uint32_t)(nweights / kBlock);
+  const uint32_t ng = (nb + kGroup - 1) / kGroup;
+  if (ng == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quantize<uint16_t>, dim3(ng), dim3(256), 0, st, W, nb, codes, q8, s2, nf4_consts());
   return hipGetLastError();
 }
 

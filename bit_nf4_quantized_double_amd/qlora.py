@@ -48,6 +48,8 @@ def lib() -> ctypes.CDLL:
     W = ctypes.POINTER(_CWeight)
     sig = {
         "qlora_quantize_nf4_dq": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
+        "qlora_quantize_nf4_dq_bf16": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
+        "qlora_merge": (ctypes.c_int, [W, _vp, _vp, _c_i32, ctypes.c_float, _vp, _vp]),
         "qlora_dequant": (ctypes.c_int, [W, _vp, _vp]),
         "qlora_linear_fwd": (ctypes.c_int, [W, _vp, _c_i64, _vp, _vp, _c_i32, ctypes.c_float,
                                             _vp, _vp, _vp, ctypes.c_size_t, _vp]),
@@ -129,7 +131,7 @@ def _empty_u8(n, device):
 
 
 def quantize(W: torch.Tensor) -> NF4Weight:
-    """fp32 [n_out, k_in] GPU tensor -> NF4Weight (codes, q8, s2)."""
+    """fp32 or bf16 [n_out, k_in] GPU tensor -> NF4Weight (codes, q8, s2)."""
     if W.dim() != 2:
         raise ValueError("W must be 2-D [n_out, k_in]")
     n_out, k_in = W.shape
@@ -140,10 +142,27 @@ def quantize(W: torch.Tensor) -> NF4Weight:
     codes = _empty_u8(nw // 2, dev)
     q8 = _empty_u8(nb, dev)
     s2 = torch.empty(max(ng, 4), dtype=torch.float32, device=dev)[:ng]
-    st = lib().qlora_quantize_nf4_dq(_dev(W, torch.float32, "W"), n_out, k_in, codes.data_ptr(),
-                                     q8.data_ptr(), s2.data_ptr(), _stream())
-    _check(st, "qlora_quantize_nf4_dq")
+    if W.dtype == torch.bfloat16:
+        st = lib().qlora_quantize_nf4_dq_bf16(_dev(W, torch.bfloat16, "W"), n_out, k_in, codes.data_ptr(),
+                                              q8.data_ptr(), s2.data_ptr(), _stream())
+        _check(st, "qlora_quantize_nf4_dq_bf16")
+    else:
+        st = lib().qlora_quantize_nf4_dq(_dev(W, torch.float32, "W"), n_out, k_in, codes.data_ptr(),
+                                         q8.data_ptr(), s2.data_ptr(), _stream())
+        _check(st, "qlora_quantize_nf4_dq")
     return NF4Weight(codes, q8, s2, n_out, k_in)
+
+
+def merge(w: NF4Weight, A: torch.Tensor | None, B: torch.Tensor | None, r: int, alpha: float,
+          out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 [n_out, k_in] merged weight bf16(W_bf16 + (alpha/r) B A)."""
+    if out is None:
+        out = torch.empty((w.n_out, w.k_in), dtype=torch.bfloat16, device=w.codes.device)
+    cw = w._c()
+    st = lib().qlora_merge(ctypes.byref(cw), _opt(A, torch.bfloat16, "A"), _opt(B, torch.bfloat16, "B"), r,
+                           float(alpha), _dev(out, torch.bfloat16, "out"), _stream())
+    _check(st, "qlora_merge")
+    return out
 
 
 def dequant(w: NF4Weight, out: torch.Tensor | None = None) -> torch.Tensor:

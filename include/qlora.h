@@ -7,6 +7,7 @@
  *   [P2] "What is QLoRA, and how does 4-bit training make consumer-hardware
  *        fine-tuning possible?"
  *   [P4] "QLoRA and Fine-Tuning on One Consumer GPU"
+ *   [P5] "QLoRA"
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -100,6 +101,32 @@ typedef struct {
 int qlora_quantize_nf4_dq(const float *W, int64_t n_out, int64_t k_in,
                           uint8_t *codes, uint8_t *absmax_q8, float *absmax_scale,
                           hipStream_t stream);
+
+/*
+ * Same as qlora_quantize_nf4_dq for a bf16 weight (widened exactly to fp32
+ * first): re-quantizes a merged weight for serving ([P1] "Shipping: merge,
+ * re-quantize, verify").
+ *   W  device bf16 (uint16 bits) [n_out, k_in].
+ */
+int qlora_quantize_nf4_dq_bf16(const uint16_t *W, int64_t n_out, int64_t k_in,
+                               uint8_t *codes, uint8_t *absmax_q8, float *absmax_scale,
+                               hipStream_t stream);
+
+/*
+ * Merge the adapter into the frozen weight ([P1] "Shipping: merge,
+ * re-quantize, verify"; [P5] "QLoRA", "Walking through the tooling": at
+ * inference W' = W + scaled B A):
+ *   W_merged  device bf16 [n_out, k_in], written:
+ *               W_merged = bf16(W_bf16 + s * (B A)),  s = fp32(alpha / r)
+ *             with W_bf16 the decoded weight, B A summed in fp32, and one
+ *             rounding to bf16 (round to nearest even).
+ *   A, B, r, alpha as in qlora_linear_fwd; r == 0 gives the decoded weight.
+ * Re-quantizing the result (qlora_quantize_nf4_dq_bf16) gives the single
+ * 4-bit weight file of the merged model; its difference from W_merged is
+ * the re-quantization drift the pages warn about.
+ */
+int qlora_merge(const qlora_nf4_weight *w, const uint16_t *A, const uint16_t *B, int32_t r,
+                float alpha, uint16_t *W_merged, hipStream_t stream);
 
 /*
  * Dequantize the whole weight to bf16 ([P1] "The mechanism in brief": the

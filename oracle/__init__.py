@@ -21,6 +21,8 @@ Modules:
 * :mod:`oracle.nf4_dq` -- NF4 table, block quantize, double quantize,
   dequantize, storage accounting.
 * :mod:`oracle.qlora_linear` -- forward and backward of the adapted linear.
+* :mod:`oracle.merge` -- merging the adapter into the weight and
+  re-quantizing the result.
 
 Every function pinned by a ``-m "not gpu"`` test says which pin covers it.
 The one construction the pages leave fully open -- the tail offset of the
@@ -48,3 +50,4 @@ from .nf4_dq import (  # noqa: F401
     quantize_groups,
 )
 from .qlora_linear import lora_scale, linear_fwd, linear_bwd  # noqa: F401
+from .merge import bf16_bits_from_f64, merge, requantize, requant_drift  # noqa: F401

@@ -135,3 +135,19 @@ def test_workspace_sizes(L):
     assert ws(2, 2048, 4096, 4096, 0) == 0
     assert ws(9, 1, 1, 64, 1) == 0
     assert ws(1, 16, 64, 64, 65) == 0
+
+
+def test_merge_and_bf16_quantize_validation(L):
+    w = ctypes.byref(_w())
+    m = L.qlora_merge
+    assert m(w, FAKE, FAKE, 99, 2.0, FAKE, None) == SHAPE        # rank above the maximum
+    assert m(w, None, FAKE, 8, 2.0, FAKE, None) == INVALID       # A missing with r > 0
+    assert m(w, FAKE, FAKE, 8, 2.0, None, None) == INVALID       # no output
+    assert m(w, FAKE, FAKE, 8, 2.0, FAKE_MIS, None) == ALIGN
+    assert m(ctypes.byref(_w(k_in=96)), FAKE, FAKE, 8, 2.0, FAKE, None) == SHAPE  # k_in % 64
+    assert m(ctypes.byref(_w(n_out=0)), FAKE, FAKE, 8, 2.0, FAKE, None) == OK    # empty weight
+    q = L.qlora_quantize_nf4_dq_bf16
+    assert q(None, 64, 64, FAKE, FAKE, FAKE, None) == INVALID
+    assert q(FAKE_MIS, 64, 64, FAKE, FAKE, FAKE, None) == ALIGN
+    assert q(FAKE, 64, 96, FAKE, FAKE, FAKE, None) == SHAPE
+    assert q(FAKE, 0, 64, FAKE, FAKE, FAKE, None) == OK

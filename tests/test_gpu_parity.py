@@ -386,3 +386,92 @@ def test_few_token_70b_gate_sampled_columns(M):
     s = oracle.lora_scale(alpha, r)
     Yr = Xf @ Wsel.T + s * (Xf @ Af.T) @ Bf[cols].T
     check_close(f64(Y)[:, cols], Yr, "Y sampled columns")
+
+
+# ------------------------------------------------------ merge, re-quantize ----
+
+MERGE_SHAPES = [
+    # (N, K, r, alpha): ragged 64-row and 128-column tiles, ranks that are not
+    # multiples of 8, more than 32 ranks, no adapter
+    (256, 256, 8, 16.0),
+    (200, 320, 3, 6.0),
+    (136, 192, 17, 5.0),
+    (96, 640, 33, 66.0),
+    (64, 128, 64, 128.0),
+    (72, 256, 0, 0.0),
+    (1024, 4096, 16, 32.0),
+]
+
+
+def _near_tie(exact, wb, A, B, s, r):
+    """Elements whose exact merged value lies closer to a bf16 rounding
+    boundary than the fp32 evaluation error of W + s * sum_j B A can reach:
+    (r + 2) * 2^-24 * (|W| + s * sum_j |B A|).  There the GPU may round to
+    either neighbour."""
+    b = oracle.bf16_bits_from_f64(exact)
+    g = np.abs(oracle.f64_from_bf16_bits(b))
+    # bf16 spacing at g, on the side of the exact value (just below a power
+    # of two the spacing is half)
+    e = np.floor(np.log2(np.where(g > 0, g, 1.0)))
+    sp = 2.0 ** (e - 7)
+    sp = np.where((np.abs(exact) < g) & (g == 2.0 ** e), sp / 2, sp)
+    d = np.abs(np.abs(np.abs(exact) - g) - sp / 2)
+    return d <= _merge_err_bound(wb, A, B, s, r), sp
+
+
+def _merge_err_bound(wb, A, B, s, r):
+    """Bound on the fp32 evaluation error of W + s * sum_j B A (MFMA sums and
+    one multiply-add): (r + 2) * 2^-23 * (|W| + s * sum_j |B A|)."""
+    mag = np.abs(oracle.f64_from_bf16_bits(wb))
+    if r > 0:
+        mag = mag + s * (np.abs(oracle.f64_from_bf16_bits(B)) @ np.abs(oracle.f64_from_bf16_bits(A)))
+    return (r + 2) * 2.0 ** -23 * mag
+
+
+@pytest.mark.parametrize("N,K,r,alpha", MERGE_SHAPES)
+def test_merge_and_requantize_parity(N, K, r, alpha):
+    _need_gpu()
+    d, q, wb = _case(4, N, K, r, seed=N + 3 * K + r)
+    w = gpu_quantize(d["W"])
+    A = dev_bf16(d["A"]) if r > 0 else None
+    B = dev_bf16(d["B"]) if r > 0 else None
+    Wm = qlora.merge(w, A, B, r, alpha)
+    torch.cuda.synchronize()
+    exact, ref = oracle.merge(wb, d["A"], d["B"], alpha, r)
+    got = host_bits(Wm)
+    sc = oracle.lora_scale(alpha, r)
+    tie, sp = _near_tie(exact, wb, d["A"], d["B"], sc, r)
+    bad = (got != ref) & ~tie
+    assert not bad.any(), (f"{bad.sum()} of {bad.size} differ; first at {np.argwhere(bad)[:4].tolist()}: "
+                           f"got {got[bad][:4]} ref {ref[bad][:4]} exact {exact[bad][:4]}")
+    # near a rounding boundary: within the evaluation error plus one spacing
+    if tie.any():
+        err = np.abs(oracle.f64_from_bf16_bits(got[tie]) - exact[tie])
+        assert np.all(err <= _merge_err_bound(wb, d["A"], d["B"], sc, r)[tie] + sp[tie])
+    # re-quantize on the GPU (bf16 input) and in the oracle: bit-exact on the
+    # groups whose merged inputs agree bit for bit
+    w2 = qlora.quantize(Wm)
+    torch.cuda.synchronize()
+    q2 = oracle.requantize(ref, N, K)
+    same_blk = (got.reshape(-1, 64) == ref.reshape(-1, 64)).all(axis=1)
+    codes = w2.codes.cpu().numpy().reshape(-1, 32)
+    assert np.array_equal(codes[same_blk], q2["codes"].reshape(-1, 32)[same_blk])
+    nb = same_blk.size
+    grp_ok = np.array([same_blk[g * 256:(g + 1) * 256].all() for g in range((nb + 255) // 256)])
+    q8 = w2.absmax_q8.cpu().numpy()
+    blk_grp = np.arange(nb) // 256
+    assert np.array_equal(q8[grp_ok[blk_grp]], q2["absmax_q8"][grp_ok[blk_grp]])
+    assert np.array_equal(w2.absmax_scale.cpu().numpy()[grp_ok], q2["absmax_scale"][grp_ok])
+    # the drift the pages warn about: the re-quantized weight vs the merged one
+    drift = oracle.requant_drift(ref, q2, N, K)
+    assert 0.0 <= drift < 0.2
+
+
+def test_quantize_bf16_input_bit_exact():
+    _need_gpu()
+    d = synth.workload_linear("cfg1", 0)
+    Wb = synth.to_bf16_bits(d["W"])
+    q = oracle.quantize_nf4_dq(oracle.f64_from_bf16_bits(Wb).astype(np.float32).reshape(d["W"].shape))
+    w = qlora.quantize(dev_bf16(Wb).reshape(d["W"].shape))
+    torch.cuda.synchronize()
+    check_codec_exact(w, q)
