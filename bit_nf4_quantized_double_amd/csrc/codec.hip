@@ -1,12 +1,12 @@
 // NF4 + double-quantization codec kernels ([P1] "The mechanism in brief";
 // [P4] "NF4 and double quantisation").
 //
-// Quantize: one 256-thread workgroup per group of 256 blocks.  A wave takes
-// one 64-weight block at a time (one weight per lane): absmax by a wave
-// max-reduction, x = w / absmax (IEEE fp32 division), code = number of
-// decision thresholds below x (the nearest level, exact ties to the lower
-// level), two codes per byte.  The block absmaxes stay in LDS; the group max
-// gives the fp32 step s2 = max / 255 and each block's 8-bit code
+// Quantize: one 256-thread workgroup per group of 256 blocks, one thread per
+// 64-weight block: absmax, x = w / absmax (IEEE fp32 division), code = number
+// of decision thresholds below x (the nearest level, exact ties to the lower
+// level; found with a table-guided search), two codes per byte.  The block
+// absmaxes stay in registers; the group max gives the fp32 step
+// s2 = max / 255 and each block's 8-bit code
 // q8 = round-half-even(absmax / s2).  No workspace.  The input is fp32 or
 // bf16 (widened exactly; used to re-quantize a merged bf16 weight).
 //
@@ -20,52 +20,105 @@ namespace qlora {
 namespace {
 
 // Weight element as fp32: fp32 input as is, bf16 input widened exactly.
-__device__ __forceinline__ float load_w(const float* W, size_t i) { return W[i]; }
-__device__ __forceinline__ float load_w(const uint16_t* W, size_t i) { return bf16_to_f32(W[i]); }
+template <typename T>
+struct WLoad;
+template <>
+struct WLoad<float> {
+  // 64 weights of one block = 16 x 16 bytes
+  static __device__ __forceinline__ void load(const float* W, size_t b, float w[64]) {
+    const uint4* p = reinterpret_cast<const uint4*>(W + b * kBlock);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint4 v = p[i];
+      w[4 * i] = __uint_as_float(v.x); w[4 * i + 1] = __uint_as_float(v.y);
+      w[4 * i + 2] = __uint_as_float(v.z); w[4 * i + 3] = __uint_as_float(v.w);
+    }
+  }
+};
+template <>
+struct WLoad<uint16_t> {
+  // 64 weights of one block = 8 x 16 bytes of bf16
+  static __device__ __forceinline__ void load(const uint16_t* W, size_t b, float w[64]) {
+    const uint4* p = reinterpret_cast<const uint4*>(W + b * kBlock);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 v = p[i];
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        w[8 * i + 2 * j] = __uint_as_float(d[j] << 16);
+        w[8 * i + 2 * j + 1] = __uint_as_float(d[j] & 0xFFFF0000u);
+      }
+    }
+  }
+};
 
+// One 256-thread workgroup per group of 256 blocks, one thread per block:
+// the thread loads its 64 weights (all loads in flight), takes the absmax,
+// codes each weight with the table-guided search and writes 32 bytes of
+// packed codes; the group max then gives s2 and every thread's q8.
 template <typename T>
 __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ W, uint32_t nb,
                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ q8,
-                                                  float* __restrict__ s2, Nf4Consts c) {
-  __shared__ float s_amax[kGroup];
+                                                  float* __restrict__ s2, QuantSearch qs) {
+  __shared__ uint8_t s_cand[256];
+  __shared__ float s_thr[16];
   __shared__ float s_red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  s_cand[tid] = qs.cand[tid];
+  if (tid < 16) s_thr[tid] = qs.thr16[tid];
   const uint32_t g = blockIdx.x, b0 = g * kGroup;
   const uint32_t nblk = min((uint32_t)kGroup, nb - b0);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool valid = (uint32_t)tid < nblk;
+  const uint32_t b = b0 + tid;
 
-  for (uint32_t bl = wave; bl < (uint32_t)kGroup; bl += 4) {
-    float am = 0.f;
-    if (bl < nblk) {
-      const uint32_t b = b0 + bl;
-      const float w = load_w(W, (size_t)b * kBlock + lane);
-      float m = fabsf(w);
+  float w[kBlock];
+  if (valid) {
+    WLoad<T>::load(W, b, w);
+  } else {
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-      am = m;
-      const float x = am > 0.f ? w / am : 0.f;
-      uint32_t code = 0;
-#pragma unroll
-      for (int i = 0; i < 15; ++i) code += (x > c.thr[i]) ? 1u : 0u;
-      const uint32_t hi = __shfl_down(code, 1);
-      if ((lane & 1) == 0) codes[(size_t)b * (kBlock / 2) + (lane >> 1)] = (uint8_t)(code | (hi << 4));
-    }
-    if (lane == 0) s_amax[bl] = am;
+    for (int i = 0; i < kBlock; ++i) w[i] = 0.f;
   }
-  __syncthreads();
-  float m = s_amax[tid];
+  float am = 0.f;
+#pragma unroll
+  for (int i = 0; i < kBlock; ++i) am = fmaxf(am, fabsf(w[i]));
+  __syncthreads();  // search tables ready
+
+  if (valid) {
+    uint32_t packed[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = am > 0.f ? w[8 * d + e] / am : 0.f;  // IEEE division
+        const int cell = min(max((int)(x * 128.f + 128.f), 0), 255);
+        const uint32_t c0 = s_cand[cell];
+        const uint32_t code = c0 + (x > s_thr[c0] ? 1u : 0u);
+        word |= code << (4 * e);
+      }
+      packed[d] = word;
+    }
+    uint4* out = reinterpret_cast<uint4*>(codes + (size_t)b * (kBlock / 2));
+    out[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    out[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+  }
+
+  // group max -> s2 = max / 255, q8 = round-half-even(absmax / s2)
+  float m = am;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   if (lane == 0) s_red[wave] = m;
   __syncthreads();
   const float gmax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   const float step = gmax / 255.0f;
-  if ((uint32_t)tid < nblk) {
+  if (valid) {
     uint32_t q = 0;
     if (step > 0.f) {
-      const float t = rintf(s_amax[tid] / step);  // round half to even
+      const float t = rintf(am / step);  // round half to even
       q = (uint32_t)fminf(fmaxf(t, 0.f), 255.f);
     }
-    q8[b0 + tid] = (uint8_t)q;
+    q8[b] = (uint8_t)q;
   }
   if (tid == 0) s2[g] = step;
 }
@@ -95,7 +148,7 @@ hipError_t launch_quantize(const float* W, int64_t nweights, uint8_t* codes, uin
   const uint32_t nb = (uint32_t)(nweights / kBlock);
   const uint32_t ng = (nb + kGroup - 1) / kGroup;
   if (ng == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_quantize<float>, dim3(ng), dim3(256), 0, st, W, nb, codes, q8, s2, nf4_consts());
+  hipLaunchKernelGGL(k_quantize<float>, dim3(ng), dim3(256), 0, st, W, nb, codes, q8, s2, quant_search());
   return hipGetLastError();
 }
 
@@ -104,7 +157,7 @@ hipError_t launch_quantize_bf16(const uint16_t* W, int64_t nweights, uint8_t* co
   const uint32_t nb = (uint32_t)(nweights / kBlock);
   const uint32_t ng = (nb + kGroup - 1) / kGroup;
   if (ng == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_quantize<uint16_t>, dim3(ng), dim3(256), 0, st, W, nb, codes, q8, s2, nf4_consts());
+  hipLaunchKernelGGL(k_quantize<uint16_t>, dim3(ng), dim3(256), 0, st, W, nb, codes, q8, s2, quant_search());
   return hipGetLastError();
 }
 

@@ -12,7 +12,9 @@
 // double precision, to adjacent doubles: accurate to ~1e-15 relative, far
 // inside the smallest fp32 rounding margin of any level.
 #include <cmath>
+#include <limits>
 #include <mutex>
+#include <stdexcept>
 
 #include "common.h"
 
@@ -63,6 +65,25 @@ const Nf4Consts& nf4_consts() {
   static Nf4Consts consts;
   std::call_once(once, [] { consts = build(); });
   return consts;
+}
+
+const QuantSearch& quant_search() {
+  static std::once_flag once;
+  static QuantSearch qs;
+  std::call_once(once, [] {
+    const Nf4Consts& c = nf4_consts();
+    for (int i = 0; i < 14; ++i)  // the search needs thresholds > 3 cells apart
+      if ((double)c.thr[i + 1] - (double)c.thr[i] <= 3.0 / 128.0) throw std::logic_error("NF4 thresholds too close");
+    for (int i = 0; i < 256; ++i) {
+      const double start = i == 0 ? -std::numeric_limits<double>::infinity() : (i - 1) / 128.0 - 1.0;
+      int n = 0;
+      for (int t = 0; t < 15; ++t) n += (double)c.thr[t] < start ? 1 : 0;
+      qs.cand[i] = (uint8_t)n;
+    }
+    for (int t = 0; t < 15; ++t) qs.thr16[t] = c.thr[t];
+    qs.thr16[15] = std::numeric_limits<float>::infinity();
+  });
+  return qs;
 }
 
 }  // namespace qlora
