@@ -4,9 +4,10 @@
 // Quantize: one 256-thread workgroup per group of 256 blocks, one thread per
 // 64-weight block: absmax, x = w / absmax (IEEE fp32 division), code = number
 // of decision thresholds below x (the nearest level, exact ties to the lower
-// level; found with a table-guided search), two codes per byte.  The block
-// absmaxes stay in registers; the group max gives the fp32 step
-// s2 = max / 255 and each block's 8-bit code
+// level; found with a table-guided search on a reciprocal product, the IEEE
+// quotient formed only for blocks with a weight next to a threshold), two
+// codes per byte.  The block absmaxes stay in registers; the group max gives
+// the fp32 step s2 = max / 255 and each block's 8-bit code
 // q8 = round-half-even(absmax / s2).  No workspace.  The input is fp32 or
 // bf16 (widened exactly; used to re-quantize a merged bf16 weight).
 //
@@ -19,85 +20,127 @@
 namespace qlora {
 namespace {
 
-// Weight element as fp32: fp32 input as is, bf16 input widened exactly.
-template <typename T>
-struct WLoad;
-template <>
-struct WLoad<float> {
-  // 64 weights of one block = 16 x 16 bytes
-  static __device__ __forceinline__ void load(const float* W, size_t b, float w[64]) {
-    const uint4* p = reinterpret_cast<const uint4*>(W + b * kBlock);
+// Element of the input as fp32: fp32 as is, bf16 widened exactly.
+__device__ __forceinline__ void widen4(const uint4& v, const float*, float* w) {
+  w[0] = __uint_as_float(v.x); w[1] = __uint_as_float(v.y);
+  w[2] = __uint_as_float(v.z); w[3] = __uint_as_float(v.w);
+}
+__device__ __forceinline__ void widen4(const uint4& v, const uint16_t*, float* w) {
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint4 v = p[i];
-      w[4 * i] = __uint_as_float(v.x); w[4 * i + 1] = __uint_as_float(v.y);
-      w[4 * i + 2] = __uint_as_float(v.z); w[4 * i + 3] = __uint_as_float(v.w);
-    }
+  for (int j = 0; j < 4; ++j) {
+    w[2 * j] = __uint_as_float(d[j] << 16);
+    w[2 * j + 1] = __uint_as_float(d[j] & 0xFFFF0000u);
   }
-};
-template <>
-struct WLoad<uint16_t> {
-  // 64 weights of one block = 8 x 16 bytes of bf16
-  static __device__ __forceinline__ void load(const uint16_t* W, size_t b, float w[64]) {
-    const uint4* p = reinterpret_cast<const uint4*>(W + b * kBlock);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint4 v = p[i];
-      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        w[8 * i + 2 * j] = __uint_as_float(d[j] << 16);
-        w[8 * i + 2 * j + 1] = __uint_as_float(d[j] & 0xFFFF0000u);
-      }
-    }
-  }
-};
+}
 
 // One 256-thread workgroup per group of 256 blocks, one thread per block:
-// the thread loads its 64 weights (all loads in flight), takes the absmax,
+// the group is staged through LDS, the thread takes its 64 weights and the absmax,
 // codes each weight with the table-guided search and writes 32 bytes of
 // packed codes; the group max then gives s2 and every thread's q8.
 template <typename T>
 __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ W, uint32_t nb,
                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ q8,
                                                   float* __restrict__ s2, QuantSearch qs) {
-  __shared__ uint8_t s_cand[256];
-  __shared__ float s_thr[16];
+  constexpr int kWords = kBlock * (int)sizeof(T) / 4;  // 32-bit words per block
+  constexpr int kChunks = kWords / 4;                  // 16-byte chunks per block
+  constexpr int kPitch = kWords + 4;                   // 4 words mod 32 banks between blocks
+  __shared__ __attribute__((aligned(16))) uint32_t s_w[kGroup * kPitch];
+  // per table cell: the candidate threshold t and the candidate count c0
+  // (t = 2 past the last threshold: never exceeded, never close)
+  __shared__ uint2 s_ct[256];
   __shared__ float s_red[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  s_cand[tid] = qs.cand[tid];
-  if (tid < 16) s_thr[tid] = qs.thr16[tid];
+  {
+    const uint32_t c0 = qs.cand[tid];
+    s_ct[tid] = make_uint2(__float_as_uint(c0 < 15 ? qs.thr16[c0] : 2.0f), c0);
+  }
   const uint32_t g = blockIdx.x, b0 = g * kGroup;
   const uint32_t nblk = min((uint32_t)kGroup, nb - b0);
   const bool valid = (uint32_t)tid < nblk;
   const uint32_t b = b0 + tid;
 
-  float w[kBlock];
-  if (valid) {
-    WLoad<T>::load(W, b, w);
-  } else {
+  // the group's weights -> LDS with coalesced loads (each wave instruction
+  // reads 1 KB contiguous), then every thread takes its own block
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(W) + (size_t)b0 * kChunks;
+    uint4 v[kChunks];
 #pragma unroll
-    for (int i = 0; i < kBlock; ++i) w[i] = 0.f;
+    for (int j = 0; j < kChunks; ++j) {
+      const int c = tid + 256 * j;
+      v[j] = (uint32_t)(c / kChunks) < nblk ? src[c] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) {
+      const int c = tid + 256 * j;
+      *reinterpret_cast<uint4*>(s_w + (c / kChunks) * kPitch + 4 * (c % kChunks)) = v[j];
+    }
   }
+  __syncthreads();  // staged weights and search tables ready
+  float w[kBlock];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i)
+    widen4(*reinterpret_cast<const uint4*>(s_w + tid * kPitch + 4 * i), W, w + (kBlock / kChunks) * i);
+
   float am = 0.f;
 #pragma unroll
   for (int i = 0; i < kBlock; ++i) am = fmaxf(am, fabsf(w[i]));
-  __syncthreads();  // search tables ready
 
   if (valid) {
+    // x = w / am (IEEE division) decides each code.  The fast pass takes x
+    // as w * fp32(1 / am), within 2^-22 relative of the quotient: that picks
+    // the table cell (a neighbouring cell gives the same answer) and decides
+    // the comparison with the candidate threshold t unless x lies within
+    // 2^-20 |t| of t.  A block with any weight that close is coded again
+    // with the quotient itself (about one block in 3000 for normal data).  A block whose
+    // absmax is so small that 1 / am would overflow is scaled by 2^64 first
+    // (exact: every quotient is unchanged).
+    float amq = am;
+    if (am < 0x1p-100f) {
+#pragma unroll
+      for (int i = 0; i < kBlock; ++i) w[i] *= 0x1p64f;
+      amq = am * 0x1p64f;
+    }
+    const float rcp = amq > 0.f ? 1.0f / amq : 0.f;
     uint32_t packed[8];
+    float nd = 1.f;  // min over the block of |x - t| - 2^-20 |t|; <= 0: some x is close to its t
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      uint32_t word = 0;
+    for (int h = 0; h < 4; ++h) {  // 16 weights per batch: all 16 table reads in flight
+      float x[16];
+      uint2 ct[16];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = am > 0.f ? w[8 * d + e] / am : 0.f;  // IEEE division
-        const int cell = min(max((int)(x * 128.f + 128.f), 0), 255);
-        const uint32_t c0 = s_cand[cell];
-        const uint32_t code = c0 + (x > s_thr[c0] ? 1u : 0u);
-        word |= code << (4 * e);
+      for (int i = 0; i < 16; ++i) {
+        x[i] = w[16 * h + i] * rcp;
+        const int cell = min(max((int)(x[i] * 128.f + 128.f), 0), 255);
+        ct[i] = s_ct[cell];
       }
-      packed[d] = word;
+#pragma unroll
+      for (int dd = 0; dd < 2; ++dd) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 8 * dd + e;
+          const float t = __uint_as_float(ct[i].x);
+          nd = fminf(nd, fabsf(x[i] - t) - fabsf(t) * 0x1p-20f);
+          word |= (ct[i].y + (x[i] > t ? 1u : 0u)) << (4 * e);
+        }
+        packed[2 * h + dd] = word;
+      }
+    }
+    const bool near = nd <= 0.f;
+    if (near) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = amq > 0.f ? w[8 * d + e] / amq : 0.f;  // IEEE division
+          const int cell = min(max((int)(x * 128.f + 128.f), 0), 255);
+          const uint2 ct = s_ct[cell];
+          word |= (ct.y + (x > __uint_as_float(ct.x) ? 1u : 0u)) << (4 * e);
+        }
+        packed[d] = word;
+      }
     }
     uint4* out = reinterpret_cast<uint4*>(codes + (size_t)b * (kBlock / 2));
     out[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);

@@ -9,13 +9,20 @@
 // exactly as in the products; the rank-r sum is accumulated in fp32 and the
 // result rounded once to bf16 (round to nearest even).
 //
-// Workgroup: 64 rows x 128 columns, 4 waves of 16 rows.  The rank-r product
-// runs on v_mfma_f32_16x16x32_bf16 with r zero-padded to RP (32 or 64): the
-// A operand is B[n][j] (16 bytes of a row per lane), the B operand is
-// A[j][k], read column-wise from an LDS copy of A[:, k0 : k0 + 128] with the
-// transposing ds_read_b64_tr_b16.  The 64 x 128 fp32 product goes through LDS
-// to a row-major pass in which each thread decodes 8 weights, adds s * t and
-// writes 16 bytes of the merged bf16 weight.
+// Workgroup: 4 waves over a 256-column slice of the weight; the slice of A
+// (RP x 256, zero-padded to RP = 32 or 64 ranks) is staged once in LDS and
+// each wave then walks 16-row blocks on its own, with no workgroup barrier.
+// The rank-r product of a 16 x 256 block runs on v_mfma_f32_16x16x32_bf16
+// with the operands arranged so the accumulator lands where the output goes:
+// the MFMA's M index runs over columns, permuted so that lane l ends up
+// holding t[n][64 g + 0 .. 63] of row n = l & 15, g = l >> 4 -- exactly one
+// 64-weight block.  The lane decodes that block's 32 bytes of codes, adds
+// s * t and puts the 128 bytes of merged weight in a wave-private LDS tile,
+// which the wave reads back row by row so every store instruction writes two
+// contiguous 512-byte rows (16-byte pieces of 64 separate rows per store ran
+// at half the speed).  The M-operand comes from the LDS copy of A through
+// the transposing ds_read_b64_tr_b16, the N-operand is B[n][j] (16 bytes of
+// a row per lane).
 #include <algorithm>
 
 #include "common.h"
@@ -27,9 +34,16 @@ typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(8))) short i16x8;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kMTileN = 64, kMTileK = 128;
-constexpr int kAPitch = kMTileK + 8;   // bf16 per row of the A copy
-constexpr int kTPitch = kMTileK + 4;   // fp32 per row of the product tile
+constexpr int kTileK = 256;       // weight columns per workgroup
+constexpr int kWaveRows = 16;     // rows per wave block
+constexpr int kSubBlocks = 4;     // 16-row blocks per wave (workgroup: 4 x 4 x 16 rows)
+constexpr int kRowsPerWg = 4 * kWaveRows * kSubBlocks;
+// bf16 per row of the A copy: 8 words mod 32 banks between rows, so the 16
+// lanes of a transposing read (4 rows x 4 eight-byte pieces) hit 32 banks
+constexpr int kAPitch = kTileK + 16;
+// bf16 per row of a wave's output staging tile: 4 words mod 32 banks between
+// rows, so 8 lanes writing 16 bytes each to 8 rows hit 32 banks
+constexpr int kOPitch = kTileK + 8;
 
 // 8 consecutive bf16 of a row, elements past `valid` (and everything when
 // !ok) read as zero.
@@ -44,73 +58,118 @@ __device__ __forceinline__ uint4 load8(const uint16_t* p, int valid, bool ok, bo
 }
 
 template <int RP>
-__global__ __launch_bounds__(256) void k_merge(const uint32_t* __restrict__ codes, const uint8_t* __restrict__ q8,
+__global__ __launch_bounds__(256) void k_merge(const uint4* __restrict__ codes, const uint8_t* __restrict__ q8,
                                                const float* __restrict__ s2, int N, int K,
                                                const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                                                int r, float s, uint16_t* __restrict__ out, Nf4Consts c) {
   __shared__ __attribute__((aligned(16))) uint16_t sa[RP * kAPitch];
-  __shared__ __attribute__((aligned(16))) float st[kMTileN * kTPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t so[4 * kWaveRows * kOPitch];
   __shared__ float lv[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int k0 = blockIdx.x * kMTileK, n0 = blockIdx.y * kMTileN;
+  const int k0 = blockIdx.x * kTileK, n0 = blockIdx.y * kRowsPerWg;
   const bool vec = (r & 7) == 0;
   if (tid < 16) lv[tid] = c.level[tid];
 
-  // A[:, k0 : k0 + 128] -> LDS (rows j >= r and columns >= K are zero)
-  for (int idx = tid; idx < RP * (kMTileK / 8); idx += 256) {
-    const int j = idx / (kMTileK / 8), cc = idx % (kMTileK / 8), k = k0 + 8 * cc;
+  // A[:, k0 : k0 + 256] -> LDS (rows j >= r and columns >= K are zero).
+  // Column k0 + 64 p + 4 m + e (p < 4, m < 16, e < 4) is stored at
+  // 16 m + 4 p + e, so MFMA tile m reads a contiguous 16-column window.
+  for (int idx = tid; idx < RP * (kTileK / 8); idx += 256) {
+    const int j = idx / (kTileK / 8), kl = 8 * (idx % (kTileK / 8)), k = k0 + kl;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (j < r && k < K) v = *reinterpret_cast<const uint4*>(A + (int64_t)j * K + k);
-    *reinterpret_cast<uint4*>(sa + j * kAPitch + 8 * cc) = v;
+    const int p = kl >> 6, m = (kl & 63) >> 2;  // m even: the 8 columns are tiles m, m + 1
+    uint16_t* d = sa + j * kAPitch + 16 * m + 4 * p;
+    *reinterpret_cast<uint2*>(d) = make_uint2(v.x, v.y);
+    *reinterpret_cast<uint2*>(d + 16) = make_uint2(v.z, v.w);
   }
   __syncthreads();
 
-  // t[n][k] = sum_j B[n][j] A[j][k] for this wave's 16 rows x 128 columns
   const int row = lane & 15, g = lane >> 4;
-  const int n = n0 + 16 * wave + row;
-  f32x4 acc[kMTileK / 16];
-#pragma unroll
-  for (int ct = 0; ct < kMTileK / 16; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s32 = 0; s32 < RP / 32; ++s32) {
-    const int j = 32 * s32 + 8 * g;
-    const bf16x8 af = __builtin_bit_cast(bf16x8, load8(B + (int64_t)n * r + j, r - j, n < N, vec));
-    const int p = row & 3, q = row >> 2;
-    const int jb = 32 * s32 + 8 * g + q;
-#pragma unroll
-    for (int ct = 0; ct < kMTileK / 16; ++ct) {
-      // lane p + 4q of each 16-lane group addresses row jb, columns 16 ct + 4p;
-      // it receives column 16 ct + (lane & 15), rows jb - q .. + 3 (and + 4 .. + 7)
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sa + jb * kAPitch + 16 * ct + 4 * p));
-      const i16x4 hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sa + (jb + 4) * kAPitch + 16 * ct + 4 * p));
-      const i16x8 bv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, bv), acc[ct], 0, 0, 0);
-    }
-  }
-  // D layout: lane l, element v -> row 4 (l >> 4) + v of the wave, column l & 15 of the tile
-#pragma unroll
-  for (int ct = 0; ct < kMTileK / 16; ++ct)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) st[(16 * wave + 4 * g + v) * kTPitch + 16 * ct + row] = acc[ct][v];
-  __syncthreads();
+  const int p = row & 3, q = row >> 2;  // transposing-read address of this lane
+  const int kl = 64 * g;                // this lane's block of columns in the slice
+  const bool kok = k0 + kl < K;
 
-  // row-major pass: thread -> (row, 8 columns); Wm = bf16(Wbf + s * t)
-  for (int idx = tid; idx < kMTileN * (kMTileK / 8); idx += 256) {
-    const int rl = idx / (kMTileK / 8), cc = idx % (kMTileK / 8);
-    const int nn = n0 + rl, k = k0 + 8 * cc;
-    if (nn >= N || k >= K) continue;
-    const uint32_t e = (uint32_t)nn * (uint32_t)K + (uint32_t)k;  // weight index
-    const uint4 wb = decode8(codes[e >> 3], block_scale(q8, s2, e >> 6), lv);
-    const float* tp = st + rl * kTPitch + 8 * cc;
-    const uint32_t wv[4] = {wb.x, wb.y, wb.z, wb.w};
-    uint32_t o[4];
+  // operands of one 16-row block held in registers: this lane's 64 codes
+  // and block scale, and its B fragments (B[n][32 u + 8 g .. + 7]).  The
+  // next block's are requested before the current one is computed.
+  uint4 cw[2];
+  float sc;
+  uint4 bf[RP / 32];
+  auto fetch = [&](int nb) {
+    const int n = nb + row;
+    const bool ok = n < N && kok;
+    const uint32_t e = (uint32_t)n * (uint32_t)K + (uint32_t)(k0 + kl);  // first weight of the block
+    cw[0] = ok ? codes[e >> 5] : make_uint4(0, 0, 0, 0);
+    cw[1] = ok ? codes[(e >> 5) + 1] : make_uint4(0, 0, 0, 0);
+    sc = ok ? block_scale(q8, s2, e >> 6) : 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float w0 = bf16_to_f32((uint16_t)(wv[i] & 0xFFFFu)), w1 = bf16_to_f32((uint16_t)(wv[i] >> 16));
-      o[i] = pack_bf16x2(w0 + s * tp[2 * i], w1 + s * tp[2 * i + 1]);
+    for (int u = 0; u < RP / 32; ++u) {
+      const int j = 32 * u + 8 * g;
+      bf[u] = load8(B + (int64_t)n * r + j, r - j, n < N, vec);
     }
-    *reinterpret_cast<uint4*>(out + e) = make_uint4(o[0], o[1], o[2], o[3]);
+  };
+  const int nw0 = n0 + kWaveRows * wave;
+  fetch(nw0);
+
+  for (int sb = 0; sb < kSubBlocks; ++sb) {
+    const int nb = nw0 + 4 * kWaveRows * sb;
+    if (nb >= N) break;  // uniform over the wave
+    const uint4 cc0 = cw[0], cc1 = cw[1];
+    const float scc = sc;
+    uint4 bcur[RP / 32];
+#pragma unroll
+    for (int u = 0; u < RP / 32; ++u) bcur[u] = bf[u];
+    if (sb + 1 < kSubBlocks) fetch(nb + 4 * kWaveRows);
+
+    // acc[m][v] = t[nb + row][k0 + 64 g + 4 m + v] = sum_j A[j][k] B[n][j]
+    f32x4 acc[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < RP / 32; ++u) {
+      const int jb = 32 * u + 8 * g + q;
+      const bf16x8 bn = __builtin_bit_cast(bf16x8, bcur[u]);
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        // lane p + 4 q addresses row jb, stored columns 16 m + 4 p .. + 3; it
+        // receives stored column 16 m + (lane & 15), rows jb - q .. + 3 (and + 4 .. + 7)
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sa + jb * kAPitch + 16 * m + 4 * p));
+        const i16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sa + (jb + 4) * kAPitch + 16 * m + 4 * p));
+        const i16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bn, acc[m], 0, 0, 0);
+      }
+    }
+    // decode the block and form Wm = bf16(Wbf + s * t) into this wave's
+    // staging tile (row, columns 64 g .. + 63)
+    uint16_t* sw = so + wave * (kWaveRows * kOPitch);
+    const uint32_t cwd[8] = {cc0.x, cc0.y, cc0.z, cc0.w, cc1.x, cc1.y, cc1.z, cc1.w};
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint4 wb = decode8(cwd[d], scc, lv);  // weights 8 d .. 8 d + 7 = tiles 2 d, 2 d + 1
+      const uint32_t wv[4] = {wb.x, wb.y, wb.z, wb.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4& t = acc[2 * d + (i >> 1)];
+        const float w0 = bf16_to_f32((uint16_t)(wv[i] & 0xFFFFu)), w1 = bf16_to_f32((uint16_t)(wv[i] >> 16));
+        o[i] = pack_bf16x2(w0 + s * t[2 * (i & 1)], w1 + s * t[2 * (i & 1) + 1]);
+      }
+      *reinterpret_cast<uint4*>(sw + row * kOPitch + kl + 8 * d) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    // LDS operations of one wave complete in order: read the tile back row by
+    // row (two 512-byte rows per instruction) and write it out coalesced
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < kWaveRows / 2; ++i) {
+      const int rr = 2 * i + (lane >> 5), cl = 8 * (lane & 31);
+      const uint4 v = *reinterpret_cast<const uint4*>(sw + rr * kOPitch + cl);
+      typedef __attribute__((ext_vector_type(4))) unsigned v4u;
+      if (nb + rr < N && k0 + cl < K)
+        __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w},
+                                    reinterpret_cast<v4u*>(out + (size_t)(nb + rr) * K + k0 + cl));
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -118,8 +177,8 @@ __global__ __launch_bounds__(256) void k_merge(const uint32_t* __restrict__ code
 
 hipError_t launch_merge(const uint8_t* codes, const uint8_t* q8, const float* s2, int N, int K, const uint16_t* A,
                         const uint16_t* B, int r, float s, uint16_t* out, hipStream_t st) {
-  const dim3 grid((K + kMTileK - 1) / kMTileK, (N + kMTileN - 1) / kMTileN);
-  const uint32_t* cw = reinterpret_cast<const uint32_t*>(codes);
+  const dim3 grid((K + kTileK - 1) / kTileK, (N + kRowsPerWg - 1) / kRowsPerWg);
+  const uint4* cw = reinterpret_cast<const uint4*>(codes);
   if (r <= 32)
     hipLaunchKernelGGL(k_merge<32>, grid, dim3(256), 0, st, cw, q8, s2, N, K, A, B, r, s, out, nf4_consts());
   else

@@ -130,8 +130,10 @@ def _empty_u8(n, device):
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)[:n]
 
 
-def quantize(W: torch.Tensor) -> NF4Weight:
-    """fp32 or bf16 [n_out, k_in] GPU tensor -> NF4Weight (codes, q8, s2)."""
+def quantize(W: torch.Tensor, out: NF4Weight | None = None) -> NF4Weight:
+    """fp32 or bf16 [n_out, k_in] GPU tensor -> NF4Weight (codes, q8, s2).
+    ``out``: an NF4Weight of the same shape whose buffers are overwritten
+    (no allocation)."""
     if W.dim() != 2:
         raise ValueError("W must be 2-D [n_out, k_in]")
     n_out, k_in = W.shape
@@ -139,9 +141,19 @@ def quantize(W: torch.Tensor) -> NF4Weight:
     nb = nw // 64
     ng = (nb + 255) // 256
     dev = W.device
-    codes = _empty_u8(nw // 2, dev)
-    q8 = _empty_u8(nb, dev)
-    s2 = torch.empty(max(ng, 4), dtype=torch.float32, device=dev)[:ng]
+    if out is not None:
+        if (out.n_out, out.k_in) != (n_out, k_in):
+            raise ValueError("out has a different shape")
+        codes, q8, s2 = out.codes, out.absmax_q8, out.absmax_scale
+        for t, dt, n, name in ((codes, torch.uint8, nw // 2, "out.codes"), (q8, torch.uint8, nb, "out.absmax_q8"),
+                               (s2, torch.float32, ng, "out.absmax_scale")):
+            _dev(t, dt, name)
+            if t.device != dev or t.numel() < n:
+                raise ValueError(f"{name} must be on W's device and hold {n} elements")
+    else:
+        codes = _empty_u8(nw // 2, dev)
+        q8 = _empty_u8(nb, dev)
+        s2 = torch.empty(max(ng, 4), dtype=torch.float32, device=dev)[:ng]
     if W.dtype == torch.bfloat16:
         st = lib().qlora_quantize_nf4_dq_bf16(_dev(W, torch.bfloat16, "W"), n_out, k_in, codes.data_ptr(),
                                               q8.data_ptr(), s2.data_ptr(), _stream())
@@ -150,7 +162,7 @@ def quantize(W: torch.Tensor) -> NF4Weight:
         st = lib().qlora_quantize_nf4_dq(_dev(W, torch.float32, "W"), n_out, k_in, codes.data_ptr(),
                                          q8.data_ptr(), s2.data_ptr(), _stream())
         _check(st, "qlora_quantize_nf4_dq")
-    return NF4Weight(codes, q8, s2, n_out, k_in)
+    return out if out is not None else NF4Weight(codes, q8, s2, n_out, k_in)
 
 
 def merge(w: NF4Weight, A: torch.Tensor | None, B: torch.Tensor | None, r: int, alpha: float,

@@ -400,6 +400,8 @@ MERGE_SHAPES = [
     (64, 128, 64, 128.0),
     (72, 256, 0, 0.0),
     (1024, 4096, 16, 32.0),
+    (520, 768, 16, 32.0),     # a workgroup with one partial 16-row block
+    (264, 320, 40, 80.0),
 ]
 
 
@@ -465,6 +467,64 @@ def test_merge_and_requantize_parity(N, K, r, alpha):
     # the drift the pages warn about: the re-quantized weight vs the merged one
     drift = oracle.requant_drift(ref, q2, N, K)
     assert 0.0 <= drift < 0.2
+
+
+def _check_merged_rows(got, exact, ref, wb, A, B, sc, r):
+    tie, sp = _near_tie(exact, wb, A, B, sc, r)
+    bad = (got != ref) & ~tie
+    assert not bad.any(), (f"{bad.sum()} of {bad.size} differ; first at {np.argwhere(bad)[:4].tolist()}: "
+                           f"got {got[bad][:4]} ref {ref[bad][:4]} exact {exact[bad][:4]}")
+    if tie.any():
+        err = np.abs(oracle.f64_from_bf16_bits(got[tie]) - exact[tie])
+        assert np.all(err <= _merge_err_bound(wb, A, B, sc, r)[tie] + sp[tie])
+
+
+def test_merge_and_requantize_70b_gate_sampled_rows():
+    """Full-size merge (28672 x 8192, rank 16, the launch the bandwidth figure
+    times) and re-quantization: 16 sampled row pairs -- each pair is one
+    double-quantization group -- against the oracle's quantize, merge and
+    re-quantize of those rows."""
+    _need_gpu()
+    d = synth.workload_linear("70b", 0, m=1, with_grad=False)
+    N, K, r, alpha = d["n_out"], d["k_in"], d["r"], d["alpha"]
+    assert (2 * K) % (64 * 256) == 0  # a row pair is exactly one group
+    w = gpu_quantize(d["W"])
+    Wm = qlora.merge(w, dev_bf16(d["A"]), dev_bf16(d["B"]), r, alpha)
+    w2 = qlora.quantize(Wm)
+    torch.cuda.synchronize()
+    pairs = sorted(set([0, N // 2 - 1] + list(np.random.default_rng(7).choice(N // 2, 14, replace=False))))
+    rows = np.array([2 * p + i for p in pairs for i in (0, 1)])
+    part = oracle.quantize_groups(d["W"].ravel(), pairs)
+    wb = np.concatenate([oracle.dequant(part[g]["codes"], part[g]["absmax_q8"], part[g]["absmax_scale"], 2, K,
+                                        first_block=256 * g)[1] for g in pairs])
+    exact, ref = oracle.merge(wb, d["A"], d["B"][rows], alpha, r)
+    got = host_bits(Wm[torch.from_numpy(rows).cuda()])
+    sc = oracle.lora_scale(alpha, r)
+    _check_merged_rows(got, exact, ref, wb, d["A"], d["B"][rows], sc, r)
+    codes = w2.codes.cpu().numpy()
+    q8 = w2.absmax_q8.cpu().numpy()
+    s2 = w2.absmax_scale.cpu().numpy()
+    for i, g in enumerate(pairs):
+        gref, gget = ref[2 * i:2 * i + 2], got[2 * i:2 * i + 2]
+        if not np.array_equal(gref, gget):
+            continue  # a near-tie rounded the other way: inputs differ
+        q2 = oracle.requantize(gref, 2, K)
+        assert np.array_equal(codes[g * 8192:(g + 1) * 8192], q2["codes"]), g
+        assert np.array_equal(q8[g * 256:(g + 1) * 256], q2["absmax_q8"]), g
+        assert s2[g].view(np.uint32) == q2["absmax_scale"][0].view(np.uint32), g
+
+
+def test_quantize_into_preallocated_buffers():
+    """quantize(W, out=w) overwrites w's buffers with the same result as a
+    fresh quantization, also when they held another weight's codes."""
+    _need_gpu()
+    d = synth.workload_linear("cfg1", 0)
+    q = oracle.quantize_nf4_dq(d["W"])
+    w = gpu_quantize(np.ascontiguousarray(d["W"][::-1]))  # other contents, same shape
+    got = qlora.quantize(torch.from_numpy(np.ascontiguousarray(d["W"])).cuda(), out=w)
+    torch.cuda.synchronize()
+    assert got is w
+    check_codec_exact(w, q)
 
 
 def test_quantize_bf16_input_bit_exact():
