@@ -23,6 +23,8 @@ Modules:
 * :mod:`oracle.qlora_linear` -- forward and backward of the adapted linear.
 * :mod:`oracle.merge` -- merging the adapter into the weight and
   re-quantizing the result.
+* :mod:`oracle.dropout` -- LoRA dropout of the adapter input: the
+  counter-based mask generator and the dropped forward and backward.
 
 Every function pinned by a ``-m "not gpu"`` test says which pin covers it.
 The one construction the pages leave fully open -- the tail offset of the
@@ -51,3 +53,11 @@ from .nf4_dq import (  # noqa: F401
 )
 from .qlora_linear import lora_scale, linear_fwd, linear_bwd  # noqa: F401
 from .merge import bf16_bits_from_f64, merge, requantize, requant_drift  # noqa: F401
+from .dropout import (  # noqa: F401
+    philox4x32_10,
+    dropout_threshold,
+    dropout_words,
+    dropout_mask,
+    linear_fwd_dropout,
+    linear_bwd_dropout,
+)
