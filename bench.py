@@ -217,6 +217,30 @@ def main():
     secondary = None
     if not args.no_secondary:
         secondary = bench_secondary(torch, qlora, synth, dev, evs)
+        # the same layer step with LoRA dropout p = 0.05 on every adapter
+        # input (the pages' setting), a fresh mask per step and linear
+        p_drop = 0.05
+
+        def step_drop(k):
+            for i, e in enumerate(lins):
+                sd = (k << 8) | i
+                qlora.linear_fwd(e["w"], e["X"], e["A"], e["B"], r, alpha, Y=e["Y"], U=e["U"], ws=e["ws_fwd"],
+                                 dropout_p=p_drop, seed=sd)
+                qlora.linear_bwd(e["w"], e["X"], e["dY"], e["A"], e["B"], r, alpha, e["U"],
+                                 dX=e["dX"], dA=e["dA"], dB=e["dB"], ws=e["ws"], dropout_p=p_drop, seed=sd)
+
+        for k in range(2):
+            step_drop(k)
+        torch.cuda.synchronize()
+        t0.record()
+        for k in range(args.steps):
+            step_drop(100 + k)
+        t1.record()
+        torch.cuda.synchronize()
+        ms_d = t0.elapsed_time(t1) / max(1, args.steps)
+        secondary["layer_7b_dropout_0.05"] = {
+            "ms_per_step": round(ms_d, 4), "TFLOP/s": round(step_flops / (ms_d * 1e-3) / 1e12, 2),
+            "slowdown_vs_no_dropout": round(ms_d / ms_per_step, 4)}
 
     # ---------------------------------------------------- cpu baseline ----
     cpu = None

@@ -3,6 +3,7 @@
 // Declarations and the contract of every entry point: include/qlora.h.
 #include <algorithm>
 #include <climits>
+#include <cmath>
 #include <cstring>
 #include <string>
 
@@ -24,11 +25,11 @@ hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_dx(const GemmArgs& a, hipStream_t st);
 void time_next_gemm(hipEvent_t start, hipEvent_t stop);
 hipError_t launch_lora_down(const uint16_t* X, int M, int K, const uint16_t* A, int r, float s, uint16_t* U,
-                            float* part, hipStream_t st);
+                            float* part, DropMask drop, hipStream_t st);
 size_t rowdot_part_bytes(int64_t M, int64_t Kd, int r);
 int coldot_chunk_rows();
 hipError_t launch_coldot(const uint16_t* v, int r, const uint16_t* in, int M, int C, float* part,
-                         hipStream_t st);
+                         DropMask drop, hipStream_t st);
 hipError_t launch_finalize(const float* part, int nmc, int r, int C, float* out, bool trans, hipStream_t st);
 hipError_t launch_vt_and_db(const uint16_t* dY, int M, int N, const uint16_t* B, const uint16_t* U, int r,
                             float s, uint16_t* V, float* vpart, float* cpart, float* dB, hipStream_t st);
@@ -91,6 +92,23 @@ int check_rows(int64_t M, int64_t n_out, int64_t k_in) {
 }
 
 float lora_scale(float alpha, int32_t r) { return r > 0 ? alpha / (float)r : 0.f; }
+
+// Dropout of the adapter input: keep threshold floor(p 2^32), key = seed, and
+// the adapter scale with the 1 / (1 - p) of inverted dropout folded in,
+// fp32(alpha / (r (1 - p))).  p = 0 is the plain layer.
+int dropout_setup(int32_t r, float alpha, double p, uint64_t seed, qlora::DropMask* dm, float* s) {
+  if (!(p >= 0.0 && p < 1.0)) return fail(QLORA_ERR_INVALID_ARG, "dropout_p must be in [0, 1)");
+  *dm = qlora::DropMask{};
+  if (p == 0.0) {
+    *s = lora_scale(alpha, r);
+    return QLORA_OK;
+  }
+  dm->thr = (uint32_t)std::floor(p * 4294967296.0);  // < 2^32 since p < 1
+  dm->k0 = (uint32_t)seed;
+  dm->k1 = (uint32_t)(seed >> 32);
+  *s = r > 0 ? (float)((double)alpha / ((double)r * (1.0 - p))) : 0.f;
+  return QLORA_OK;
+}
 
 struct BwdLayout {
   size_t u, v, part, cpart, total;  // part: U~ / V~ split-K partials; cpart: dA / dB row-chunk partials
@@ -202,9 +220,9 @@ int qlora_dequant(const qlora_nf4_weight* w, uint16_t* W_bf16, hipStream_t strea
   return e == hipSuccess ? QLORA_OK : hip_fail(e, "dequant launch");
 }
 
-int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, const uint16_t* A,
-                     const uint16_t* B, int32_t r, float alpha, uint16_t* Y, uint16_t* U_out, void* ws,
-                     size_t ws_bytes, hipStream_t stream) {
+static int linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, const uint16_t* A,
+                           const uint16_t* B, int32_t r, float alpha, const qlora::DropMask& dm, float s,
+                           uint16_t* Y, uint16_t* U_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_weight(w);
   if (st) return st;
   if ((st = check_adapter(r, A, B))) return st;
@@ -227,10 +245,9 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, co
     U = U_out ? U_out : reinterpret_cast<uint16_t*>(base);
     if (pbytes) part = reinterpret_cast<float*>(base + ubytes);
   }
-  const float s = lora_scale(alpha, r);
   hipError_t e;
   if (r > 0 && w->k_in > 0) {
-    e = qlora::launch_lora_down(X, (int)M, (int)w->k_in, A, r, s, U, part, stream);
+    e = qlora::launch_lora_down(X, (int)M, (int)w->k_in, A, r, s, U, part, dm, stream);
     if (e != hipSuccess) return hip_fail(e, "lora_down launch");
   } else if (r > 0) {
     // k_in == 0: X A^T is an empty sum
@@ -257,9 +274,10 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, co
   return e == hipSuccess ? QLORA_OK : hip_fail(e, "forward GEMM launch");
 }
 
-int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t M,
-                     const uint16_t* A, const uint16_t* B, int32_t r, float alpha, const uint16_t* U,
-                     uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, hipStream_t stream) {
+static int linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t M,
+                           const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                           const qlora::DropMask& dm, float s, const uint16_t* U, uint16_t* dX, float* dA,
+                           float* dB, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_weight(w);
   if (st) return st;
   if ((st = check_adapter(r, A, B))) return st;
@@ -298,7 +316,6 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_
     return QLORA_OK;
   }
 
-  const float s = lora_scale(alpha, r);
   char* base = static_cast<char*>(ws);
   uint16_t* Ut = nullptr;
   uint16_t* Vt = nullptr;
@@ -310,15 +327,15 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_
       Ut = const_cast<uint16_t*>(U);
     } else {
       Ut = reinterpret_cast<uint16_t*>(base + L.u);
-      if ((e = qlora::launch_lora_down(X, (int)M, (int)K, A, r, s, Ut, part, stream)) != hipSuccess)
+      if ((e = qlora::launch_lora_down(X, (int)M, (int)K, A, r, s, Ut, part, dm, stream)) != hipSuccess)
         return hip_fail(e, "lora_down launch");
     }
     // V~ = bf16(s dY B) and dB = dY^T U~ (stored [N x r]): both read dY
     float* cpart = reinterpret_cast<float*>(base + L.cpart);
     if ((e = qlora::launch_vt_and_db(dY, (int)M, (int)N, B, Ut, r, s, Vt, part, cpart, dB, stream)) != hipSuccess)
       return hip_fail(e, "V~ / dB launch");
-    // dA = V~^T X  ([r x K])
-    if ((e = qlora::launch_coldot(Vt, r, X, (int)M, (int)K, cpart, stream)) != hipSuccess)
+    // dA = V~^T (mask * X)  ([r x K])
+    if ((e = qlora::launch_coldot(Vt, r, X, (int)M, (int)K, cpart, dm, stream)) != hipSuccess)
       return hip_fail(e, "dA partials launch");
     if ((e = qlora::launch_finalize(cpart, L.nmc, r, (int)K, dA, false, stream)) != hipSuccess)
       return hip_fail(e, "dA finalize launch");
@@ -329,8 +346,44 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_
   g.lora_act = Vt; g.lora_w = A; g.r = r;
   g.out = dX; g.ld_out = K;
   g.nf4 = qlora::nf4_consts();
+  g.drop = dm;
   e = qlora::launch_gemm_dx(g, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e, "dX GEMM launch");
+}
+
+int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, const uint16_t* A,
+                     const uint16_t* B, int32_t r, float alpha, uint16_t* Y, uint16_t* U_out, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  return linear_fwd_impl(w, X, M, A, B, r, alpha, qlora::DropMask{}, lora_scale(alpha, r), Y, U_out, ws, ws_bytes,
+                         stream);
+}
+
+int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t M,
+                     const uint16_t* A, const uint16_t* B, int32_t r, float alpha, const uint16_t* U,
+                     uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return linear_bwd_impl(w, X, dY, M, A, B, r, alpha, qlora::DropMask{}, lora_scale(alpha, r), U, dX, dA, dB, ws,
+                         ws_bytes, stream);
+}
+
+int qlora_linear_fwd_dropout(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, const uint16_t* A,
+                             const uint16_t* B, int32_t r, float alpha, double dropout_p, uint64_t seed,
+                             uint16_t* Y, uint16_t* U_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  qlora::DropMask dm{};
+  float s = 0.f;
+  const int st = dropout_setup(r, alpha, dropout_p, seed, &dm, &s);
+  if (st) return st;
+  return linear_fwd_impl(w, X, M, A, B, r, alpha, dm, s, Y, U_out, ws, ws_bytes, stream);
+}
+
+int qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t M,
+                             const uint16_t* A, const uint16_t* B, int32_t r, float alpha, double dropout_p,
+                             uint64_t seed, const uint16_t* U, uint16_t* dX, float* dA, float* dB, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  qlora::DropMask dm{};
+  float s = 0.f;
+  const int st = dropout_setup(r, alpha, dropout_p, seed, &dm, &s);
+  if (st) return st;
+  return linear_bwd_impl(w, X, dY, M, A, B, r, alpha, dm, s, U, dX, dA, dB, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -32,6 +32,7 @@
 // lookup table held as byte planes in registers and indexed with v_perm_b32;
 // the two lanes sharing a block each build half the table and swap halves
 // with one DPP move.  No LDS traffic for the lookup.
+#include "dropout.h"
 #include "gemm_args.h"
 #include "nf4_lut.h"
 
@@ -364,60 +365,10 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  if (producer) {
-    const bool odd = lane & 1;
-    float th[8];
-    lane_levels(a.nf4, odd, th);
-    const LaneMask lm = lane_mask(odd);
-    const Srcs src = make_srcs<NN>(a);
-    const ActRows rows = act_rows(a, row0, lane);
-
-    // Issue order inside a step: code loads first, then activation copies,
-    // so that waiting for the codes of step s + 1 (decoded at step s) never
-    // waits for the copies issued after them (vmcnt retires in order).
-    CodeSeg c0s = load_codes<NN>(a, src, c0, kofs(0), ptid);
-    copy_act(a, src, rows, act_lds(stage_of(0)), kofs(0), lane);
-    CodeSeg c1s = load_codes<NN>(a, src, c0, kofs(1), ptid);
-    copy_act(a, src, rows, act_lds(stage_of(1)), kofs(1), lane);
-    decode_store<NN>(w_buf0, c0s, th, lm, ptid);
-    // copies of step 0 done: younger are the codes (3) and copies (8) of step 1
-    wait_vmcnt<11>();
-    __syncthreads();
-
-    auto body = [&](int step, CodeSeg& load_slot, const CodeSeg& dec, uint16_t* w_next) {
-      load_slot = load_codes<NN>(a, src, c0, kofs(step + 2), ptid);
-      __builtin_amdgcn_sched_barrier(0);  // keep all code loads ahead of the copies
-      copy_act(a, src, rows, act_lds(stage_of(step + 2)), kofs(step + 2), lane);
-      decode_store<NN>(w_next, dec, th, lm, ptid);
-      // copies of step s + 1 done: younger are the codes (3) and copies (8)
-      // of step s + 2
-      wait_vmcnt<11>();
-      step_barrier();
-    };
-    for (int step = 0; step < nst; step += 2) {
-      body(step, c0s, c1s, w_buf1);
-      body(step + 1, c1s, c0s, w_buf0);
-    }
-    wait_vmcnt<0>();  // nothing left in flight into the activation ring
-  } else {
-    __syncthreads();  // tile 0 and activations of step 0 are ready
-    const CodeSeg none{};
-    const float th0[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    const LaneMask lm0{0, 0, 0};
-    for (int step = 0; step < nst; step += 2) {
-      mma_step<NN, false>(acc, act_ptr(stage_of(step)), w_buf0, w_buf1, none, th0, lm0, 0, lane);
-      step_barrier();
-      mma_step<NN, false>(acc, act_ptr(stage_of(step + 1)), w_buf1, w_buf0, none, th0, lm0, 0, lane);
-      step_barrier();
-    }
-  }
-
   // ---- adapter step: r extra reduction columns j = 16 ks + 8 h + e --------
-  if (a.r > 0) {
-    // W buffer 0 and activation stage stage_of(nst) are no longer read.
+  // (sw: a W buffer, sa: this slice's activation stage, both free)
+  auto adapter_step = [&](uint16_t* sw, uint16_t* sa) {
     __syncthreads();
-    uint16_t* sw = w_buf0;
-    uint16_t* sa = act_ptr(stage_of(nst));
     if (producer) {
       const Srcs src = make_srcs<NN>(a);
       // All loads of the fill are issued before any LDS store (16-byte
@@ -469,7 +420,95 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
       const LaneMask lm0{0, 0, 0};
       mma_step<NN, false>(acc, sa, sw, sw, none, th0, lm0, 0, lane);
     }
+  };
+
+  // ---- dX with LoRA dropout: the adapter's part of dX passes through the
+  // dropout mask of the adapter input, mask * (V~ A).  The adapter step then
+  // runs first, alone in the accumulators, which are masked before the main
+  // reduction adds dY Wbf.  The producer of each slice draws the slice's
+  // 64 x 128 keep bytes into activation stage 1 meanwhile.
+  const bool drop_first = NN && a.drop.thr != 0 && a.r > 0;
+  if (drop_first) {
+    adapter_step(w_buf0, act_ptr(0));
+    uint8_t* keep = reinterpret_cast<uint8_t*>(act_ptr(1));
+    if (producer) {
+#pragma unroll 4
+      for (int t = 0; t < 32; ++t) {  // (row, 4-column group) pairs q = lane + 64 t
+        const int q = lane + 64 * t, rl = q >> 5, g = q & 31;
+        const uint64_t e = (uint64_t)(row0 + rl) * (uint64_t)a.C + (uint64_t)(c0 + 4 * g);
+        const uint64_t ctr = e >> 2;
+        const uint4 u = philox4x32_10(make_uint4((uint32_t)ctr, (uint32_t)(ctr >> 32), 0u, 0u), a.drop.k0, a.drop.k1);
+        const uint32_t kb = (u.x >= a.drop.thr ? 1u : 0u) | (u.y >= a.drop.thr ? 1u << 8 : 0u) |
+                            (u.z >= a.drop.thr ? 1u << 16 : 0u) | (u.w >= a.drop.thr ? 1u << 24 : 0u);
+        *reinterpret_cast<uint32_t*>(keep + 4 * q) = kb;  // byte rl * 128 + 4 g + i
+      }
+    }
+    __syncthreads();
+    if (!producer) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int rl = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), cl = 32 * j + (lane & 31);
+            if (!keep[rl * 128 + cl]) acc[i][j][v] = 0.f;
+          }
+    }
+    __syncthreads();  // stages 0 / 1 and W buffer 0 are refilled below
   }
+
+  if (producer) {
+    const bool odd = lane & 1;
+    float th[8];
+    lane_levels(a.nf4, odd, th);
+    const LaneMask lm = lane_mask(odd);
+    const Srcs src = make_srcs<NN>(a);
+    const ActRows rows = act_rows(a, row0, lane);
+
+    // Issue order inside a step: code loads first, then activation copies,
+    // so that waiting for the codes of step s + 1 (decoded at step s) never
+    // waits for the copies issued after them (vmcnt retires in order).
+    CodeSeg c0s = load_codes<NN>(a, src, c0, kofs(0), ptid);
+    copy_act(a, src, rows, act_lds(stage_of(0)), kofs(0), lane);
+    CodeSeg c1s = load_codes<NN>(a, src, c0, kofs(1), ptid);
+    copy_act(a, src, rows, act_lds(stage_of(1)), kofs(1), lane);
+    decode_store<NN>(w_buf0, c0s, th, lm, ptid);
+    // copies of step 0 done: younger are the codes (3) and copies (8) of step 1
+    wait_vmcnt<11>();
+    __syncthreads();
+
+    auto body = [&](int step, CodeSeg& load_slot, const CodeSeg& dec, uint16_t* w_next) {
+      load_slot = load_codes<NN>(a, src, c0, kofs(step + 2), ptid);
+      __builtin_amdgcn_sched_barrier(0);  // keep all code loads ahead of the copies
+      copy_act(a, src, rows, act_lds(stage_of(step + 2)), kofs(step + 2), lane);
+      decode_store<NN>(w_next, dec, th, lm, ptid);
+      // copies of step s + 1 done: younger are the codes (3) and copies (8)
+      // of step s + 2
+      wait_vmcnt<11>();
+      step_barrier();
+    };
+    for (int step = 0; step < nst; step += 2) {
+      body(step, c0s, c1s, w_buf1);
+      body(step + 1, c1s, c0s, w_buf0);
+    }
+    wait_vmcnt<0>();  // nothing left in flight into the activation ring
+  } else {
+    __syncthreads();  // tile 0 and activations of step 0 are ready
+    const CodeSeg none{};
+    const float th0[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const LaneMask lm0{0, 0, 0};
+    for (int step = 0; step < nst; step += 2) {
+      mma_step<NN, false>(acc, act_ptr(stage_of(step)), w_buf0, w_buf1, none, th0, lm0, 0, lane);
+      step_barrier();
+      mma_step<NN, false>(acc, act_ptr(stage_of(step + 1)), w_buf1, w_buf0, none, th0, lm0, 0, lane);
+      step_barrier();
+    }
+  }
+
+  // ---- adapter step at the end (no dropout): W buffer 0 and activation
+  // stage nst % 3 are no longer read
+  if (a.r > 0 && !drop_first) adapter_step(w_buf0, act_ptr(stage_of(nst)));
 
   // ---- epilogue: fp32 -> bf16 (round to nearest even) ---------------------
   if (!producer) {

@@ -2,6 +2,7 @@
 #pragma once
 
 #include "common.h"
+#include "dropout.h"
 
 namespace qlora {
 
@@ -21,6 +22,7 @@ struct GemmArgs {
   uint16_t* out;             // Y [M x n_out] or dX [M x k_in], bf16
   int64_t ld_out;
   Nf4Consts nf4;
+  DropMask drop;             // dX only: dropout of the adapter input (thr 0: none)
 };
 
 }  // namespace qlora

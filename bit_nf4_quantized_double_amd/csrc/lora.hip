@@ -11,6 +11,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "dropout.h"
 
 namespace qlora {
 
@@ -72,6 +73,7 @@ struct RowdotArgs {
   float scale;
   uint16_t* out;       // [M x r] bf16
   float* part;         // [nsplit][M][r] fp32, or null when nsplit == 1
+  DropMask drop;       // dropout of `in` (thr 0: none)
 };
 
 // Workgroup (bx, by) = (64-row block, K split) of the rowdot grid.
@@ -103,6 +105,11 @@ __device__ __forceinline__ void rowdot_body(const RowdotArgs& ra, int bx, int by
     for (int u = 0; u < 8; ++u) {
       const int k = k0 + 32 * u + 8 * kg;
       av[u] = buf_load16(rin, k < k_hi ? row_off + 2u * (uint32_t)k : kOOB);
+    }
+    if (ra.drop.thr) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        av[u] = drop8(av[u], (uint64_t)(m0 + row) * (uint64_t)Kd + (uint64_t)(k0 + 32 * u + 8 * kg), ra.drop);
     }
     // stage w for k0 .. k0 + 255 (zero past r / k_hi)
     __syncthreads();  // previous sub-chunk's reads of sw are done
@@ -216,6 +223,7 @@ struct ColdotArgs {
   const uint16_t* in;  // [M x C] bf16 (dY or X)
   int M, C, mchunk;
   float* part;         // [nmc][r][C] fp32
+  DropMask drop;       // dropout of `in` (thr 0: none)
 };
 
 // Workgroup (bx, by) = (128-column tile, row chunk) of the coldot grid.
@@ -243,6 +251,11 @@ __device__ __forceinline__ void coldot_body(const ColdotArgs& ca, int bx, int by
       const int m = m0 + 8 * g + i;
       rows[i] = (m < mend && col_ok) ? *reinterpret_cast<const uint4*>(in + (int64_t)m * C + c0 + 8 * q)
                                      : make_uint4(0, 0, 0, 0);
+    }
+    if (ca.drop.thr) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        rows[i] = drop8(rows[i], (uint64_t)(m0 + 8 * g + i) * (uint64_t)C + (uint64_t)(c0 + 8 * q), ca.drop);
     }
     bf16x8 colv[8];
 #pragma unroll
@@ -362,23 +375,23 @@ __global__ __launch_bounds__(256) void k_zero_u16(uint16_t* __restrict__ p, int6
 
 template <bool CONTIG, int RT>
 void rowdot_launch(dim3 grid, hipStream_t st, const uint16_t* in, int M, int Kd, const uint16_t* wt, int r,
-                   int kchunk, float scale, uint16_t* out, float* part) {
-  const RowdotArgs ra{in, M, Kd, wt, r, kchunk, (int)grid.y, scale, out, part};
+                   int kchunk, float scale, uint16_t* out, float* part, DropMask drop) {
+  const RowdotArgs ra{in, M, Kd, wt, r, kchunk, (int)grid.y, scale, out, part, drop};
   hipLaunchKernelGGL((k_rowdot<CONTIG, RT>), grid, dim3(256), 0, st, ra);
 }
 
 template <bool CONTIG>
 hipError_t rowdot_dispatch(const uint16_t* in, int M, int Kd, const uint16_t* wt, int r, float scale,
-                           uint16_t* out, float* part, hipStream_t st) {
+                           uint16_t* out, float* part, DropMask drop, hipStream_t st) {
   int nsplit, kchunk;
   rowdot_split(M, Kd, &nsplit, &kchunk);
   dim3 grid((M + 63) / 64, nsplit);
   float* p = nsplit > 1 ? part : nullptr;
   switch ((r + 15) / 16) {
-    case 1: rowdot_launch<CONTIG, 1>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p); break;
-    case 2: rowdot_launch<CONTIG, 2>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p); break;
-    case 3: rowdot_launch<CONTIG, 3>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p); break;
-    default: rowdot_launch<CONTIG, 4>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p); break;
+    case 1: rowdot_launch<CONTIG, 1>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
+    case 2: rowdot_launch<CONTIG, 2>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
+    case 3: rowdot_launch<CONTIG, 3>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
+    default: rowdot_launch<CONTIG, 4>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
@@ -390,21 +403,22 @@ hipError_t rowdot_dispatch(const uint16_t* in, int M, int Kd, const uint16_t* wt
 
 }  // namespace
 
-// U~ = bf16(s X A^T): in = X [M x K], A [r x K]
+// U~ = bf16(s (mask * X) A^T): in = X [M x K], A [r x K]
 hipError_t launch_lora_down(const uint16_t* X, int M, int K, const uint16_t* A, int r, float s, uint16_t* U,
-                            float* part, hipStream_t st) {
-  return rowdot_dispatch<true>(X, M, K, A, r, s, U, part, st);
+                            float* part, DropMask drop, hipStream_t st) {
+  return rowdot_dispatch<true>(X, M, K, A, r, s, U, part, drop, st);
 }
 
 
 int coldot_chunk_rows() { return 256; }
 
-// part[mc][j][c] = sum over the mc-th chunk of rows of v[m][j] * in[m][c]
-hipError_t launch_coldot(const uint16_t* v, int r, const uint16_t* in, int M, int C, float* part, hipStream_t st) {
+// part[mc][j][c] = sum over the mc-th chunk of rows of v[m][j] * (mask * in)[m][c]
+hipError_t launch_coldot(const uint16_t* v, int r, const uint16_t* in, int M, int C, float* part, DropMask drop,
+                         hipStream_t st) {
   const int mchunk = coldot_chunk_rows();
   dim3 grid((C + 127) / 128, (M + mchunk - 1) / mchunk);
   const int rt = (r + 15) / 16;
-  const ColdotArgs ca{v, r, in, M, C, mchunk, part};
+  const ColdotArgs ca{v, r, in, M, C, mchunk, part, drop};
   switch (rt) {
     case 1: hipLaunchKernelGGL((k_coldot<1>), grid, dim3(256), 0, st, ca); break;
     case 2: hipLaunchKernelGGL((k_coldot<2>), grid, dim3(256), 0, st, ca); break;
@@ -422,10 +436,10 @@ hipError_t launch_vt_and_db(const uint16_t* dY, int M, int N, const uint16_t* B,
   int nsplit, kchunk;
   rowdot_split(M, N, &nsplit, &kchunk);
   const int rb = (M + 63) / 64;
-  const RowdotArgs ra{dY, M, N, B, r, kchunk, nsplit, s, V, nsplit > 1 ? vpart : nullptr};
+  const RowdotArgs ra{dY, M, N, B, r, kchunk, nsplit, s, V, nsplit > 1 ? vpart : nullptr, DropMask{}};
   const int mchunk = coldot_chunk_rows();
   const int ctiles = (N + 127) / 128, nmc = (M + mchunk - 1) / mchunk;
-  const ColdotArgs ca{U, r, dY, M, N, mchunk, cpart};
+  const ColdotArgs ca{U, r, dY, M, N, mchunk, cpart, DropMask{}};
   const dim3 grid(rb * nsplit + ctiles * nmc);
   switch ((r + 15) / 16) {
     case 1: hipLaunchKernelGGL((k_vt_and_db<1>), grid, dim3(256), 0, st, ra, rb, ca, ctiles); break;

@@ -55,6 +55,12 @@ def lib() -> ctypes.CDLL:
                                             _vp, _vp, _vp, ctypes.c_size_t, _vp]),
         "qlora_linear_bwd": (ctypes.c_int, [W, _vp, _vp, _c_i64, _vp, _vp, _c_i32, ctypes.c_float,
                                             _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+        "qlora_linear_fwd_dropout": (ctypes.c_int, [W, _vp, _c_i64, _vp, _vp, _c_i32, ctypes.c_float,
+                                                    ctypes.c_double, ctypes.c_uint64,
+                                                    _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+        "qlora_linear_bwd_dropout": (ctypes.c_int, [W, _vp, _vp, _c_i64, _vp, _vp, _c_i32, ctypes.c_float,
+                                                    ctypes.c_double, ctypes.c_uint64,
+                                                    _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
         "qlora_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i32]),
         "qlora_nf4_table": (None, [ctypes.POINTER(ctypes.c_float)]),
         "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -205,8 +211,12 @@ def _ws(nbytes: int, device, ws: torch.Tensor | None):
 def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None,
                r: int, alpha: float, *, Y: torch.Tensor | None = None,
                U: torch.Tensor | None = None, return_u: bool = True,
-               ws: torch.Tensor | None = None):
-    """Y = X W^T + U~ B^T with U~ = bf16((alpha/r) X A^T).  Returns (Y, U~)."""
+               ws: torch.Tensor | None = None, dropout_p: float = 0.0, seed: int = 0):
+    """Y = X W^T + U~ B^T with U~ = bf16((alpha/r) X A^T).  Returns (Y, U~).
+
+    dropout_p > 0: LoRA dropout of the adapter input with the keep mask of
+    ``seed`` (qlora_linear_fwd_dropout); U~ = bf16(alpha/(r(1-p)) (keep X) A^T).
+    """
     M = X.shape[0]
     dev = X.device
     if Y is None:
@@ -216,20 +226,29 @@ def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor | None, B: torch.T
     wsb = workspace_bytes(QLORA_OP_FWD, M, w.n_out, w.k_in, r)
     wst, wsn = _ws(wsb, dev, ws)
     cw = w._c()
-    st = lib().qlora_linear_fwd(
-        ctypes.byref(cw), _dev(X, torch.bfloat16, "X"), M,
-        _opt(A, torch.bfloat16, "A"), _opt(B, torch.bfloat16, "B"), r, float(alpha),
-        _dev(Y, torch.bfloat16, "Y"), _opt(U, torch.bfloat16, "U"),
-        None if wst is None else wst.data_ptr(), wsn, _stream())
-    _check(st, "qlora_linear_fwd")
+    head = (ctypes.byref(cw), _dev(X, torch.bfloat16, "X"), M,
+            _opt(A, torch.bfloat16, "A"), _opt(B, torch.bfloat16, "B"), r, float(alpha))
+    tail = (_dev(Y, torch.bfloat16, "Y"), _opt(U, torch.bfloat16, "U"),
+            None if wst is None else wst.data_ptr(), wsn, _stream())
+    if dropout_p:
+        st = lib().qlora_linear_fwd_dropout(*head, float(dropout_p), int(seed) & (2**64 - 1), *tail)
+        _check(st, "qlora_linear_fwd_dropout")
+    else:
+        st = lib().qlora_linear_fwd(*head, *tail)
+        _check(st, "qlora_linear_fwd")
     return Y, U
 
 
 def linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor | None,
                B: torch.Tensor | None, r: int, alpha: float, U: torch.Tensor | None = None, *,
                dX: torch.Tensor | None = None, dA: torch.Tensor | None = None,
-               dB: torch.Tensor | None = None, ws: torch.Tensor | None = None):
-    """Returns (dX bf16 [M,K], dA fp32 [r,K], dB fp32 [N,r]); never dW."""
+               dB: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+               dropout_p: float = 0.0, seed: int = 0):
+    """Returns (dX bf16 [M,K], dA fp32 [r,K], dB fp32 [N,r]); never dW.
+
+    dropout_p > 0: the backward of :func:`linear_fwd` with the same
+    ``dropout_p`` and ``seed`` (qlora_linear_bwd_dropout).
+    """
     M = X.shape[0]
     dev = X.device
     if dX is None:
@@ -241,13 +260,17 @@ def linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor 
     wsb = workspace_bytes(QLORA_OP_BWD, M, w.n_out, w.k_in, r)
     wst, wsn = _ws(wsb, dev, ws)
     cw = w._c()
-    st = lib().qlora_linear_bwd(
-        ctypes.byref(cw), _dev(X, torch.bfloat16, "X"), _dev(dY, torch.bfloat16, "dY"), M,
-        _opt(A, torch.bfloat16, "A"), _opt(B, torch.bfloat16, "B"), r, float(alpha),
-        _opt(U, torch.bfloat16, "U"), _dev(dX, torch.bfloat16, "dX"),
-        _opt(dA, torch.float32, "dA"), _opt(dB, torch.float32, "dB"),
-        None if wst is None else wst.data_ptr(), wsn, _stream())
-    _check(st, "qlora_linear_bwd")
+    head = (ctypes.byref(cw), _dev(X, torch.bfloat16, "X"), _dev(dY, torch.bfloat16, "dY"), M,
+            _opt(A, torch.bfloat16, "A"), _opt(B, torch.bfloat16, "B"), r, float(alpha))
+    tail = (_opt(U, torch.bfloat16, "U"), _dev(dX, torch.bfloat16, "dX"),
+            _opt(dA, torch.float32, "dA"), _opt(dB, torch.float32, "dB"),
+            None if wst is None else wst.data_ptr(), wsn, _stream())
+    if dropout_p:
+        st = lib().qlora_linear_bwd_dropout(*head, float(dropout_p), int(seed) & (2**64 - 1), *tail)
+        _check(st, "qlora_linear_bwd_dropout")
+    else:
+        st = lib().qlora_linear_bwd(*head, *tail)
+        _check(st, "qlora_linear_bwd")
     return dX, dA, dB
 
 
@@ -255,29 +278,32 @@ class QLoRALinearFunction(torch.autograd.Function):
     """Autograd wrapper: forward saves U~ for the backward; no grad for W."""
 
     @staticmethod
-    def forward(ctx, X, A, B, w: NF4Weight, r: int, alpha: float):
+    def forward(ctx, X, A, B, w: NF4Weight, r: int, alpha: float, dropout_p: float = 0.0, seed: int = 0):
         X2 = X.reshape(-1, w.k_in).contiguous()
-        Y, U = linear_fwd(w, X2, A, B, r, alpha)
+        Y, U = linear_fwd(w, X2, A, B, r, alpha, dropout_p=dropout_p, seed=seed)
         ctx.save_for_backward(X2, A, B, U)
         ctx.w, ctx.r, ctx.alpha, ctx.xshape = w, r, alpha, X.shape
+        ctx.dropout_p, ctx.seed = dropout_p, seed
         return Y.reshape(*X.shape[:-1], w.n_out)
 
     @staticmethod
     def backward(ctx, dY):
         X2, A, B, U = ctx.saved_tensors
         dY2 = dY.reshape(-1, ctx.w.n_out).contiguous().to(torch.bfloat16)
-        dX, dA, dB = linear_bwd(ctx.w, X2, dY2, A, B, ctx.r, ctx.alpha, U)
+        dX, dA, dB = linear_bwd(ctx.w, X2, dY2, A, B, ctx.r, ctx.alpha, U,
+                                dropout_p=ctx.dropout_p, seed=ctx.seed)
         gA = dA.to(A.dtype) if (A is not None and ctx.needs_input_grad[1]) else None
         gB = dB.to(B.dtype) if (B is not None and ctx.needs_input_grad[2]) else None
-        return dX.reshape(ctx.xshape), gA, gB, None, None, None
+        return dX.reshape(ctx.xshape), gA, gB, None, None, None, None, None
 
 
 class QLoRALinear(torch.nn.Module):
     """nn.Linear replacement: frozen NF4 weight + trainable bf16 adapter."""
 
     def __init__(self, weight_fp32: torch.Tensor, r: int = 16, alpha: float = 32.0,
-                 A: torch.Tensor | None = None, B: torch.Tensor | None = None):
+                 A: torch.Tensor | None = None, B: torch.Tensor | None = None, lora_dropout: float = 0.0):
         super().__init__()
+        self.lora_dropout = float(lora_dropout)
         n_out, k_in = weight_fp32.shape
         self.w = quantize(weight_fp32.contiguous())
         self.r, self.alpha = r, float(alpha)
@@ -290,4 +316,8 @@ class QLoRALinear(torch.nn.Module):
         self.B = torch.nn.Parameter(B.to(torch.bfloat16).contiguous())
 
     def forward(self, X):
-        return QLoRALinearFunction.apply(X, self.A, self.B, self.w, self.r, self.alpha)
+        # a fresh mask per training step (the seed is drawn from torch's host
+        # generator); no dropout in eval mode
+        p = self.lora_dropout if self.training else 0.0
+        seed = int(torch.randint(0, 2**62, (1,)).item()) if p else 0
+        return QLoRALinearFunction.apply(X, self.A, self.B, self.w, self.r, self.alpha, p, seed)

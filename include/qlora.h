@@ -187,6 +187,38 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_
                      float alpha, const uint16_t *U, uint16_t *dX, float *dA, float *dB,
                      void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Forward and backward with LoRA dropout of the adapter input.  The pages'
+ * adapter configurations set lora_dropout = 0.05 ([P1] "A complete run on a
+ * 12 GB-class GPU"; [P5] "Walking through the tooling") without defining
+ * it; this is inverted dropout of the adapter's input x (x is dropped before
+ * A; the frozen path W x sees the undropped x):
+ *   keep(m, k)  element (m, k) of X, flat index e = m k_in + k, is kept iff
+ *               word (e & 3) of Philox4x32-10(counter (lo32(e >> 2),
+ *               hi32(e >> 2), 0, 0), key (lo32(seed), hi32(seed))) is
+ *               >= floor(dropout_p 2^32)  (Salmon et al., SC'11).
+ *   s_d         fp32(alpha / (r (1 - dropout_p)))  (1 / (1 - p) folded in).
+ *   forward     U~ = bf16(s_d (keep * X) A^T);  Y = X W_bf16^T + U~ B^T.
+ *   backward    V~ = bf16(s_d dY B);  dX = dY W_bf16 + keep * (V~ A);
+ *               dA = V~^T (keep * X);  dB = dY^T U~.
+ * The mask depends only on (seed, element position), so the backward
+ * regenerates it: pass the forward's seed.  U may be the forward's U_out
+ * (it already holds the mask) or NULL (recomputed with the mask).  Every
+ * other argument, the workspace size and the error behaviour are those of
+ * qlora_linear_fwd / qlora_linear_bwd; dropout_p outside [0, 1) (or NaN)
+ * returns QLORA_ERR_INVALID_ARG.  dropout_p == 0 gives exactly the results
+ * of qlora_linear_fwd / qlora_linear_bwd.
+ */
+int qlora_linear_fwd_dropout(const qlora_nf4_weight *w, const uint16_t *X, int64_t M,
+                             const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
+                             double dropout_p, uint64_t seed, uint16_t *Y, uint16_t *U_out,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
+int qlora_linear_bwd_dropout(const qlora_nf4_weight *w, const uint16_t *X, const uint16_t *dY,
+                             int64_t M, const uint16_t *A, const uint16_t *B, int32_t r,
+                             float alpha, double dropout_p, uint64_t seed, const uint16_t *U,
+                             uint16_t *dX, float *dA, float *dB, void *ws, size_t ws_bytes,
+                             hipStream_t stream);
+
 /* Workspace bytes needed by qlora_linear_fwd (op = QLORA_OP_FWD) or
  * qlora_linear_bwd (op = QLORA_OP_BWD) for these sizes: enough for any
  * U_out / U argument (U_out == NULL, U == NULL is the worst case).  Returns 0

@@ -151,3 +151,19 @@ def test_merge_and_bf16_quantize_validation(L):
     assert q(FAKE_MIS, 64, 64, FAKE, FAKE, FAKE, None) == ALIGN
     assert q(FAKE, 64, 96, FAKE, FAKE, FAKE, None) == SHAPE
     assert q(FAKE, 0, 64, FAKE, FAKE, FAKE, None) == OK
+
+
+def test_dropout_entry_points_validation(L):
+    w = ctypes.byref(_w())
+    f = L.qlora_linear_fwd_dropout
+    b = L.qlora_linear_bwd_dropout
+    for p in (-0.1, 1.0, 1.5, float("nan")):
+        assert f(w, FAKE, 16, FAKE, FAKE, 8, 2.0, p, 7, FAKE, FAKE, None, 0, 0) == INVALID, p
+        assert b(w, FAKE, FAKE, 16, FAKE, FAKE, 8, 2.0, p, 7, FAKE, FAKE, FAKE, FAKE, None, 0, 0) == INVALID, p
+    assert b"dropout_p" in L.qlora_last_error()
+    # a valid probability leaves the other checks as in the plain entry points
+    assert f(w, FAKE, 16, FAKE, FAKE, 65, 2.0, 0.05, 7, FAKE, FAKE, None, 0, 0) == SHAPE
+    assert f(w, FAKE_MIS, 16, FAKE, FAKE, 8, 2.0, 0.05, 7, FAKE, FAKE, None, 0, 0) == ALIGN
+    assert f(w, FAKE, 16, FAKE, FAKE, 8, 2.0, 0.05, 7, FAKE, None, None, 0, 0) == WORKSPACE
+    assert b(w, FAKE, FAKE, 16, FAKE, FAKE, 8, 2.0, 0.05, 7, None, FAKE, FAKE, FAKE, None, 0, 0) == WORKSPACE
+    assert f(w, None, 0, FAKE, FAKE, 8, 2.0, 0.05, 7, None, None, None, 0, 0) == OK

@@ -11,6 +11,8 @@ rows / groups the oracle computes one by one, plus exact full-tensor checks
 where the oracle is cheap (dA, dB).
 """
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -320,6 +322,119 @@ def test_autograd_module_matches_entry_points():
     check_close(f64(X.grad), dXr, "module dX")
     check_close(f64(mod.A.grad.float()), dAr, "module dA")
     check_close(f64(mod.B.grad.float()), dBr, "module dB")
+
+
+# ------------------------------------------------------------ LoRA dropout ----
+
+DROP_SHAPES = [
+    # (M, N, K, r, alpha, p): GEMM path with ragged tiles, the few-token path,
+    # a rank that is not a multiple of 8, a heavy drop rate
+    (100, 200, 192, 16, 32.0, 0.05),
+    (300, 520, 640, 64, 128.0, 0.05),
+    (5, 1000, 384, 16, 32.0, 0.05),
+    (17, 136, 320, 17, 5.0, 0.3),
+    (257, 384, 512, 8, 16.0, 0.5),
+]
+
+
+def _drop_seed(M, N):
+    return (0x5EED << 40) | (M * 1009 + N)  # exercises both key words
+
+
+@pytest.mark.parametrize("M,N,K,r,alpha,p", DROP_SHAPES)
+def test_dropout_forward_backward_parity(M, N, K, r, alpha, p):
+    _need_gpu()
+    d, q, wb = _case(M, N, K, r, seed=M * 17 + N + K)
+    w = gpu_quantize(d["W"])
+    X, A, B, dY = _dev_inputs(d, r)
+    seed = _drop_seed(M, N)
+    Y, U = qlora.linear_fwd(w, X, A, B, r, alpha, dropout_p=p, seed=seed)
+    dX, dA, dB = qlora.linear_bwd(w, X, dY, A, B, r, alpha, U, dropout_p=p, seed=seed)
+    torch.cuda.synchronize()
+    mask = oracle.dropout_mask(M, K, p, seed)
+    Yr, Ur = oracle.linear_fwd_dropout(wb, d["X"], d["A"], d["B"], alpha, r, mask, p)
+    dXr, dAr, dBr = oracle.linear_bwd_dropout(wb, d["X"], d["dY"], d["A"], d["B"], alpha, r, mask, p)
+    s = oracle.lora_scale(alpha, r)
+    check_close(f64(Y), Yr, "Y")
+    check_close(f64(U), s * Ur, "U~")
+    check_close(f64(dX), dXr, "dX")
+    check_close(f64(dA), dAr, "dA")
+    check_close(f64(dB), dBr, "dB")
+    # the backward regenerates the mask when it recomputes U~
+    dX2, dA2, dB2 = qlora.linear_bwd(w, X, dY, A, B, r, alpha, None, dropout_p=p, seed=seed)
+    torch.cuda.synchronize()
+    assert torch.equal(dX.view(torch.int16), dX2.view(torch.int16))
+    assert torch.equal(dA, dA2) and torch.equal(dB, dB2)
+
+
+def test_dropout_p_zero_equals_plain_entry_points():
+    _need_gpu()
+    M, N, K, r, alpha = 100, 200, 192, 16, 32.0
+    d, q, wb = _case(M, N, K, r, seed=3)
+    w = gpu_quantize(d["W"])
+    X, A, B, dY = _dev_inputs(d, r)
+    Y, U = qlora.linear_fwd(w, X, A, B, r, alpha)
+    g = qlora.linear_bwd(w, X, dY, A, B, r, alpha, U)
+    L = qlora.lib()
+    cw = w._c()
+    Y0 = torch.empty_like(Y)
+    U0 = torch.empty_like(U)
+    ws = qlora.new_workspace(qlora.QLORA_OP_BWD, M, N, K, r, "cuda")
+    st = L.qlora_linear_fwd_dropout(ctypes.byref(cw), X.data_ptr(), M, A.data_ptr(), B.data_ptr(), r, alpha,
+                                    0.0, 99, Y0.data_ptr(), U0.data_ptr(), ws.data_ptr(), ws.numel(),
+                                    qlora._stream())
+    assert st == 0
+    dX0 = torch.empty_like(g[0])
+    dA0 = torch.empty_like(g[1])
+    dB0 = torch.empty_like(g[2])
+    st = L.qlora_linear_bwd_dropout(ctypes.byref(cw), X.data_ptr(), dY.data_ptr(), M, A.data_ptr(),
+                                    B.data_ptr(), r, alpha, 0.0, 99, U0.data_ptr(), dX0.data_ptr(),
+                                    dA0.data_ptr(), dB0.data_ptr(), ws.data_ptr(), ws.numel(), qlora._stream())
+    assert st == 0
+    torch.cuda.synchronize()
+    for a, b in ((Y, Y0), (U, U0), (g[0], dX0)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(g[1], dA0) and torch.equal(g[2], dB0)
+
+
+def test_dropout_mask_bit_exact_in_every_kernel():
+    """The kept / dropped pattern itself, bit for bit, against the oracle's
+    mask.  W = 0 makes dX = keep * (V~ A) exactly (the dX GEMM's mask at
+    every (m, k)); one-hot rows of X (row m has its single 1 at column k_m,
+    all distinct) make U~[m, :] = s_d keep(m, k_m) A[:, k_m] and
+    dA[:, k_m] = keep(m, k_m) V~[m, :] (the rowdot's and the coldot's
+    mask)."""
+    _need_gpu()
+    M, N, K, r, alpha, p = 256, 128, 512, 16, 32.0, 0.3
+    rng = np.random.default_rng(12)
+    seed = 0xABCDEF0123456789
+    W = np.zeros((N, K), dtype=np.float32)
+    w = gpu_quantize(W)
+    km = (np.arange(M) * 7 + 3) % K
+    Xh = np.zeros((M, K), dtype=np.float32)
+    Xh[np.arange(M), km] = 1.0
+    A = rng.standard_normal((r, K)).astype(np.float32)
+    B = rng.standard_normal((N, r)).astype(np.float32)
+    dY = rng.standard_normal((M, N)).astype(np.float32)
+    Xb, Ab, Bb, dYb = (synth.to_bf16_bits(t) for t in (Xh, A, B, dY))
+    X, Ad, Bd, dYd = (dev_bf16(t) for t in (Xb, Ab, Bb, dYb))
+    Y, U = qlora.linear_fwd(w, X, Ad, Bd, r, alpha, dropout_p=p, seed=seed)
+    dX, dA, dB = qlora.linear_bwd(w, X, dYd, Ad, Bd, r, alpha, U, dropout_p=p, seed=seed)
+    torch.cuda.synchronize()
+    mask = oracle.dropout_mask(M, K, p, seed)
+    assert 0.6 < mask.mean() < 0.8
+    Af = oracle.f64_from_bf16_bits(Ab)
+    Vt = f64(dYd) @ oracle.f64_from_bf16_bits(Bb)  # nonzero rows almost surely
+    # dX GEMM: nonzero exactly where kept (V~ A is nonzero everywhere here)
+    assert np.all(np.abs(Vt @ Af) > 0)
+    assert np.array_equal(f64(dX) != 0, mask)
+    # rowdot (U~): row m is zero iff (m, k_m) was dropped
+    row_kept = mask[np.arange(M), km]
+    assert np.array_equal(np.any(f64(U) != 0, axis=1), row_kept)
+    # coldot (dA): column k_m is zero iff (m, k_m) was dropped
+    assert np.array_equal(np.any(f64(dA)[:, km] != 0, axis=0), row_kept)
+    other = np.setdiff1d(np.arange(K), km)
+    assert np.count_nonzero(f64(dA)[:, other]) == 0
 
 
 # ------------------------------------------------- full-size, sampled rows ----
