@@ -25,6 +25,8 @@ Modules:
   re-quantizing the result.
 * :mod:`oracle.dropout` -- LoRA dropout of the adapter input: the
   counter-based mask generator and the dropped forward and backward.
+* :mod:`oracle.formats` -- the storage-format variants the pages compare
+  against (no double quantization; evenly spaced int4 levels).
 
 Every function pinned by a ``-m "not gpu"`` test says which pin covers it.
 The one construction the pages leave fully open -- the tail offset of the
@@ -61,3 +63,4 @@ from .dropout import (  # noqa: F401
     linear_fwd_dropout,
     linear_bwd_dropout,
 )
+from . import formats  # noqa: F401
