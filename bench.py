@@ -276,6 +276,8 @@ def bench_secondary(torch, qlora, synth, dev, evs, reps=10):
         rng = synth.rng_for("70b", idx)
         W = torch.from_numpy(synth.draw(rng, (lin.n_out, lin.k_in), 0.02)).to(dev)
         w0 = qlora.quantize(W)
+        if idx == 0:
+            res["formats_70b_gate"] = bench_formats(torch, qlora, W, reps)
         del W
         copies = [w0] + [qlora.NF4Weight(w0.codes.clone(), w0.absmax_q8.clone(), w0.absmax_scale.clone(),
                                           w0.n_out, w0.k_in) for _ in range(2)]
@@ -353,6 +355,40 @@ def bench_secondary(torch, qlora, synth, dev, evs, reps=10):
         del copies, w0
         torch.cuda.empty_cache()
     return res
+
+
+def bench_formats(torch, qlora, W, reps):
+    """The storage formats the pages weigh NF4-DQ against, on one weight:
+    bits per weight, relative Frobenius error of the decoded bf16 weight, and
+    standalone dequant time (3 rotated copies) and bandwidth."""
+    out = {}
+    n, k = W.shape
+    nw = n * k
+    Wd = W.double()
+    wnorm = float(torch.linalg.vector_norm(Wd))
+    dst = torch.empty((n, k), dtype=torch.bfloat16, device=W.device)
+    for fmt in ("nf4_dq", "nf4", "int4_dq", "int4"):
+        copies = [qlora.quantize_format(W, fmt) for _ in range(3)]
+        qlora.dequant_format(copies[0], dst)
+        torch.cuda.synchronize()
+        err = float(torch.linalg.vector_norm(dst.double() - Wd)) / wnorm
+        packed = copies[0].nbytes()
+        for c in copies:
+            qlora.dequant_format(c, dst)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(3 * reps):
+            qlora.dequant_format(copies[i % 3], dst)
+        b.record()
+        torch.cuda.synchronize()
+        us = 1e3 * a.elapsed_time(b) / (3 * reps)
+        gbs = (packed + 2 * nw) / (us * 1e-6) / 1e9
+        out[fmt] = {"bits_per_weight": round(8 * packed / nw, 4), "rel_error": round(err, 5),
+                    "dequant_us": round(us, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        del copies
+    del Wd, dst
+    return out
 
 
 def bench_cpu(host, r, alpha, m_sample=2048, min_seconds=10.0):

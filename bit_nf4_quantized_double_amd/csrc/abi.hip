@@ -19,6 +19,10 @@ hipError_t launch_quantize_bf16(const uint16_t* W, int64_t nweights, uint8_t* co
                                 hipStream_t st);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* q8, const float* s2, int64_t nweights,
                           uint16_t* out, hipStream_t st);
+hipError_t launch_quantize_fmt(const float* W, int64_t nweights, bool uniform, bool dq, uint8_t* codes,
+                               uint8_t* q8, float* s2, float* absmax, hipStream_t st);
+hipError_t launch_dequant_fmt(const uint8_t* codes, const uint8_t* q8, const float* s2, const float* absmax,
+                              int64_t nweights, bool uniform, bool dq, uint16_t* out, hipStream_t st);
 hipError_t launch_merge(const uint8_t* codes, const uint8_t* q8, const float* s2, int N, int K, const uint16_t* A,
                         const uint16_t* B, int r, float s, uint16_t* out, hipStream_t st);
 hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st);
@@ -130,6 +134,17 @@ BwdLayout bwd_layout(int64_t M, int64_t n_out, int64_t k_in, int32_t r) {
   L.cpart = L.part + round_up(part);
   L.total = L.cpart + round_up((size_t)L.nmc * r * widest * 4);
   return L;
+}
+
+// Storage-format variants: checks shared by quantize and dequant.
+int check_format(int format, int64_t n_out, int64_t k_in, const void* codes, const void* scales,
+                 const void* s2, bool* uniform, bool* dq) {
+  if (format < QLORA_FORMAT_NF4_DQ || format > QLORA_FORMAT_INT4) return fail(QLORA_ERR_INVALID_ARG, "unknown format");
+  *uniform = format == QLORA_FORMAT_INT4_DQ || format == QLORA_FORMAT_INT4;
+  *dq = format == QLORA_FORMAT_NF4_DQ || format == QLORA_FORMAT_INT4_DQ;
+  qlora_nf4_weight w{n_out, k_in, static_cast<const uint8_t*>(codes), static_cast<const uint8_t*>(scales),
+                     *dq ? static_cast<const float*>(s2) : reinterpret_cast<const float*>(scales)};
+  return check_weight(&w);
 }
 
 }  // namespace
@@ -384,6 +399,45 @@ int qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t* X, const
   const int st = dropout_setup(r, alpha, dropout_p, seed, &dm, &s);
   if (st) return st;
   return linear_bwd_impl(w, X, dY, M, A, B, r, alpha, dm, s, U, dX, dA, dB, ws, ws_bytes, stream);
+}
+
+int qlora_format_table(int format, float out[16]) {
+  if (format < QLORA_FORMAT_NF4_DQ || format > QLORA_FORMAT_INT4) return fail(QLORA_ERR_INVALID_ARG, "unknown format");
+  if (!out) return fail(QLORA_ERR_INVALID_ARG, "out is NULL");
+  const bool uniform = format == QLORA_FORMAT_INT4_DQ || format == QLORA_FORMAT_INT4;
+  const qlora::Nf4Consts& c = uniform ? qlora::int4_consts() : qlora::nf4_consts();
+  std::memcpy(out, c.level, sizeof(c.level));
+  return QLORA_OK;
+}
+
+int qlora_quantize_format(int format, const float* W, int64_t n_out, int64_t k_in, uint8_t* codes, void* scales,
+                          float* absmax_scale, hipStream_t stream) {
+  bool uniform = false, dq = false;
+  int st = check_format(format, n_out, k_in, codes, scales, absmax_scale, &uniform, &dq);
+  if (st) return st;
+  if (n_out * k_in == 0) return QLORA_OK;
+  if (!W) return fail(QLORA_ERR_INVALID_ARG, "W is NULL");
+  if (!aligned16(W)) return fail(QLORA_ERR_ALIGN, "W must be 16-byte aligned");
+  hipError_t e = qlora::launch_quantize_fmt(W, n_out * k_in, uniform, dq, codes,
+                                            dq ? static_cast<uint8_t*>(scales) : nullptr,
+                                            dq ? absmax_scale : nullptr,
+                                            dq ? nullptr : static_cast<float*>(scales), stream);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e, "quantize launch");
+}
+
+int qlora_dequant_format(int format, int64_t n_out, int64_t k_in, const uint8_t* codes, const void* scales,
+                         const float* absmax_scale, uint16_t* W_bf16, hipStream_t stream) {
+  bool uniform = false, dq = false;
+  int st = check_format(format, n_out, k_in, codes, scales, absmax_scale, &uniform, &dq);
+  if (st) return st;
+  if (n_out * k_in == 0) return QLORA_OK;
+  if (!W_bf16) return fail(QLORA_ERR_INVALID_ARG, "W_bf16 is NULL");
+  if (!aligned16(W_bf16)) return fail(QLORA_ERR_ALIGN, "W_bf16 must be 16-byte aligned");
+  hipError_t e = qlora::launch_dequant_fmt(codes, dq ? static_cast<const uint8_t*>(scales) : nullptr,
+                                           dq ? absmax_scale : nullptr,
+                                           dq ? nullptr : static_cast<const float*>(scales), n_out * k_in,
+                                           uniform, dq, W_bf16, stream);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e, "dequant launch");
 }
 
 }  // extern "C"

@@ -13,6 +13,13 @@
 //
 // Dequant: a streaming decode, 8 weights (one code dword -> 16 bytes of bf16)
 // per thread per iteration; HBM-bound (2.516 bytes moved per weight).
+//
+// Both kernels also serve the storage-format variants the pages compare NF4
+// with double quantization against ([P1] "The mechanism in brief": one fp32
+// absmax per block costs 4.5 bits per weight; [P2] "Follow-up questions to
+// expect": evenly spaced int4 levels): the level table and its code search
+// are arguments, and without double quantization the fp32 block absmax is
+// stored and read directly.
 #include <algorithm>
 
 #include "common.h"
@@ -38,10 +45,13 @@ __device__ __forceinline__ void widen4(const uint4& v, const uint16_t*, float* w
 // the group is staged through LDS, the thread takes its 64 weights and the absmax,
 // codes each weight with the table-guided search and writes 32 bytes of
 // packed codes; the group max then gives s2 and every thread's q8.
-template <typename T>
+// DQ: block absmaxes double-quantized into q8 codes and one s2 per group;
+// otherwise each block's fp32 absmax is written to `absmax` (q8, s2 unused).
+template <typename T, bool DQ>
 __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ W, uint32_t nb,
                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ q8,
-                                                  float* __restrict__ s2, QuantSearch qs) {
+                                                  float* __restrict__ s2, float* __restrict__ absmax,
+                                                  QuantSearch qs) {
   constexpr int kWords = kBlock * (int)sizeof(T) / 4;  // 32-bit words per block
   constexpr int kChunks = kWords / 4;                  // 16-byte chunks per block
   constexpr int kPitch = kWords + 4;                   // 4 words mod 32 banks between blocks
@@ -147,6 +157,10 @@ __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ W, uint3
     out[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
   }
 
+  if (!DQ) {
+    if (valid) absmax[b] = am;
+    return;
+  }
   // group max -> s2 = max / 255, q8 = round-half-even(absmax / s2)
   float m = am;
 #pragma unroll
@@ -166,9 +180,10 @@ __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ W, uint3
   if (tid == 0) s2[g] = step;
 }
 
+template <bool DQ>
 __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ codes, const uint8_t* __restrict__ q8,
-                                                 const float* __restrict__ s2, uint32_t ndw,
-                                                 uint4* __restrict__ out, Nf4Consts c) {
+                                                 const float* __restrict__ s2, const float* __restrict__ absmax,
+                                                 uint32_t ndw, uint4* __restrict__ out, Nf4Consts c) {
   __shared__ float lv[16];
   if (threadIdx.x < 16) lv[threadIdx.x] = c.level[threadIdx.x];
   __syncthreads();
@@ -179,20 +194,27 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ co
   typedef __attribute__((ext_vector_type(4))) unsigned v4u;
   const uint32_t stride = gridDim.x * blockDim.x;
   for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < ndw; i += stride) {
-    const uint4 o = decode8(codes[i], block_scale(q8, s2, i >> 3), lv);
+    const uint4 o = decode8(codes[i], DQ ? block_scale(q8, s2, i >> 3) : absmax[i >> 3], lv);
     __builtin_nontemporal_store(v4u{o.x, o.y, o.z, o.w}, reinterpret_cast<v4u*>(out + i));
   }
 }
 
 }  // namespace
 
-hipError_t launch_quantize(const float* W, int64_t nweights, uint8_t* codes, uint8_t* q8, float* s2,
-                           hipStream_t st) {
+hipError_t launch_quantize_fmt(const float* W, int64_t nweights, bool uniform, bool dq, uint8_t* codes,
+                               uint8_t* q8, float* s2, float* absmax, hipStream_t st) {
   const uint32_t nb = (uint32_t)(nweights / kBlock);
   const uint32_t ng = (nb + kGroup - 1) / kGroup;
   if (ng == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_quantize<float>, dim3(ng), dim3(256), 0, st, W, nb, codes, q8, s2, quant_search());
+  const QuantSearch& qs = uniform ? quant_search_int4() : quant_search();
+  if (dq) hipLaunchKernelGGL((k_quantize<float, true>), dim3(ng), dim3(256), 0, st, W, nb, codes, q8, s2, absmax, qs);
+  else hipLaunchKernelGGL((k_quantize<float, false>), dim3(ng), dim3(256), 0, st, W, nb, codes, q8, s2, absmax, qs);
   return hipGetLastError();
+}
+
+hipError_t launch_quantize(const float* W, int64_t nweights, uint8_t* codes, uint8_t* q8, float* s2,
+                           hipStream_t st) {
+  return launch_quantize_fmt(W, nweights, false, true, codes, q8, s2, nullptr, st);
 }
 
 hipError_t launch_quantize_bf16(const uint16_t* W, int64_t nweights, uint8_t* codes, uint8_t* q8, float* s2,
@@ -200,18 +222,27 @@ hipError_t launch_quantize_bf16(const uint16_t* W, int64_t nweights, uint8_t* co
   const uint32_t nb = (uint32_t)(nweights / kBlock);
   const uint32_t ng = (nb + kGroup - 1) / kGroup;
   if (ng == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_quantize<uint16_t>, dim3(ng), dim3(256), 0, st, W, nb, codes, q8, s2, quant_search());
+  hipLaunchKernelGGL((k_quantize<uint16_t, true>), dim3(ng), dim3(256), 0, st, W, nb, codes, q8, s2,
+                     (float*)nullptr, quant_search());
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_fmt(const uint8_t* codes, const uint8_t* q8, const float* s2, const float* absmax,
+                              int64_t nweights, bool uniform, bool dq, uint16_t* out, hipStream_t st) {
+  const uint32_t ndw = (uint32_t)(nweights / 8);
+  if (ndw == 0) return hipSuccess;
+  const uint32_t blocks = std::min<uint32_t>((ndw + 255) / 256, 4096u);
+  const uint32_t* cw = reinterpret_cast<const uint32_t*>(codes);
+  uint4* o = reinterpret_cast<uint4*>(out);
+  const Nf4Consts& c = uniform ? int4_consts() : nf4_consts();
+  if (dq) hipLaunchKernelGGL((k_dequant<true>), dim3(blocks), dim3(256), 0, st, cw, q8, s2, absmax, ndw, o, c);
+  else hipLaunchKernelGGL((k_dequant<false>), dim3(blocks), dim3(256), 0, st, cw, q8, s2, absmax, ndw, o, c);
   return hipGetLastError();
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* q8, const float* s2, int64_t nweights,
                           uint16_t* out, hipStream_t st) {
-  const uint32_t ndw = (uint32_t)(nweights / 8);
-  if (ndw == 0) return hipSuccess;
-  const uint32_t blocks = std::min<uint32_t>((ndw + 255) / 256, 4096u);
-  hipLaunchKernelGGL(k_dequant, dim3(blocks), dim3(256), 0, st, reinterpret_cast<const uint32_t*>(codes), q8,
-                     s2, ndw, reinterpret_cast<uint4*>(out), nf4_consts());
-  return hipGetLastError();
+  return launch_dequant_fmt(codes, q8, s2, nullptr, nweights, false, true, out, st);
 }
 
 }  // namespace qlora

@@ -27,7 +27,7 @@ const Nf4Consts& nf4_consts();  // host, built once
 // Table-guided code search for quantization.  With x in [-1, 1] split into
 // 256 cells of width 1/128 (cell i = int(x * 128 + 128), clamped), cand[i] is
 // the number of thresholds below the start of cell i - 1.  No three
-// consecutive cells hold two thresholds (they are >= 0.08 apart), so the
+// consecutive cells hold two thresholds (they are > 3/128 apart), so the
 // code -- the number of thresholds below x -- is cand[i] + (x > thr16[cand[i]])
 // even when rounding of x * 128 + 128 moves x into a neighbouring cell
 // (thr16[15] = +inf).
@@ -37,6 +37,11 @@ struct QuantSearch {
 };
 
 const QuantSearch& quant_search();  // host, built once
+
+// Format variants: 16 evenly spaced levels -1 + 2 i / 15 with the same
+// round-down midpoint thresholds, and their code search (host, built once).
+const Nf4Consts& int4_consts();
+const QuantSearch& quant_search_int4();
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;

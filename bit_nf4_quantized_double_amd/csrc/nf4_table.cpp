@@ -1,4 +1,5 @@
-// Host construction of the NF4 levels and decision thresholds.
+// Host construction of the NF4 levels and decision thresholds (and of the
+// evenly spaced 4-bit levels of the format variants).
 //
 // The levels sit at quantiles of the standard normal distribution ([P1] "The
 // mechanism in brief"; [P4] "NF4 and double quantisation"): 8 positive
@@ -40,6 +41,38 @@ float round_down_f32(double x) {
   return f;
 }
 
+void set_thresholds(Nf4Consts& c) {
+  for (int i = 0; i < 15; ++i) {
+    double mid = ((double)c.level[i] + (double)c.level[i + 1]) * 0.5;  // exact
+    c.thr[i] = round_down_f32(mid);
+  }
+}
+
+// Evenly spaced levels over [-1, 1] ("plain int4", the alternative NF4 is
+// compared with in [P2] "Follow-up questions to expect"): fp32 of
+// -1 + 2 i / 15.
+Nf4Consts build_uniform() {
+  Nf4Consts c;
+  for (int i = 0; i < 16; ++i) c.level[i] = (float)(-1.0 + 2.0 * i / 15.0);
+  set_thresholds(c);
+  return c;
+}
+
+QuantSearch build_search(const Nf4Consts& c) {
+  QuantSearch qs;
+  for (int i = 0; i < 14; ++i)  // the search needs thresholds > 3 cells apart
+    if ((double)c.thr[i + 1] - (double)c.thr[i] <= 3.0 / 128.0) throw std::logic_error("thresholds too close");
+  for (int i = 0; i < 256; ++i) {
+    const double start = i == 0 ? -std::numeric_limits<double>::infinity() : (i - 1) / 128.0 - 1.0;
+    int n = 0;
+    for (int t = 0; t < 15; ++t) n += (double)c.thr[t] < start ? 1 : 0;
+    qs.cand[i] = (uint8_t)n;
+  }
+  for (int t = 0; t < 15; ++t) qs.thr16[t] = c.thr[t];
+  qs.thr16[15] = std::numeric_limits<float>::infinity();
+  return qs;
+}
+
 Nf4Consts build() {
   const double d = 0.5 * ((1.0 - 1.0 / 30.0) + (1.0 - 1.0 / 32.0));
   const double step = d - 0.5;
@@ -51,10 +84,7 @@ Nf4Consts build() {
   for (int j = 1; j <= 8; ++j) lv[7 + j] = normal_quantile(0.5 + step * (j / 8.0)) / top;
   Nf4Consts c;
   for (int i = 0; i < 16; ++i) c.level[i] = (float)lv[i];
-  for (int i = 0; i < 15; ++i) {
-    double mid = ((double)c.level[i] + (double)c.level[i + 1]) * 0.5;  // exact
-    c.thr[i] = round_down_f32(mid);
-  }
+  set_thresholds(c);
   return c;
 }
 
@@ -70,19 +100,21 @@ const Nf4Consts& nf4_consts() {
 const QuantSearch& quant_search() {
   static std::once_flag once;
   static QuantSearch qs;
-  std::call_once(once, [] {
-    const Nf4Consts& c = nf4_consts();
-    for (int i = 0; i < 14; ++i)  // the search needs thresholds > 3 cells apart
-      if ((double)c.thr[i + 1] - (double)c.thr[i] <= 3.0 / 128.0) throw std::logic_error("NF4 thresholds too close");
-    for (int i = 0; i < 256; ++i) {
-      const double start = i == 0 ? -std::numeric_limits<double>::infinity() : (i - 1) / 128.0 - 1.0;
-      int n = 0;
-      for (int t = 0; t < 15; ++t) n += (double)c.thr[t] < start ? 1 : 0;
-      qs.cand[i] = (uint8_t)n;
-    }
-    for (int t = 0; t < 15; ++t) qs.thr16[t] = c.thr[t];
-    qs.thr16[15] = std::numeric_limits<float>::infinity();
-  });
+  std::call_once(once, [] { qs = build_search(nf4_consts()); });
+  return qs;
+}
+
+const Nf4Consts& int4_consts() {
+  static std::once_flag once;
+  static Nf4Consts consts;
+  std::call_once(once, [] { consts = build_uniform(); });
+  return consts;
+}
+
+const QuantSearch& quant_search_int4() {
+  static std::once_flag once;
+  static QuantSearch qs;
+  std::call_once(once, [] { qs = build_search(int4_consts()); });
   return qs;
 }
 

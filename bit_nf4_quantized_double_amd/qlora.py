@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libqlora.so")
 QLORA_OK = 0
 QLORA_OP_FWD = 1
 QLORA_OP_BWD = 2
+FORMATS = {"nf4_dq": 0, "nf4": 1, "int4_dq": 2, "int4": 3}  # QLORA_FORMAT_*
 MAX_RANK = 64
 
 _c_i64 = ctypes.c_int64
@@ -61,6 +62,9 @@ def lib() -> ctypes.CDLL:
         "qlora_linear_bwd_dropout": (ctypes.c_int, [W, _vp, _vp, _c_i64, _vp, _vp, _c_i32, ctypes.c_float,
                                                     ctypes.c_double, ctypes.c_uint64,
                                                     _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+        "qlora_quantize_format": (ctypes.c_int, [ctypes.c_int, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
+        "qlora_dequant_format": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp]),
+        "qlora_format_table": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_float)]),
         "qlora_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i32]),
         "qlora_nf4_table": (None, [ctypes.POINTER(ctypes.c_float)]),
         "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -169,6 +173,57 @@ def quantize(W: torch.Tensor, out: NF4Weight | None = None) -> NF4Weight:
                                          q8.data_ptr(), s2.data_ptr(), _stream())
         _check(st, "qlora_quantize_nf4_dq")
     return out if out is not None else NF4Weight(codes, q8, s2, n_out, k_in)
+
+
+@dataclass
+class FormatWeight:
+    """A weight in one of the storage-format variants (see FORMATS)."""
+    fmt: str
+    codes: torch.Tensor            # uint8 [n_out*k_in/2]
+    scales: torch.Tensor           # uint8 q8 [nb] (*_dq) or float32 absmax [nb]
+    absmax_scale: torch.Tensor | None  # float32 [ng] (*_dq) or None
+    n_out: int
+    k_in: int
+
+    def nbytes(self) -> int:
+        n = self.codes.numel() + self.scales.numel() * self.scales.element_size()
+        return n + (0 if self.absmax_scale is None else 4 * self.absmax_scale.numel())
+
+
+def format_table(fmt: str) -> list:
+    buf = (ctypes.c_float * 16)()
+    _check(lib().qlora_format_table(FORMATS[fmt], buf), "qlora_format_table")
+    return list(buf)
+
+
+def quantize_format(W: torch.Tensor, fmt: str) -> FormatWeight:
+    """fp32 [n_out, k_in] GPU tensor -> FormatWeight in format ``fmt``."""
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [n_out, k_in]")
+    n_out, k_in = W.shape
+    nw = n_out * k_in
+    nb, dev = nw // 64, W.device
+    ng = (nb + 255) // 256
+    dq = fmt.endswith("_dq")
+    codes = _empty_u8(nw // 2, dev)
+    scales = _empty_u8(nb, dev) if dq else torch.empty(max(nb, 4), dtype=torch.float32, device=dev)[:nb]
+    s2 = torch.empty(max(ng, 4), dtype=torch.float32, device=dev)[:ng] if dq else None
+    st = lib().qlora_quantize_format(FORMATS[fmt], _dev(W, torch.float32, "W"), n_out, k_in, codes.data_ptr(),
+                                     scales.data_ptr(), None if s2 is None else s2.data_ptr(), _stream())
+    _check(st, "qlora_quantize_format")
+    return FormatWeight(fmt, codes, scales, s2, n_out, k_in)
+
+
+def dequant_format(w: FormatWeight, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Whole weight of a FormatWeight as bf16 [n_out, k_in]."""
+    if out is None:
+        out = torch.empty((w.n_out, w.k_in), dtype=torch.bfloat16, device=w.codes.device)
+    st = lib().qlora_dequant_format(FORMATS[w.fmt], w.n_out, w.k_in, _dev(w.codes, torch.uint8, "codes"),
+                                    w.scales.data_ptr(),
+                                    None if w.absmax_scale is None else w.absmax_scale.data_ptr(),
+                                    _dev(out, torch.bfloat16, "out"), _stream())
+    _check(st, "qlora_dequant_format")
+    return out
 
 
 def merge(w: NF4Weight, A: torch.Tensor | None, B: torch.Tensor | None, r: int, alpha: float,

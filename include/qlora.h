@@ -74,6 +74,16 @@ enum {
 /* Operation ids for qlora_workspace_bytes. */
 enum { QLORA_OP_FWD = 1, QLORA_OP_BWD = 2 };
 
+/* Storage formats of qlora_quantize_format / qlora_dequant_format.  The
+ * products use QLORA_FORMAT_NF4_DQ (the format above); the others are the
+ * alternatives the pages weigh it against. */
+enum {
+  QLORA_FORMAT_NF4_DQ = 0,   /* NF4 levels, q8 block scales + fp32 step per 256 blocks */
+  QLORA_FORMAT_NF4 = 1,      /* NF4 levels, one fp32 absmax per block (4.5 bits/weight) */
+  QLORA_FORMAT_INT4_DQ = 2,  /* evenly spaced levels -1 + 2i/15, double-quantized scales */
+  QLORA_FORMAT_INT4 = 3      /* evenly spaced levels, fp32 absmax per block */
+};
+
 /* The frozen weight: borrowed device pointers, never written. */
 typedef struct {
   int64_t n_out;              /* rows of W (output features) */
@@ -239,6 +249,35 @@ void qlora_time_next_gemm(hipEvent_t start, hipEvent_t stop);
  * (ascending; 7 negative, an exact 0, 8 positive, extremes -1 and +1: 16
  * levels at normal quantiles, [P1] "The mechanism in brief"). */
 void qlora_nf4_table(float out[16]);
+
+/*
+ * Storage-format variants, for measuring what NF4 and double quantization
+ * buy ([P1] "The mechanism in brief" and [P4] "NF4 and double
+ * quantisation": one fp32 absmax per 64 weights costs 0.5 bit, double
+ * quantization brings the overhead to about 0.127; [P2] "Follow-up
+ * questions to expect": evenly spaced int4 levels waste levels on rare
+ * large values, so NF4's error is lower).  Every format uses blocks of 64,
+ * x = fp32(w / max|w|) by IEEE division, the nearest level with exact ties
+ * to the lower one, and the low nibble for the even element.
+ *   format         QLORA_FORMAT_*; anything else -> QLORA_ERR_INVALID_ARG.
+ *   codes          device uint8 [n_out*k_in/2].
+ *   scales         *_DQ formats: device uint8 q8 [nb], as absmax_q8 above;
+ *                  plain formats: device fp32 absmax [nb] (stored exactly).
+ *   absmax_scale   *_DQ formats: device fp32 [ng] (s2 as above); plain
+ *                  formats: unused, may be NULL.
+ * qlora_quantize_format writes codes, scales (and absmax_scale); decoding
+ * is W_bf16 = bf16(level[c] * a') with a' = fp32(q8 * s2) or the fp32
+ * absmax.  QLORA_FORMAT_NF4_DQ gives exactly the results of
+ * qlora_quantize_nf4_dq / qlora_dequant.  Shapes, alignment and errors as
+ * for those two.  qlora_format_table copies the format's 16 fp32 levels to
+ * host memory out[16] (QLORA_ERR_INVALID_ARG for an unknown format).
+ */
+int qlora_quantize_format(int format, const float *W, int64_t n_out, int64_t k_in,
+                          uint8_t *codes, void *scales, float *absmax_scale, hipStream_t stream);
+int qlora_dequant_format(int format, int64_t n_out, int64_t k_in, const uint8_t *codes,
+                         const void *scales, const float *absmax_scale, uint16_t *W_bf16,
+                         hipStream_t stream);
+int qlora_format_table(int format, float out[16]);
 
 /* Host function: static description of a status code. */
 const char *qlora_status_string(int status);

@@ -167,3 +167,33 @@ def test_dropout_entry_points_validation(L):
     assert f(w, FAKE, 16, FAKE, FAKE, 8, 2.0, 0.05, 7, FAKE, None, None, 0, 0) == WORKSPACE
     assert b(w, FAKE, FAKE, 16, FAKE, FAKE, 8, 2.0, 0.05, 7, None, FAKE, FAKE, FAKE, None, 0, 0) == WORKSPACE
     assert f(w, None, 0, FAKE, FAKE, 8, 2.0, 0.05, 7, None, None, None, 0, 0) == OK
+
+
+def test_format_tables_match_oracle_bitwise(L):
+    from oracle import formats
+    for name, fid in qlora.FORMATS.items():
+        t = np.array(qlora.format_table(name), dtype=np.float32)
+        assert np.array_equal(t.view(np.uint32), formats.format_table(name).view(np.uint32)), name
+    buf = (ctypes.c_float * 16)()
+    assert L.qlora_format_table(4, buf) == INVALID
+    assert L.qlora_format_table(-1, buf) == INVALID
+    assert L.qlora_format_table(0, None) == INVALID
+
+
+def test_format_entry_points_validation(L):
+    q, d = L.qlora_quantize_format, L.qlora_dequant_format
+    for fmt in (4, -1):
+        assert q(fmt, FAKE, 64, 64, FAKE, FAKE, FAKE, 0) == INVALID
+        assert d(fmt, 64, 64, FAKE, FAKE, FAKE, FAKE, 0) == INVALID
+    assert b"format" in L.qlora_last_error()
+    for fmt in range(4):
+        assert q(fmt, FAKE, 64, 96, FAKE, FAKE, FAKE, 0) == SHAPE
+        assert q(fmt, FAKE_MIS, 64, 64, FAKE, FAKE, FAKE, 0) == ALIGN
+        assert q(fmt, FAKE, 64, 64, FAKE, FAKE_MIS, FAKE, 0) == ALIGN
+        assert q(fmt, FAKE, 64, 64, None, FAKE, FAKE, 0) == INVALID
+        assert d(fmt, 64, 64, FAKE, FAKE, FAKE, None, 0) == INVALID
+        assert q(fmt, FAKE, 0, 64, None, None, None, 0) == OK
+    # the step array is needed only with double quantization
+    assert q(0, FAKE, 64, 64, FAKE, FAKE, None, 0) == INVALID
+    assert q(2, FAKE, 64, 64, FAKE, FAKE, None, 0) == INVALID
+    assert d(0, 64, 64, FAKE, FAKE, FAKE_MIS, FAKE, 0) == ALIGN

@@ -164,6 +164,47 @@ def test_quantize_dequant_full_size_sampled_groups(workload, index):
         assert np.array_equal(got, wb.ravel()), g
 
 
+# ------------------------------------------------------- format variants ----
+
+@pytest.mark.parametrize("fmt", ["nf4_dq", "nf4", "int4_dq", "int4"])
+def test_format_variants_bit_exact(fmt):
+    """Every storage-format variant: codes, block scales and the decoded bf16
+    weight bit-exact against the oracle, on the edge-case weight (ties,
+    +-absmax, zeros, -0.0, subnormals, a partial group) and a normal one
+    spanning several groups."""
+    from oracle import formats
+    _need_gpu()
+    rng = np.random.default_rng(31)
+    for W in (_edge_weight(), (rng.standard_normal((136, 1984), dtype=np.float32) * np.float32(0.02))):
+        W = np.ascontiguousarray(W, dtype=np.float32)
+        n, k = W.shape
+        q = formats.quantize_format(W, fmt)
+        _, wb = formats.dequant_format(q, n, k, fmt)
+        w = qlora.quantize_format(torch.from_numpy(W).cuda(), fmt)
+        out = qlora.dequant_format(w)
+        torch.cuda.synchronize()
+        assert np.array_equal(w.codes.cpu().numpy(), q["codes"]), "codes"
+        if fmt.endswith("_dq"):
+            assert np.array_equal(w.scales.cpu().numpy(), q["absmax_q8"]), "q8"
+            assert np.array_equal(w.absmax_scale.cpu().numpy().view(np.uint32),
+                                  q["absmax_scale"].view(np.uint32)), "s2"
+        else:
+            assert np.array_equal(w.scales.cpu().numpy().view(np.uint32), q["absmax"].view(np.uint32)), "absmax"
+        assert np.array_equal(host_bits(out), wb), "dequantized bf16"
+
+
+def test_format_nf4_dq_equals_main_codec():
+    _need_gpu()
+    d = synth.workload_linear("cfg1", 0)
+    Wt = torch.from_numpy(d["W"]).cuda()
+    a = qlora.quantize(Wt)
+    b = qlora.quantize_format(Wt, "nf4_dq")
+    torch.cuda.synchronize()
+    assert torch.equal(a.codes, b.codes) and torch.equal(a.absmax_q8, b.scales)
+    assert torch.equal(a.absmax_scale, b.absmax_scale)
+    assert torch.equal(qlora.dequant(a).view(torch.int16), qlora.dequant_format(b).view(torch.int16))
+
+
 # ------------------------------------------------------- forward/backward ----
 
 SHAPES = [
