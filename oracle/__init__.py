@@ -27,6 +27,8 @@ Modules:
   counter-based mask generator and the dropped forward and backward.
 * :mod:`oracle.formats` -- the storage-format variants the pages compare
   against (no double quantization; evenly spaced int4 levels).
+* :mod:`oracle.f16` -- the fp16 compute-dtype instance (fp16 rounding and
+  the fp16 dequant).
 
 Every function pinned by a ``-m "not gpu"`` test says which pin covers it.
 The one construction the pages leave fully open -- the tail offset of the
@@ -64,3 +66,4 @@ from .dropout import (  # noqa: F401
     linear_bwd_dropout,
 )
 from . import formats  # noqa: F401
+from . import f16  # noqa: F401
