@@ -202,8 +202,8 @@ def main():
     dom = max(per, key=lambda k: per[k]["total_ms"])
     dk = per[dom]
     achieved = dk["avg_flops"] / (dk["avg_us"] * 1e-6) / 1e12
-    kname = {"fwd": "k_gemm_nf4<false> (fused forward GEMM, 256x128 tiles, wave-specialised)",
-             "dx": "k_gemm_nf4<true> (fused dX GEMM, 256x128 tiles, wave-specialised)"}[dom]
+    kname = {"fwd": "k_gemm_nf4<false, Bf16> (fused forward GEMM, 256x128 tiles, wave-specialised)",
+             "dx": "k_gemm_nf4<true, Bf16> (fused dX GEMM, 256x128 tiles, wave-specialised)"}[dom]
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": load_traffic("gemm_" + dom + "_7b"),
@@ -241,6 +241,36 @@ def main():
         secondary["layer_7b_dropout_0.05"] = {
             "ms_per_step": round(ms_d, 4), "TFLOP/s": round(step_flops / (ms_d * 1e-3) / 1e12, 2),
             "slowdown_vs_no_dropout": round(ms_d / ms_per_step, 4)}
+
+        # the same layer step in the fp16 instance (the bf16 inputs converted
+        # exactly to fp16; outputs fp16)
+        h = []
+        for e in lins:
+            f = {k: e[k].to(torch.float16) for k in ("X", "A", "B", "dY")}
+            f["Y"] = torch.empty_like(e["Y"], dtype=torch.float16)
+            f["U"] = torch.empty_like(e["U"], dtype=torch.float16)
+            f["dX"] = torch.empty_like(e["dX"], dtype=torch.float16)
+            h.append(f)
+
+        def step_f16():
+            for e, f in zip(lins, h):
+                qlora.linear_fwd(e["w"], f["X"], f["A"], f["B"], r, alpha, Y=f["Y"], U=f["U"], ws=e["ws_fwd"])
+                qlora.linear_bwd(e["w"], f["X"], f["dY"], f["A"], f["B"], r, alpha, f["U"],
+                                 dX=f["dX"], dA=e["dA"], dB=e["dB"], ws=e["ws"])
+
+        for _ in range(2):
+            step_f16()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(args.steps):
+            step_f16()
+        t1.record()
+        torch.cuda.synchronize()
+        ms_h = t0.elapsed_time(t1) / max(1, args.steps)
+        secondary["layer_7b_fp16"] = {
+            "ms_per_step": round(ms_h, 4), "TFLOP/s": round(step_flops / (ms_h * 1e-3) / 1e12, 2),
+            "frac_fp16_mfma_peak": round(step_flops / (ms_h * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del h
 
     # ---------------------------------------------------- cpu baseline ----
     cpu = None

@@ -18,25 +18,25 @@ hipError_t launch_quantize(const float* W, int64_t nweights, uint8_t* codes, uin
 hipError_t launch_quantize_bf16(const uint16_t* W, int64_t nweights, uint8_t* codes, uint8_t* q8, float* s2,
                                 hipStream_t st);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* q8, const float* s2, int64_t nweights,
-                          uint16_t* out, hipStream_t st);
+                          uint16_t* out, bool f16, hipStream_t st);
 hipError_t launch_quantize_fmt(const float* W, int64_t nweights, bool uniform, bool dq, uint8_t* codes,
                                uint8_t* q8, float* s2, float* absmax, hipStream_t st);
 hipError_t launch_dequant_fmt(const uint8_t* codes, const uint8_t* q8, const float* s2, const float* absmax,
-                              int64_t nweights, bool uniform, bool dq, uint16_t* out, hipStream_t st);
+                              int64_t nweights, bool uniform, bool dq, bool f16, uint16_t* out, hipStream_t st);
 hipError_t launch_merge(const uint8_t* codes, const uint8_t* q8, const float* s2, int N, int K, const uint16_t* A,
                         const uint16_t* B, int r, float s, uint16_t* out, hipStream_t st);
 hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_dx(const GemmArgs& a, hipStream_t st);
 void time_next_gemm(hipEvent_t start, hipEvent_t stop);
 hipError_t launch_lora_down(const uint16_t* X, int M, int K, const uint16_t* A, int r, float s, uint16_t* U,
-                            float* part, DropMask drop, hipStream_t st);
+                            float* part, DropMask drop, bool f16, hipStream_t st);
 size_t rowdot_part_bytes(int64_t M, int64_t Kd, int r);
 int coldot_chunk_rows();
 hipError_t launch_coldot(const uint16_t* v, int r, const uint16_t* in, int M, int C, float* part,
-                         DropMask drop, hipStream_t st);
+                         DropMask drop, bool f16, hipStream_t st);
 hipError_t launch_finalize(const float* part, int nmc, int r, int C, float* out, bool trans, hipStream_t st);
 hipError_t launch_vt_and_db(const uint16_t* dY, int M, int N, const uint16_t* B, const uint16_t* U, int r,
-                            float s, uint16_t* V, float* vpart, float* cpart, float* dB, hipStream_t st);
+                            float s, uint16_t* V, float* vpart, float* cpart, float* dB, bool f16, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_zero_u16(uint16_t* p, int64_t n, hipStream_t st);
 }  // namespace qlora
@@ -216,7 +216,7 @@ int qlora_merge(const qlora_nf4_weight* w, const uint16_t* A, const uint16_t* B,
   hipError_t e;
   if (r == 0) {
     // no adapter: the merged weight is the dequantized weight
-    e = qlora::launch_dequant(w->codes, w->absmax_q8, w->absmax_scale, w->n_out * w->k_in, W_merged, stream);
+    e = qlora::launch_dequant(w->codes, w->absmax_q8, w->absmax_scale, w->n_out * w->k_in, W_merged, false, stream);
   } else {
     e = qlora::launch_merge(w->codes, w->absmax_q8, w->absmax_scale, (int)w->n_out, (int)w->k_in, A, B, r,
                             lora_scale(alpha, r), W_merged, stream);
@@ -224,20 +224,28 @@ int qlora_merge(const qlora_nf4_weight* w, const uint16_t* A, const uint16_t* B,
   return e == hipSuccess ? QLORA_OK : hip_fail(e, "merge launch");
 }
 
-int qlora_dequant(const qlora_nf4_weight* w, uint16_t* W_bf16, hipStream_t stream) {
+static int dequant_impl(const qlora_nf4_weight* w, uint16_t* W16, bool f16, hipStream_t stream) {
   int st = check_weight(w);
   if (st) return st;
   if (w->n_out * w->k_in == 0) return QLORA_OK;
-  if (!W_bf16) return fail(QLORA_ERR_INVALID_ARG, "W_bf16 is NULL");
-  if (!aligned16(W_bf16)) return fail(QLORA_ERR_ALIGN, "W_bf16 must be 16-byte aligned");
-  hipError_t e = qlora::launch_dequant(w->codes, w->absmax_q8, w->absmax_scale, w->n_out * w->k_in, W_bf16,
+  if (!W16) return fail(QLORA_ERR_INVALID_ARG, "output weight is NULL");
+  if (!aligned16(W16)) return fail(QLORA_ERR_ALIGN, "output weight must be 16-byte aligned");
+  hipError_t e = qlora::launch_dequant(w->codes, w->absmax_q8, w->absmax_scale, w->n_out * w->k_in, W16, f16,
                                        stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e, "dequant launch");
 }
 
+int qlora_dequant(const qlora_nf4_weight* w, uint16_t* W_bf16, hipStream_t stream) {
+  return dequant_impl(w, W_bf16, false, stream);
+}
+
+int qlora_dequant_f16(const qlora_nf4_weight* w, uint16_t* W_f16, hipStream_t stream) {
+  return dequant_impl(w, W_f16, true, stream);
+}
+
 static int linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, const uint16_t* A,
                            const uint16_t* B, int32_t r, float alpha, const qlora::DropMask& dm, float s,
-                           uint16_t* Y, uint16_t* U_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+                           uint16_t* Y, uint16_t* U_out, void* ws, size_t ws_bytes, bool f16, hipStream_t stream) {
   int st = check_weight(w);
   if (st) return st;
   if ((st = check_adapter(r, A, B))) return st;
@@ -262,7 +270,7 @@ static int linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t
   }
   hipError_t e;
   if (r > 0 && w->k_in > 0) {
-    e = qlora::launch_lora_down(X, (int)M, (int)w->k_in, A, r, s, U, part, dm, stream);
+    e = qlora::launch_lora_down(X, (int)M, (int)w->k_in, A, r, s, U, part, dm, f16, stream);
     if (e != hipSuccess) return hip_fail(e, "lora_down launch");
   } else if (r > 0) {
     // k_in == 0: X A^T is an empty sum
@@ -276,6 +284,7 @@ static int linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t
     k.U = U; k.B = B; k.Y = Y;
     k.M = (int)M; k.N = (int)w->n_out; k.K = (int)w->k_in; k.r = r;
     k.nf4 = qlora::nf4_consts();
+    k.f16 = f16;
     e = qlora::launch_skinny_fwd(k, stream);
     return e == hipSuccess ? QLORA_OK : hip_fail(e, "few-token forward launch");
   }
@@ -285,6 +294,7 @@ static int linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t
   g.lora_act = U; g.lora_w = B; g.r = r;
   g.out = Y; g.ld_out = w->n_out;
   g.nf4 = qlora::nf4_consts();
+  g.f16 = f16;
   e = qlora::launch_gemm_fwd(g, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e, "forward GEMM launch");
 }
@@ -292,7 +302,7 @@ static int linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t
 static int linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t M,
                            const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
                            const qlora::DropMask& dm, float s, const uint16_t* U, uint16_t* dX, float* dA,
-                           float* dB, void* ws, size_t ws_bytes, hipStream_t stream) {
+                           float* dB, void* ws, size_t ws_bytes, bool f16, hipStream_t stream) {
   int st = check_weight(w);
   if (st) return st;
   if ((st = check_adapter(r, A, B))) return st;
@@ -342,15 +352,15 @@ static int linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const u
       Ut = const_cast<uint16_t*>(U);
     } else {
       Ut = reinterpret_cast<uint16_t*>(base + L.u);
-      if ((e = qlora::launch_lora_down(X, (int)M, (int)K, A, r, s, Ut, part, dm, stream)) != hipSuccess)
+      if ((e = qlora::launch_lora_down(X, (int)M, (int)K, A, r, s, Ut, part, dm, f16, stream)) != hipSuccess)
         return hip_fail(e, "lora_down launch");
     }
     // V~ = bf16(s dY B) and dB = dY^T U~ (stored [N x r]): both read dY
     float* cpart = reinterpret_cast<float*>(base + L.cpart);
-    if ((e = qlora::launch_vt_and_db(dY, (int)M, (int)N, B, Ut, r, s, Vt, part, cpart, dB, stream)) != hipSuccess)
+    if ((e = qlora::launch_vt_and_db(dY, (int)M, (int)N, B, Ut, r, s, Vt, part, cpart, dB, f16, stream)) != hipSuccess)
       return hip_fail(e, "V~ / dB launch");
     // dA = V~^T (mask * X)  ([r x K])
-    if ((e = qlora::launch_coldot(Vt, r, X, (int)M, (int)K, cpart, dm, stream)) != hipSuccess)
+    if ((e = qlora::launch_coldot(Vt, r, X, (int)M, (int)K, cpart, dm, f16, stream)) != hipSuccess)
       return hip_fail(e, "dA partials launch");
     if ((e = qlora::launch_finalize(cpart, L.nmc, r, (int)K, dA, false, stream)) != hipSuccess)
       return hip_fail(e, "dA finalize launch");
@@ -362,6 +372,7 @@ static int linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const u
   g.out = dX; g.ld_out = K;
   g.nf4 = qlora::nf4_consts();
   g.drop = dm;
+  g.f16 = f16;
   e = qlora::launch_gemm_dx(g, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e, "dX GEMM launch");
 }
@@ -370,14 +381,28 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, co
                      const uint16_t* B, int32_t r, float alpha, uint16_t* Y, uint16_t* U_out, void* ws,
                      size_t ws_bytes, hipStream_t stream) {
   return linear_fwd_impl(w, X, M, A, B, r, alpha, qlora::DropMask{}, lora_scale(alpha, r), Y, U_out, ws, ws_bytes,
-                         stream);
+                         false, stream);
+}
+
+int qlora_linear_fwd_f16(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, const uint16_t* A,
+                         const uint16_t* B, int32_t r, float alpha, uint16_t* Y, uint16_t* U_out, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  return linear_fwd_impl(w, X, M, A, B, r, alpha, qlora::DropMask{}, lora_scale(alpha, r), Y, U_out, ws, ws_bytes,
+                         true, stream);
 }
 
 int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t M,
                      const uint16_t* A, const uint16_t* B, int32_t r, float alpha, const uint16_t* U,
                      uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, hipStream_t stream) {
   return linear_bwd_impl(w, X, dY, M, A, B, r, alpha, qlora::DropMask{}, lora_scale(alpha, r), U, dX, dA, dB, ws,
-                         ws_bytes, stream);
+                         ws_bytes, false, stream);
+}
+
+int qlora_linear_bwd_f16(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t M,
+                         const uint16_t* A, const uint16_t* B, int32_t r, float alpha, const uint16_t* U,
+                         uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return linear_bwd_impl(w, X, dY, M, A, B, r, alpha, qlora::DropMask{}, lora_scale(alpha, r), U, dX, dA, dB, ws,
+                         ws_bytes, true, stream);
 }
 
 int qlora_linear_fwd_dropout(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, const uint16_t* A,
@@ -387,7 +412,7 @@ int qlora_linear_fwd_dropout(const qlora_nf4_weight* w, const uint16_t* X, int64
   float s = 0.f;
   const int st = dropout_setup(r, alpha, dropout_p, seed, &dm, &s);
   if (st) return st;
-  return linear_fwd_impl(w, X, M, A, B, r, alpha, dm, s, Y, U_out, ws, ws_bytes, stream);
+  return linear_fwd_impl(w, X, M, A, B, r, alpha, dm, s, Y, U_out, ws, ws_bytes, false, stream);
 }
 
 int qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t M,
@@ -398,7 +423,7 @@ int qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t* X, const
   float s = 0.f;
   const int st = dropout_setup(r, alpha, dropout_p, seed, &dm, &s);
   if (st) return st;
-  return linear_bwd_impl(w, X, dY, M, A, B, r, alpha, dm, s, U, dX, dA, dB, ws, ws_bytes, stream);
+  return linear_bwd_impl(w, X, dY, M, A, B, r, alpha, dm, s, U, dX, dA, dB, ws, ws_bytes, false, stream);
 }
 
 int qlora_format_table(int format, float out[16]) {
@@ -436,7 +461,7 @@ int qlora_dequant_format(int format, int64_t n_out, int64_t k_in, const uint8_t*
   hipError_t e = qlora::launch_dequant_fmt(codes, dq ? static_cast<const uint8_t*>(scales) : nullptr,
                                            dq ? absmax_scale : nullptr,
                                            dq ? nullptr : static_cast<const float*>(scales), n_out * k_in,
-                                           uniform, dq, W_bf16, stream);
+                                           uniform, dq, false, W_bf16, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e, "dequant launch");
 }
 

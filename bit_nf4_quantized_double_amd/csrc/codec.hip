@@ -180,7 +180,7 @@ __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ W, uint3
   if (tid == 0) s2[g] = step;
 }
 
-template <bool DQ>
+template <bool DQ, typename E>
 __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ codes, const uint8_t* __restrict__ q8,
                                                  const float* __restrict__ s2, const float* __restrict__ absmax,
                                                  uint32_t ndw, uint4* __restrict__ out, Nf4Consts c) {
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ co
   typedef __attribute__((ext_vector_type(4))) unsigned v4u;
   const uint32_t stride = gridDim.x * blockDim.x;
   for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < ndw; i += stride) {
-    const uint4 o = decode8(codes[i], DQ ? block_scale(q8, s2, i >> 3) : absmax[i >> 3], lv);
+    const uint4 o = decode8<E>(codes[i], DQ ? block_scale(q8, s2, i >> 3) : absmax[i >> 3], lv);
     __builtin_nontemporal_store(v4u{o.x, o.y, o.z, o.w}, reinterpret_cast<v4u*>(out + i));
   }
 }
@@ -228,21 +228,26 @@ hipError_t launch_quantize_bf16(const uint16_t* W, int64_t nweights, uint8_t* co
 }
 
 hipError_t launch_dequant_fmt(const uint8_t* codes, const uint8_t* q8, const float* s2, const float* absmax,
-                              int64_t nweights, bool uniform, bool dq, uint16_t* out, hipStream_t st) {
+                              int64_t nweights, bool uniform, bool dq, bool f16, uint16_t* out, hipStream_t st) {
   const uint32_t ndw = (uint32_t)(nweights / 8);
   if (ndw == 0) return hipSuccess;
   const uint32_t blocks = std::min<uint32_t>((ndw + 255) / 256, 4096u);
   const uint32_t* cw = reinterpret_cast<const uint32_t*>(codes);
   uint4* o = reinterpret_cast<uint4*>(out);
   const Nf4Consts& c = uniform ? int4_consts() : nf4_consts();
-  if (dq) hipLaunchKernelGGL((k_dequant<true>), dim3(blocks), dim3(256), 0, st, cw, q8, s2, absmax, ndw, o, c);
-  else hipLaunchKernelGGL((k_dequant<false>), dim3(blocks), dim3(256), 0, st, cw, q8, s2, absmax, ndw, o, c);
+  if (f16) {
+    if (dq) hipLaunchKernelGGL((k_dequant<true, F16>), dim3(blocks), dim3(256), 0, st, cw, q8, s2, absmax, ndw, o, c);
+    else hipLaunchKernelGGL((k_dequant<false, F16>), dim3(blocks), dim3(256), 0, st, cw, q8, s2, absmax, ndw, o, c);
+  } else {
+    if (dq) hipLaunchKernelGGL((k_dequant<true, Bf16>), dim3(blocks), dim3(256), 0, st, cw, q8, s2, absmax, ndw, o, c);
+    else hipLaunchKernelGGL((k_dequant<false, Bf16>), dim3(blocks), dim3(256), 0, st, cw, q8, s2, absmax, ndw, o, c);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* q8, const float* s2, int64_t nweights,
-                          uint16_t* out, hipStream_t st) {
-  return launch_dequant_fmt(codes, q8, s2, nullptr, nweights, false, true, out, st);
+                          uint16_t* out, bool f16, hipStream_t st) {
+  return launch_dequant_fmt(codes, q8, s2, nullptr, nweights, false, true, f16, out, st);
 }
 
 }  // namespace qlora

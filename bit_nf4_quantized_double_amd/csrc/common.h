@@ -59,15 +59,55 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 
+// 16-bit element type of a product: the weights are decoded to it, and
+// the activations, adapter operands and outputs are stored in it.  bf16 is
+// the pages' compute dtype ([P1] "A complete run on a 12 GB-class GPU" sets
+// bnb_4bit_compute_dtype=torch.bfloat16); fp16 is the one the same listing
+// names for GPUs without bf16.  Each kernel is instantiated once per type.
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+
+struct Bf16 {
+  typedef bf16x8 v8;
+  // two fp32 -> packed pair, round to nearest even (v_cvt_pk_bf16_f32)
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+  static __device__ __forceinline__ float widen(uint16_t b) { return bf16_to_f32(b); }
+  static __device__ __forceinline__ v8 vec(uint4 u) { return __builtin_bit_cast(v8, u); }
+  static __device__ __forceinline__ f32x16 mfma32(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+struct F16 {
+  typedef f16x8 v8;
+  // two fp32 -> packed pair, round to nearest even (v_cvt_pk_f16_f32)
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+  static __device__ __forceinline__ float widen(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+  static __device__ __forceinline__ v8 vec(uint4 u) { return __builtin_bit_cast(v8, u); }
+  static __device__ __forceinline__ f32x16 mfma32(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
 // Decode 8 packed NF4 codes (one dword, element 0 in the low nibble) with
-// block scale a into 4 dwords of bf16 pairs: w = bf16(level[c] * a).
+// block scale a into 4 dwords of element pairs: w = E(level[c] * a).
 // `lv` is the 16-entry level table in LDS (16 distinct banks: conflict-free).
+template <typename E = Bf16>
 __device__ __forceinline__ uint4 decode8(uint32_t d, float a, const float* lv) {
   uint4 o;
-  o.x = pack_bf16x2(lv[d & 15u] * a, lv[(d >> 4) & 15u] * a);
-  o.y = pack_bf16x2(lv[(d >> 8) & 15u] * a, lv[(d >> 12) & 15u] * a);
-  o.z = pack_bf16x2(lv[(d >> 16) & 15u] * a, lv[(d >> 20) & 15u] * a);
-  o.w = pack_bf16x2(lv[(d >> 24) & 15u] * a, lv[d >> 28] * a);
+  o.x = E::pack2(lv[d & 15u] * a, lv[(d >> 4) & 15u] * a);
+  o.y = E::pack2(lv[(d >> 8) & 15u] * a, lv[(d >> 12) & 15u] * a);
+  o.z = E::pack2(lv[(d >> 16) & 15u] * a, lv[(d >> 20) & 15u] * a);
+  o.w = E::pack2(lv[(d >> 24) & 15u] * a, lv[d >> 28] * a);
   return o;
 }
 

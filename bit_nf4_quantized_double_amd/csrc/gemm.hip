@@ -92,11 +92,11 @@ __device__ __forceinline__ Srcs make_srcs(const GemmArgs& a) {
   return s;
 }
 
-// 8 consecutive bf16 starting at element e of a buffer, of which the first
+// 8 consecutive 16-bit elements starting at element e of a buffer, of which the first
 // `valid` (clamped to 0..8) are real and the rest read as zero; nothing at
 // all when !ok.  vec: e is a multiple of 8 (one 16-byte load); otherwise the
 // elements are loaded one by one (all loads independent).
-__device__ __forceinline__ uint4 load_bf16x8(__amdgpu_buffer_rsrc_t r, uint32_t e, bool ok, int valid,
+__device__ __forceinline__ uint4 load_e16x8(__amdgpu_buffer_rsrc_t r, uint32_t e, bool ok, int valid,
                                              bool vec) {
   if (!ok || valid <= 0) return make_uint4(0, 0, 0, 0);
   if (vec && valid >= 8) return buf_load16(r, 2u * e);
@@ -128,10 +128,10 @@ __device__ __forceinline__ CodeSeg load_codes(const GemmArgs& a, const Srcs& src
   return cs;
 }
 
-template <bool NN>
+template <bool NN, typename E>
 __device__ __forceinline__ void decode_store(uint16_t* s, const CodeSeg& cs, const float th[8],
                                              const LaneMask& lm, int tid) {
-  const Lut L = build_lut<LutPartner::kXor1>(th, (float)cs.q * cs.s2);  // a' = fp32(q8 * s2)
+  const Lut L = build_lut<LutPartner::kXor1, E>(th, (float)cs.q * cs.s2);  // a' = fp32(q8 * s2)
   const uint4 w0 = decode8_lut(L, cs.code.x, lm);
   const uint4 w1 = decode8_lut(L, cs.code.y, lm);
   const uint4 w2 = decode8_lut(L, cs.code.z, lm);
@@ -191,18 +191,16 @@ __device__ __forceinline__ void copy_act(const GemmArgs& a, const Srcs& src, con
 }
 
 // A operand for MFMA sub-step ks, rows 32 i .. 32 i + 31 of the wave's slice.
-__device__ __forceinline__ bf16x8 load_afrag(const uint16_t* st, int i, int ks, int lane) {
+__device__ __forceinline__ uint4 load_afrag(const uint16_t* st, int i, int ks, int lane) {
   const uint32_t r = 32 * i + (lane & 31);
-  const uint4 v = *reinterpret_cast<const uint4*>(st + r * 64u + (((2u * ks + (lane >> 5)) ^ swz(r)) << 3));
-  return __builtin_bit_cast(bf16x8, v);
+  return *reinterpret_cast<const uint4*>(st + r * 64u + (((2u * ks + (lane >> 5)) ^ swz(r)) << 3));
 }
 
 // B operand for MFMA sub-step ks, columns col0..col0+31.
 template <bool NN>
-__device__ __forceinline__ bf16x8 load_bfrag(const uint16_t* s, int col0, int ks, int lane) {
+__device__ __forceinline__ uint4 load_bfrag(const uint16_t* s, int col0, int ks, int lane) {
   if (!NN) {
-    const uint4 v = *reinterpret_cast<const uint4*>(s + kt_off(col0 + (lane & 31), 2 * ks + (lane >> 5)));
-    return __builtin_bit_cast(bf16x8, v);
+    return *reinterpret_cast<const uint4*>(s + kt_off(col0 + (lane & 31), 2 * ks + (lane >> 5)));
   } else {
     // 16-lane group g: lanes 0-31 are half 0 (rows 16 ks .. +7), 32-63 half 1
     // (rows 16 ks + 8 .. +15); odd groups take columns 16..31.  Lane p + 4q addresses row nb + q, columns cb + 4p and
@@ -213,7 +211,7 @@ __device__ __forceinline__ bf16x8 load_bfrag(const uint16_t* s, int col0, int ks
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(s + nn_off(nb, cb)));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(s + nn_off(nb + 4, cb)));
     const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, v);
+    return __builtin_bit_cast(uint4, v);
   }
 }
 
@@ -229,20 +227,20 @@ __device__ __forceinline__ void store_w8(uint16_t* s_next, const uint4& w, int q
   else *reinterpret_cast<uint4*>(s_next + kt_off(tid >> 1, (tid & 1) * 4 + q)) = w;
 }
 
-template <bool NN, bool DECODE>
+template <bool NN, bool DECODE, typename E>
 __device__ __forceinline__ void mma_step(f32x16 (&acc)[2][4], const uint16_t* act, const uint16_t* sw,
                                          uint16_t* s_next, const CodeSeg& cs, const float th[8],
                                          const LaneMask& lm, int tid, int lane) {
-  bf16x8 nb[4], na[2];
+  uint4 nb[4], na[2];
 #pragma unroll
   for (int j = 0; j < 4; ++j) nb[j] = load_bfrag<NN>(sw, 32 * j, 0, lane);
 #pragma unroll
   for (int i = 0; i < 2; ++i) na[i] = load_afrag(act, i, 0, lane);
   Lut L;
-  if (DECODE) L = build_lut<LutPartner::kXor1>(th, (float)cs.q * cs.s2);  // a' = fp32(q8 * s2)
+  if (DECODE) L = build_lut<LutPartner::kXor1, E>(th, (float)cs.q * cs.s2);  // a' = fp32(q8 * s2)
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    bf16x8 bf[4], af[2];
+    uint4 bf[4], af[2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) bf[j] = nb[j];
 #pragma unroll
@@ -261,7 +259,7 @@ __device__ __forceinline__ void mma_step(f32x16 (&acc)[2][4], const uint16_t* ac
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = E::mfma32(E::vec(af[i]), E::vec(bf[j]), acc[i][j]);
     if (DECODE) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -322,7 +320,7 @@ __device__ __forceinline__ void tile_coords(int& tm, int& tn) {
 // Producer pipeline at step s: load codes of step s + 2 (2-slot register
 // ring), copy activations of step s + 2 (3-stage LDS ring), decode codes of
 // step s + 1 into W buffer (s + 1) % 2, then wait for the copies of step s + 1.
-template <bool NN>
+template <bool NN, typename E>
 __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
   // Two distinct LDS objects: the compiler can then tell that the producers'
   // stores of decoded W tiles never alias the activation copies in flight
@@ -382,10 +380,10 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
         const int idx = ptid + u * kThreads;  // 0 .. 1023 chunk slots
         if (!NN) {
           const int col = idx >> 3, jc = idx & 7, n = c0 + col;
-          wv[u] = load_bf16x8(src.lora_w, (uint32_t)n * (uint32_t)a.r + 8u * jc, n < a.C, a.r - 8 * jc, vec);
+          wv[u] = load_e16x8(src.lora_w, (uint32_t)n * (uint32_t)a.r + 8u * jc, n < a.C, a.r - 8 * jc, vec);
         } else {
           const int j = idx >> 4, cc = idx & 15, c = c0 + 8 * cc;
-          wv[u] = load_bf16x8(src.lora_w, (uint32_t)j * (uint32_t)a.K + (uint32_t)c, j < a.r && c < a.C, 8, true);
+          wv[u] = load_e16x8(src.lora_w, (uint32_t)j * (uint32_t)a.K + (uint32_t)c, j < a.r && c < a.C, 8, true);
         }
       }
       // token-side operand: U~ / V~ rows of this producer's consumer slice
@@ -394,7 +392,7 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
       for (int u = 0; u < 8; ++u) {
         const int idx = lane + 64 * u;  // 0 .. 511: row idx >> 3, chunk idx & 7
         const int rr = idx >> 3, jc = idx & 7, m = row0 + rr;
-        av[u] = load_bf16x8(src.lora_act, (uint32_t)m * (uint32_t)a.r + 8u * jc, m < a.M, a.r - 8 * jc, vec);
+        av[u] = load_e16x8(src.lora_act, (uint32_t)m * (uint32_t)a.r + 8u * jc, m < a.M, a.r - 8 * jc, vec);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -418,7 +416,7 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
       const CodeSeg none{};
       const float th0[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       const LaneMask lm0{0, 0, 0};
-      mma_step<NN, false>(acc, sa, sw, sw, none, th0, lm0, 0, lane);
+      mma_step<NN, false, E>(acc, sa, sw, sw, none, th0, lm0, 0, lane);
     }
   };
 
@@ -473,7 +471,7 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
     copy_act(a, src, rows, act_lds(stage_of(0)), kofs(0), lane);
     CodeSeg c1s = load_codes<NN>(a, src, c0, kofs(1), ptid);
     copy_act(a, src, rows, act_lds(stage_of(1)), kofs(1), lane);
-    decode_store<NN>(w_buf0, c0s, th, lm, ptid);
+    decode_store<NN, E>(w_buf0, c0s, th, lm, ptid);
     // copies of step 0 done: younger are the codes (3) and copies (8) of step 1
     wait_vmcnt<11>();
     __syncthreads();
@@ -482,7 +480,7 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
       load_slot = load_codes<NN>(a, src, c0, kofs(step + 2), ptid);
       __builtin_amdgcn_sched_barrier(0);  // keep all code loads ahead of the copies
       copy_act(a, src, rows, act_lds(stage_of(step + 2)), kofs(step + 2), lane);
-      decode_store<NN>(w_next, dec, th, lm, ptid);
+      decode_store<NN, E>(w_next, dec, th, lm, ptid);
       // copies of step s + 1 done: younger are the codes (3) and copies (8)
       // of step s + 2
       wait_vmcnt<11>();
@@ -499,9 +497,9 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
     const float th0[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const LaneMask lm0{0, 0, 0};
     for (int step = 0; step < nst; step += 2) {
-      mma_step<NN, false>(acc, act_ptr(stage_of(step)), w_buf0, w_buf1, none, th0, lm0, 0, lane);
+      mma_step<NN, false, E>(acc, act_ptr(stage_of(step)), w_buf0, w_buf1, none, th0, lm0, 0, lane);
       step_barrier();
-      mma_step<NN, false>(acc, act_ptr(stage_of(step + 1)), w_buf1, w_buf0, none, th0, lm0, 0, lane);
+      mma_step<NN, false, E>(acc, act_ptr(stage_of(step + 1)), w_buf1, w_buf0, none, th0, lm0, 0, lane);
       step_barrier();
     }
   }
@@ -521,7 +519,7 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; v += 2) {
           const int row = row0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const uint32_t pk = pack_bf16x2(acc[i][j][v], acc[i][j][v + 1]);
+          const uint32_t pk = E::pack2(acc[i][j][v], acc[i][j][v + 1]);
           if (row < a.M) a.out[(int64_t)row * a.ld_out + col] = (uint16_t)(pk & 0xFFFFu);
           if (row + 1 < a.M) a.out[(int64_t)(row + 1) * a.ld_out + col] = (uint16_t)(pk >> 16);
         }
@@ -533,7 +531,7 @@ thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
 
 template <bool NN>
 hipError_t launch(const GemmArgs& a, hipStream_t st) {
-  auto kern = k_gemm_nf4<NN>;
+  auto kern = a.f16 ? k_gemm_nf4<NN, F16> : k_gemm_nf4<NN, Bf16>;
   hipError_t e;
   hipEvent_t ev0, ev1;
   take_gemm_events(ev0, ev1);

@@ -23,6 +23,7 @@ struct GemmArgs {
   int64_t ld_out;
   Nf4Consts nf4;
   DropMask drop;             // dX only: dropout of the adapter input (thr 0: none)
+  bool f16;                  // element type of act, lora_*, out and the decoded W: fp16 (else bf16)
 };
 
 }  // namespace qlora

@@ -7,7 +7,8 @@
 //   finalize: out = sum over chunks, in a fixed order (deterministic)
 //             dA = V~^T X  [r x K]      dB = dY^T U~  -> stored [N x r]
 //
-// All use v_mfma_f32_16x16x32_bf16 with the rank on the 16-wide side.
+// All use v_mfma_f32_16x16x32 on 16-bit elements (bf16, or fp16 for the fp16
+// instance) with the rank on the 16-wide side.
 #include <algorithm>
 
 #include "common.h"
@@ -38,7 +39,6 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) short i16x8;
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ---------------------------------------------------------------- rowdot ----
 // out[m][j] = bf16(scale * sum_k in[m][k] * w(j, k)), j < r.
@@ -77,7 +77,7 @@ struct RowdotArgs {
 };
 
 // Workgroup (bx, by) = (64-row block, K split) of the rowdot grid.
-template <bool CONTIG, int RT>
+template <bool CONTIG, int RT, typename E>
 __device__ __forceinline__ void rowdot_body(const RowdotArgs& ra, int bx, int by, uint16_t* sw) {
   using Ly = RowdotLds<CONTIG, RT>;
   const uint16_t* __restrict__ in = ra.in;
@@ -140,13 +140,13 @@ __device__ __forceinline__ void rowdot_body(const RowdotArgs& ra, int bx, int by
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, av[u]);
+      const typename E::v8 a = E::vec(av[u]);
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
-        bf16x8 b;
+        typename E::v8 b;
         if (CONTIG) {
           const uint4 v = *reinterpret_cast<const uint4*>(sw + (16 * t + row) * Ly::kPitch + 32 * u + 8 * kg);
-          b = __builtin_bit_cast(bf16x8, v);
+          b = E::vec(v);
         } else {
           // lane p + 4q of k-group kg addresses row kb + q, columns 4p..4p+3
           // and receives column (lane & 15), rows kb .. kb + 3
@@ -157,9 +157,9 @@ __device__ __forceinline__ void rowdot_body(const RowdotArgs& ra, int bx, int by
           const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_i16x4*)(sw + (kb + 4) * Ly::kPitch + 16 * t + 4 * p));
           const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          b = __builtin_bit_cast(bf16x8, v);
+          b = E::vec(__builtin_bit_cast(uint4, v));
         }
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[t], 0, 0, 0);
+        acc[t] = E::mfma16(a, b, acc[t]);
       }
     }
   }
@@ -174,7 +174,7 @@ __device__ __forceinline__ void rowdot_body(const RowdotArgs& ra, int bx, int by
         if (part) {
           part[((int64_t)split * M + m) * r + j] = acc[t][v];
         } else {
-          const uint32_t pk = pack_bf16x2(scale * acc[t][v], 0.f);
+          const uint32_t pk = E::pack2(scale * acc[t][v], 0.f);
           out[(int64_t)m * r + j] = (uint16_t)(pk & 0xFFFFu);
         }
       }
@@ -182,13 +182,14 @@ __device__ __forceinline__ void rowdot_body(const RowdotArgs& ra, int bx, int by
   }
 }
 
-template <bool CONTIG, int RT>
+template <bool CONTIG, int RT, typename E>
 __global__ __launch_bounds__(256) void k_rowdot(RowdotArgs ra) {
   __shared__ __attribute__((aligned(16))) uint16_t sw[RowdotLds<CONTIG, RT>::kElems];
-  rowdot_body<CONTIG, RT>(ra, blockIdx.x, blockIdx.y, sw);
+  rowdot_body<CONTIG, RT, E>(ra, blockIdx.x, blockIdx.y, sw);
 }
 
 // out[m][j] = bf16(scale * sum_{split} part[split][m][j]), fixed order.
+template <typename E>
 __device__ __forceinline__ void rowdot_finalize_body(const float* __restrict__ part, int nsplit, int64_t n,
                                                      float scale, uint16_t* __restrict__ out, int b, int nb) {
   for (int64_t i = (int64_t)b * 256 + threadIdx.x; i < n; i += (int64_t)nb * 256) {
@@ -202,14 +203,15 @@ __device__ __forceinline__ void rowdot_finalize_body(const float* __restrict__ p
       for (int j = 0; j < 8; ++j) s += v[j];
     }
     for (; k < nsplit; ++k) s += part[(int64_t)k * n + i];
-    const uint32_t pk = pack_bf16x2(scale * s, 0.f);
+    const uint32_t pk = E::pack2(scale * s, 0.f);
     out[i] = (uint16_t)(pk & 0xFFFFu);
   }
 }
 
+template <typename E>
 __global__ __launch_bounds__(256) void k_rowdot_finalize(const float* __restrict__ part, int nsplit, int64_t n,
                                                          float scale, uint16_t* __restrict__ out) {
-  rowdot_finalize_body(part, nsplit, n, scale, out, blockIdx.x, gridDim.x);
+  rowdot_finalize_body<E>(part, nsplit, n, scale, out, blockIdx.x, gridDim.x);
 }
 
 // ---------------------------------------------------------------- coldot ----
@@ -227,7 +229,7 @@ struct ColdotArgs {
 };
 
 // Workgroup (bx, by) = (128-column tile, row chunk) of the coldot grid.
-template <int RT>
+template <int RT, typename E>
 __device__ __forceinline__ void coldot_body(const ColdotArgs& ca, int bx, int by, f32x4 (*red)[8][64]) {
   const uint16_t* __restrict__ v = ca.v;
   const uint16_t* __restrict__ in = ca.in;
@@ -257,7 +259,7 @@ __device__ __forceinline__ void coldot_body(const ColdotArgs& ca, int bx, int by
       for (int i = 0; i < 8; ++i)
         rows[i] = drop8(rows[i], (uint64_t)(m0 + 8 * g + i) * (uint64_t)C + (uint64_t)(c0 + 8 * q), ca.drop);
     }
-    bf16x8 colv[8];
+    uint4 colv[8];
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
       const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
@@ -268,7 +270,7 @@ __device__ __forceinline__ void coldot_body(const ColdotArgs& ca, int bx, int by
         const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&rows[2 * mm + 1]);
         d[mm] = __builtin_amdgcn_perm(r1[jj >> 1], r0[jj >> 1], sel);
       }
-      colv[jj] = as_bf16x8(make_uint4(d[0], d[1], d[2], d[3]));
+      colv[jj] = make_uint4(d[0], d[1], d[2], d[3]);
     }
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
@@ -283,7 +285,7 @@ __device__ __forceinline__ void coldot_body(const ColdotArgs& ca, int bx, int by
                             e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16));
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj)
-        acc[t][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), colv[jj], acc[t][jj], 0, 0, 0);
+        acc[t][jj] = E::mfma16(E::vec(av), E::vec(colv[jj]), acc[t][jj]);
     }
   }
   // D[j][col]: j = 16t + 4*(lane>>4) + v, column index lane&15 -> c0 + 8*(lane&15) + jj
@@ -308,10 +310,10 @@ __device__ __forceinline__ void coldot_body(const ColdotArgs& ca, int bx, int by
   }
 }
 
-template <int RT>
+template <int RT, typename E>
 __global__ __launch_bounds__(256) void k_coldot(ColdotArgs ca) {
   __shared__ f32x4 red[4][8][64];
-  coldot_body<RT>(ca, blockIdx.x, blockIdx.y, red);
+  coldot_body<RT, E>(ca, blockIdx.x, blockIdx.y, red);
 }
 
 // out[j][c] (or out[c][j] when TRANS) = sum_{mc} part[mc][j][c], fixed order.
@@ -344,24 +346,25 @@ __global__ __launch_bounds__(256) void k_finalize(const float* __restrict__ part
 // ---- merged launches of the backward (independent work, one dispatch) ----
 // Blocks [0, nr) run the V~ rowdot grid (nr = row blocks x splits), blocks
 // [nr, nr + nc) the dB coldot grid: both read dY, neither needs the other.
-template <int RT>
+template <int RT, typename E>
 __global__ __launch_bounds__(256) void k_vt_and_db(RowdotArgs ra, int rb, ColdotArgs ca, int ctiles) {
   __shared__ __attribute__((aligned(16))) uint16_t sw[RowdotLds<false, RT>::kElems];
   __shared__ f32x4 red[4][8][64];
   const int nr = rb * ra.nsplit;
   const int b = blockIdx.x;
-  if (b < nr) rowdot_body<false, RT>(ra, b % rb, b / rb, sw);
-  else coldot_body<RT>(ca, (b - nr) % ctiles, (b - nr) / ctiles, red);
+  if (b < nr) rowdot_body<false, RT, E>(ra, b % rb, b / rb, sw);
+  else coldot_body<RT, E>(ca, (b - nr) % ctiles, (b - nr) / ctiles, red);
 }
 
 // Blocks [0, n1) finalize V~ (when it was split), blocks [n1, n1 + n2)
 // finalize dB (stored [N x r]).
+template <typename E>
 __global__ __launch_bounds__(256) void k_fin_vt_and_db(const float* __restrict__ vpart, int nsplit, int64_t nv,
                                                        float scale, uint16_t* __restrict__ vout, int n1,
                                                        const float* __restrict__ cpart, int nmc, int r, int C,
                                                        float* __restrict__ dB, int n2) {
   const int b = blockIdx.x;
-  if (b < n1) rowdot_finalize_body(vpart, nsplit, nv, scale, vout, b, n1);
+  if (b < n1) rowdot_finalize_body<E>(vpart, nsplit, nv, scale, vout, b, n1);
   else finalize_body<true>(cpart, nmc, r, C, dB, b - n1, n2);
 }
 
@@ -373,14 +376,14 @@ __global__ __launch_bounds__(256) void k_zero_u16(uint16_t* __restrict__ p, int6
   for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
 }
 
-template <bool CONTIG, int RT>
+template <bool CONTIG, int RT, typename E>
 void rowdot_launch(dim3 grid, hipStream_t st, const uint16_t* in, int M, int Kd, const uint16_t* wt, int r,
                    int kchunk, float scale, uint16_t* out, float* part, DropMask drop) {
   const RowdotArgs ra{in, M, Kd, wt, r, kchunk, (int)grid.y, scale, out, part, drop};
-  hipLaunchKernelGGL((k_rowdot<CONTIG, RT>), grid, dim3(256), 0, st, ra);
+  hipLaunchKernelGGL((k_rowdot<CONTIG, RT, E>), grid, dim3(256), 0, st, ra);
 }
 
-template <bool CONTIG>
+template <bool CONTIG, typename E>
 hipError_t rowdot_dispatch(const uint16_t* in, int M, int Kd, const uint16_t* wt, int r, float scale,
                            uint16_t* out, float* part, DropMask drop, hipStream_t st) {
   int nsplit, kchunk;
@@ -388,43 +391,63 @@ hipError_t rowdot_dispatch(const uint16_t* in, int M, int Kd, const uint16_t* wt
   dim3 grid((M + 63) / 64, nsplit);
   float* p = nsplit > 1 ? part : nullptr;
   switch ((r + 15) / 16) {
-    case 1: rowdot_launch<CONTIG, 1>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
-    case 2: rowdot_launch<CONTIG, 2>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
-    case 3: rowdot_launch<CONTIG, 3>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
-    default: rowdot_launch<CONTIG, 4>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
+    case 1: rowdot_launch<CONTIG, 1, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
+    case 2: rowdot_launch<CONTIG, 2, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
+    case 3: rowdot_launch<CONTIG, 3, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
+    default: rowdot_launch<CONTIG, 4, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
   const int64_t n = (int64_t)M * r;
   const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 2048));
-  hipLaunchKernelGGL(k_rowdot_finalize, dim3(blocks), dim3(256), 0, st, part, nsplit, n, scale, out);
+  hipLaunchKernelGGL(k_rowdot_finalize<E>, dim3(blocks), dim3(256), 0, st, part, nsplit, n, scale, out);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// U~ = bf16(s (mask * X) A^T): in = X [M x K], A [r x K]
+// U~ = E(s (mask * X) A^T): in = X [M x K], A [r x K]; E = fp16 when f16, else bf16
 hipError_t launch_lora_down(const uint16_t* X, int M, int K, const uint16_t* A, int r, float s, uint16_t* U,
-                            float* part, DropMask drop, hipStream_t st) {
-  return rowdot_dispatch<true>(X, M, K, A, r, s, U, part, drop, st);
+                            float* part, DropMask drop, bool f16, hipStream_t st) {
+  return f16 ? rowdot_dispatch<true, F16>(X, M, K, A, r, s, U, part, drop, st)
+             : rowdot_dispatch<true, Bf16>(X, M, K, A, r, s, U, part, drop, st);
 }
-
 
 int coldot_chunk_rows() { return 256; }
 
+namespace {
+
+template <typename E>
+void coldot_launch(dim3 grid, const ColdotArgs& ca, int rt, hipStream_t st) {
+  switch (rt) {
+    case 1: hipLaunchKernelGGL((k_coldot<1, E>), grid, dim3(256), 0, st, ca); break;
+    case 2: hipLaunchKernelGGL((k_coldot<2, E>), grid, dim3(256), 0, st, ca); break;
+    case 3: hipLaunchKernelGGL((k_coldot<3, E>), grid, dim3(256), 0, st, ca); break;
+    default: hipLaunchKernelGGL((k_coldot<4, E>), grid, dim3(256), 0, st, ca); break;
+  }
+}
+
+template <typename E>
+void vt_and_db_launch(dim3 grid, const RowdotArgs& ra, int rb, const ColdotArgs& ca, int ctiles, int rt,
+                      hipStream_t st) {
+  switch (rt) {
+    case 1: hipLaunchKernelGGL((k_vt_and_db<1, E>), grid, dim3(256), 0, st, ra, rb, ca, ctiles); break;
+    case 2: hipLaunchKernelGGL((k_vt_and_db<2, E>), grid, dim3(256), 0, st, ra, rb, ca, ctiles); break;
+    case 3: hipLaunchKernelGGL((k_vt_and_db<3, E>), grid, dim3(256), 0, st, ra, rb, ca, ctiles); break;
+    default: hipLaunchKernelGGL((k_vt_and_db<4, E>), grid, dim3(256), 0, st, ra, rb, ca, ctiles); break;
+  }
+}
+
+}  // namespace
+
 // part[mc][j][c] = sum over the mc-th chunk of rows of v[m][j] * (mask * in)[m][c]
 hipError_t launch_coldot(const uint16_t* v, int r, const uint16_t* in, int M, int C, float* part, DropMask drop,
-                         hipStream_t st) {
+                         bool f16, hipStream_t st) {
   const int mchunk = coldot_chunk_rows();
   dim3 grid((C + 127) / 128, (M + mchunk - 1) / mchunk);
-  const int rt = (r + 15) / 16;
   const ColdotArgs ca{v, r, in, M, C, mchunk, part, drop};
-  switch (rt) {
-    case 1: hipLaunchKernelGGL((k_coldot<1>), grid, dim3(256), 0, st, ca); break;
-    case 2: hipLaunchKernelGGL((k_coldot<2>), grid, dim3(256), 0, st, ca); break;
-    case 3: hipLaunchKernelGGL((k_coldot<3>), grid, dim3(256), 0, st, ca); break;
-    default: hipLaunchKernelGGL((k_coldot<4>), grid, dim3(256), 0, st, ca); break;
-  }
+  if (f16) coldot_launch<F16>(grid, ca, (r + 15) / 16, st);
+  else coldot_launch<Bf16>(grid, ca, (r + 15) / 16, st);
   return hipGetLastError();
 }
 
@@ -432,7 +455,7 @@ hipError_t launch_coldot(const uint16_t* v, int r, const uint16_t* in, int M, in
 //   1. V~ split partials (or V~ itself when unsplit) and dB row-chunk partials;
 //   2. V~ finalize (when split) and dB finalize.
 hipError_t launch_vt_and_db(const uint16_t* dY, int M, int N, const uint16_t* B, const uint16_t* U, int r,
-                            float s, uint16_t* V, float* vpart, float* cpart, float* dB, hipStream_t st) {
+                            float s, uint16_t* V, float* vpart, float* cpart, float* dB, bool f16, hipStream_t st) {
   int nsplit, kchunk;
   rowdot_split(M, N, &nsplit, &kchunk);
   const int rb = (M + 63) / 64;
@@ -441,20 +464,20 @@ hipError_t launch_vt_and_db(const uint16_t* dY, int M, int N, const uint16_t* B,
   const int ctiles = (N + 127) / 128, nmc = (M + mchunk - 1) / mchunk;
   const ColdotArgs ca{U, r, dY, M, N, mchunk, cpart, DropMask{}};
   const dim3 grid(rb * nsplit + ctiles * nmc);
-  switch ((r + 15) / 16) {
-    case 1: hipLaunchKernelGGL((k_vt_and_db<1>), grid, dim3(256), 0, st, ra, rb, ca, ctiles); break;
-    case 2: hipLaunchKernelGGL((k_vt_and_db<2>), grid, dim3(256), 0, st, ra, rb, ca, ctiles); break;
-    case 3: hipLaunchKernelGGL((k_vt_and_db<3>), grid, dim3(256), 0, st, ra, rb, ca, ctiles); break;
-    default: hipLaunchKernelGGL((k_vt_and_db<4>), grid, dim3(256), 0, st, ra, rb, ca, ctiles); break;
-  }
+  if (f16) vt_and_db_launch<F16>(grid, ra, rb, ca, ctiles, (r + 15) / 16, st);
+  else vt_and_db_launch<Bf16>(grid, ra, rb, ca, ctiles, (r + 15) / 16, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nv = (int64_t)M * r;
   const int n1 = nsplit > 1 ? (int)std::max<int64_t>(1, std::min<int64_t>((nv + 255) / 256, 2048)) : 0;
   const int64_t nc = (int64_t)r * N;
   const int n2 = (int)std::max<int64_t>(1, std::min<int64_t>((nc + 255) / 256, 4096));
-  hipLaunchKernelGGL(k_fin_vt_and_db, dim3(n1 + n2), dim3(256), 0, st, vpart, nsplit, nv, s, V, n1, cpart, nmc, r,
-                     N, dB, n2);
+  if (f16)
+    hipLaunchKernelGGL(k_fin_vt_and_db<F16>, dim3(n1 + n2), dim3(256), 0, st, vpart, nsplit, nv, s, V, n1, cpart,
+                       nmc, r, N, dB, n2);
+  else
+    hipLaunchKernelGGL(k_fin_vt_and_db<Bf16>, dim3(n1 + n2), dim3(256), 0, st, vpart, nsplit, nv, s, V, n1, cpart,
+                       nmc, r, N, dB, n2);
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
-// Register lookup-table decode of packed NF4 codes to bf16, shared by the
-// fused GEMM and the few-token forward kernel.
+// Register lookup-table decode of packed NF4 codes to 16-bit floats (bf16 or
+// fp16; only the table entries are rounded), shared by the fused GEMM and the
+// few-token forward kernel.
 //
 // A 64-weight block has one scale a' = fp32(q8 * s2); its 16 possible
 // decoded values bf16(level[c] * a') ([P1] "The mechanism in brief") form a
@@ -33,13 +34,14 @@ enum class LutPartner {
   kRows16,
 };
 
-// th[] = the 8 levels this lane owns; a = the block scale.
-template <LutPartner P>
+// th[] = the 8 levels this lane owns; a = the block scale; E = the 16-bit
+// element type the entries are rounded to (round to nearest even).
+template <LutPartner P, typename E = Bf16>
 __device__ __forceinline__ Lut build_lut(const float th[8], float a) {
-  const uint32_t p0 = pack_bf16x2(th[0] * a, th[1] * a);
-  const uint32_t p1 = pack_bf16x2(th[2] * a, th[3] * a);
-  const uint32_t p2 = pack_bf16x2(th[4] * a, th[5] * a);
-  const uint32_t p3 = pack_bf16x2(th[6] * a, th[7] * a);
+  const uint32_t p0 = E::pack2(th[0] * a, th[1] * a);
+  const uint32_t p1 = E::pack2(th[2] * a, th[3] * a);
+  const uint32_t p2 = E::pack2(th[4] * a, th[5] * a);
+  const uint32_t p3 = E::pack2(th[6] * a, th[7] * a);
   const uint32_t lo0 = __builtin_amdgcn_perm(p1, p0, 0x06040200u);
   const uint32_t hi0 = __builtin_amdgcn_perm(p1, p0, 0x07050301u);
   const uint32_t lo1 = __builtin_amdgcn_perm(p3, p2, 0x06040200u);

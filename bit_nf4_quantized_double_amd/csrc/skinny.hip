@@ -8,7 +8,7 @@
 // (0.516 B per weight), and decoding it is the only real arithmetic.  Every
 // weight is decoded exactly once, from its codes straight into MFMA operand
 // registers -- no LDS tile, no barrier in the main loop.  The product uses
-// v_mfma_f32_16x16x32_bf16 with 16 W rows on one side and the (zero-padded)
+// v_mfma_f32_16x16x32_bf16 (or _f16) with 16 W rows on one side and the (zero-padded)
 // 16 tokens on the other.
 //
 // Workgroup: 8 waves (two per SIMD, so up to 256 VGPRs per lane for deep
@@ -53,7 +53,7 @@ struct SkSrcs {
 // SL: the workgroup's block scales (absmax codes of its rows, and the
 // second-level scales they use) are staged in LDS once, with coalesced loads,
 // instead of two scattered small loads per 32 weights.
-template <int TPW, int RD, bool SL>
+template <int TPW, int RD, bool SL, typename E>
 __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
   extern __shared__ __attribute__((aligned(16))) float4 s_dyn[];
   float4* const s_red = s_dyn;  // [tiles][nwk][64], used after the main loop
@@ -176,21 +176,17 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
     for (int t = 0; t < TPW; ++t) {
       const SkSeg cs = rg[t];
       const float scale = SL ? sc[t] : (float)cs.q * cs.s2;  // a' = fp32(q8 * s2)
-      const Lut L = build_lut<LutPartner::kRows16>(th, scale);
+      const Lut L = build_lut<LutPartner::kRows16, E>(th, scale);
       const uint4 w0 = decode8_lut_eo(L, cs.code.x, kc);
       const uint4 w1 = decode8_lut_eo(L, cs.code.y, kc);
       const uint4 w2 = decode8_lut_eo(L, cs.code.z, kc);
       const uint4 w3 = decode8_lut_eo(L, cs.code.w, kc);
       rg[t] = load(t, i + RD);  // the same tile, RD chunks ahead
       __builtin_amdgcn_sched_barrier(0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w0),
-                                                      __builtin_bit_cast(bf16x8, xc[0]), acc[t], 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w1),
-                                                      __builtin_bit_cast(bf16x8, xc[1]), acc[t], 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w2),
-                                                      __builtin_bit_cast(bf16x8, xc[2]), acc[t], 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w3),
-                                                      __builtin_bit_cast(bf16x8, xc[3]), acc[t], 0, 0, 0);
+      acc[t] = E::mfma16(E::vec(w0), E::vec(xc[0]), acc[t]);
+      acc[t] = E::mfma16(E::vec(w1), E::vec(xc[1]), acc[t]);
+      acc[t] = E::mfma16(E::vec(w2), E::vec(xc[2]), acc[t]);
+      acc[t] = E::mfma16(E::vec(w3), E::vec(xc[3]), acc[t]);
     }
   };
   // unrolled by U = max(RD, 2): static ring slot (u % RD) and X buffer (u % 2)
@@ -238,8 +234,7 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
                             v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
           }
         }
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bf),
-                                                        __builtin_bit_cast(bf16x8, uf), acc[t], 0, 0, 0);
+        acc[t] = E::mfma16(E::vec(bf), E::vec(uf), acc[t]);
       }
     }
   }
@@ -265,8 +260,8 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
     const int n = (blockIdx.x * a.tiles + tt) * 16 + 4 * (l >> 4);
     if (m < a.M && n < a.N) {  // n_out % 8 == 0: the 4 rows are all in range
       uint2 o;
-      o.x = pack_bf16x2(s.x, s.y);
-      o.y = pack_bf16x2(s.z, s.w);
+      o.x = E::pack2(s.x, s.y);
+      o.y = E::pack2(s.z, s.w);
       *reinterpret_cast<uint2*>(a.Y + (int64_t)m * a.N + n) = o;
     }
   }
@@ -278,8 +273,13 @@ hipError_t sk_launch(const SkinnyArgs& a, int grid, size_t lds, bool sl, hipStre
   take_gemm_events(ev0, ev1);
   hipError_t e;
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
-  if (sl) hipLaunchKernelGGL((k_skinny_fwd<TPW, RD, true>), dim3(grid), dim3(kSkThreads), lds, st, a);
-  else hipLaunchKernelGGL((k_skinny_fwd<TPW, RD, false>), dim3(grid), dim3(kSkThreads), lds, st, a);
+  if (a.f16) {
+    if (sl) hipLaunchKernelGGL((k_skinny_fwd<TPW, RD, true, F16>), dim3(grid), dim3(kSkThreads), lds, st, a);
+    else hipLaunchKernelGGL((k_skinny_fwd<TPW, RD, false, F16>), dim3(grid), dim3(kSkThreads), lds, st, a);
+  } else {
+    if (sl) hipLaunchKernelGGL((k_skinny_fwd<TPW, RD, true, Bf16>), dim3(grid), dim3(kSkThreads), lds, st, a);
+    else hipLaunchKernelGGL((k_skinny_fwd<TPW, RD, false, Bf16>), dim3(grid), dim3(kSkThreads), lds, st, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
   return hipSuccess;

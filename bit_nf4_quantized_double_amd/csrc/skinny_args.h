@@ -6,7 +6,7 @@
 namespace qlora {
 
 struct SkinnyArgs {
-  const uint16_t* X;  // [M x K] bf16 tokens
+  const uint16_t* X;  // [M x K] tokens (16-bit elements, see f16)
   const uint8_t* codes;
   const uint8_t* q8;
   const float* s2;
@@ -18,6 +18,7 @@ struct SkinnyArgs {
   int nwk_log2;       // log2 of the waves sharing one tile group; set by the launcher
   int nci;            // chunk iterations per wave; set by the launcher
   Nf4Consts nf4;
+  bool f16;           // X, U, B, Y and the decoded W are fp16 (else bf16)
 };
 
 int skinny_max_tokens();

@@ -27,8 +27,10 @@ CSRC = os.path.join(HERE, "csrc")
 
 # kernel key -> (kernel-name match, source files that define the kernel)
 KERNELS = {
-    "gemm_fwd_7b": ("k_gemm_nf4<false>", ["gemm.hip", "gemm_args.h", "nf4_lut.h", "common.h"]),
-    "gemm_dx_7b": ("k_gemm_nf4<true>", ["gemm.hip", "gemm_args.h", "nf4_lut.h", "common.h"]),
+    "gemm_fwd_7b": ("k_gemm_nf4<false, qlora::Bf16>", ["gemm.hip", "gemm_args.h", "nf4_lut.h", "common.h",
+                                                      "dropout.h"]),
+    "gemm_dx_7b": ("k_gemm_nf4<true, qlora::Bf16>", ["gemm.hip", "gemm_args.h", "nf4_lut.h", "common.h",
+                                                    "dropout.h"]),
 }
 COPY_KERNEL = "neg_kernel"  # torch.neg over PMC_COPY_BYTES of fp32 (bench.py --pmc-pass)
 

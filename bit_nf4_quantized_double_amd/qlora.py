@@ -52,6 +52,11 @@ def lib() -> ctypes.CDLL:
         "qlora_quantize_nf4_dq_bf16": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
         "qlora_merge": (ctypes.c_int, [W, _vp, _vp, _c_i32, ctypes.c_float, _vp, _vp]),
         "qlora_dequant": (ctypes.c_int, [W, _vp, _vp]),
+        "qlora_dequant_f16": (ctypes.c_int, [W, _vp, _vp]),
+        "qlora_linear_fwd_f16": (ctypes.c_int, [W, _vp, _c_i64, _vp, _vp, _c_i32, ctypes.c_float,
+                                                _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+        "qlora_linear_bwd_f16": (ctypes.c_int, [W, _vp, _vp, _c_i64, _vp, _vp, _c_i32, ctypes.c_float,
+                                                _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
         "qlora_linear_fwd": (ctypes.c_int, [W, _vp, _c_i64, _vp, _vp, _c_i32, ctypes.c_float,
                                             _vp, _vp, _vp, ctypes.c_size_t, _vp]),
         "qlora_linear_bwd": (ctypes.c_int, [W, _vp, _vp, _c_i64, _vp, _vp, _c_i32, ctypes.c_float,
@@ -238,14 +243,30 @@ def merge(w: NF4Weight, A: torch.Tensor | None, B: torch.Tensor | None, r: int, 
     return out
 
 
-def dequant(w: NF4Weight, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Whole weight as a bf16 [n_out, k_in] GPU tensor."""
+def dequant(w: NF4Weight, out: torch.Tensor | None = None, dtype=torch.bfloat16) -> torch.Tensor:
+    """Whole weight as a bf16 (or, with dtype=torch.float16 or an fp16
+    ``out``, fp16) [n_out, k_in] GPU tensor."""
+    if out is not None:
+        dtype = out.dtype
+    if dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("dequant produces bf16 or fp16")
     if out is None:
-        out = torch.empty((w.n_out, w.k_in), dtype=torch.bfloat16, device=w.codes.device)
+        out = torch.empty((w.n_out, w.k_in), dtype=dtype, device=w.codes.device)
     cw = w._c()
-    st = lib().qlora_dequant(ctypes.byref(cw), _dev(out, torch.bfloat16, "out"), _stream())
-    _check(st, "qlora_dequant")
+    if dtype == torch.float16:
+        st = lib().qlora_dequant_f16(ctypes.byref(cw), _dev(out, torch.float16, "out"), _stream())
+        _check(st, "qlora_dequant_f16")
+    else:
+        st = lib().qlora_dequant(ctypes.byref(cw), _dev(out, torch.bfloat16, "out"), _stream())
+        _check(st, "qlora_dequant")
     return out
+
+
+def _elem(X: torch.Tensor):
+    """16-bit element type of a product: bf16 or fp16, from the activations."""
+    if X.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"X must be bf16 or fp16, got {X.dtype}")
+    return X.dtype
 
 
 def new_workspace(op: int, M: int, n_out: int, k_in: int, r: int, device) -> torch.Tensor:
@@ -274,18 +295,22 @@ def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor | None, B: torch.T
     """
     M = X.shape[0]
     dev = X.device
+    et = _elem(X)
     if Y is None:
-        Y = torch.empty((M, w.n_out), dtype=torch.bfloat16, device=dev)
+        Y = torch.empty((M, w.n_out), dtype=et, device=dev)
     if return_u and r > 0 and U is None:
-        U = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+        U = torch.empty((M, r), dtype=et, device=dev)
     wsb = workspace_bytes(QLORA_OP_FWD, M, w.n_out, w.k_in, r)
     wst, wsn = _ws(wsb, dev, ws)
     cw = w._c()
-    head = (ctypes.byref(cw), _dev(X, torch.bfloat16, "X"), M,
-            _opt(A, torch.bfloat16, "A"), _opt(B, torch.bfloat16, "B"), r, float(alpha))
-    tail = (_dev(Y, torch.bfloat16, "Y"), _opt(U, torch.bfloat16, "U"),
-            None if wst is None else wst.data_ptr(), wsn, _stream())
-    if dropout_p:
+    head = (ctypes.byref(cw), _dev(X, et, "X"), M, _opt(A, et, "A"), _opt(B, et, "B"), r, float(alpha))
+    tail = (_dev(Y, et, "Y"), _opt(U, et, "U"), None if wst is None else wst.data_ptr(), wsn, _stream())
+    if et == torch.float16:
+        if dropout_p:
+            raise NotImplementedError("LoRA dropout is exposed for the bf16 instance only")
+        st = lib().qlora_linear_fwd_f16(*head, *tail)
+        _check(st, "qlora_linear_fwd_f16")
+    elif dropout_p:
         st = lib().qlora_linear_fwd_dropout(*head, float(dropout_p), int(seed) & (2**64 - 1), *tail)
         _check(st, "qlora_linear_fwd_dropout")
     else:
@@ -306,8 +331,9 @@ def linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor 
     """
     M = X.shape[0]
     dev = X.device
+    et = _elem(X)
     if dX is None:
-        dX = torch.empty((M, w.k_in), dtype=torch.bfloat16, device=dev)
+        dX = torch.empty((M, w.k_in), dtype=et, device=dev)
     if r > 0 and dA is None:
         dA = torch.empty((r, w.k_in), dtype=torch.float32, device=dev)
     if r > 0 and dB is None:
@@ -315,12 +341,17 @@ def linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor 
     wsb = workspace_bytes(QLORA_OP_BWD, M, w.n_out, w.k_in, r)
     wst, wsn = _ws(wsb, dev, ws)
     cw = w._c()
-    head = (ctypes.byref(cw), _dev(X, torch.bfloat16, "X"), _dev(dY, torch.bfloat16, "dY"), M,
-            _opt(A, torch.bfloat16, "A"), _opt(B, torch.bfloat16, "B"), r, float(alpha))
-    tail = (_opt(U, torch.bfloat16, "U"), _dev(dX, torch.bfloat16, "dX"),
+    head = (ctypes.byref(cw), _dev(X, et, "X"), _dev(dY, et, "dY"), M,
+            _opt(A, et, "A"), _opt(B, et, "B"), r, float(alpha))
+    tail = (_opt(U, et, "U"), _dev(dX, et, "dX"),
             _opt(dA, torch.float32, "dA"), _opt(dB, torch.float32, "dB"),
             None if wst is None else wst.data_ptr(), wsn, _stream())
-    if dropout_p:
+    if et == torch.float16:
+        if dropout_p:
+            raise NotImplementedError("LoRA dropout is exposed for the bf16 instance only")
+        st = lib().qlora_linear_bwd_f16(*head, *tail)
+        _check(st, "qlora_linear_bwd_f16")
+    elif dropout_p:
         st = lib().qlora_linear_bwd_dropout(*head, float(dropout_p), int(seed) & (2**64 - 1), *tail)
         _check(st, "qlora_linear_bwd_dropout")
     else:

@@ -57,6 +57,12 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16).copy()
 
 
+def to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> fp16 (RNE, torch CPU) as uint16 bits."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
 def rng_for(workload: str, linear_index: int) -> np.random.Generator:
     if workload == "cfg1":
         return np.random.default_rng(0)
@@ -68,25 +74,26 @@ def draw(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
 
 
 def linear_inputs(n_out: int, k_in: int, m: int, r: int, rng: np.random.Generator,
-                  with_grad: bool = True) -> dict:
+                  with_grad: bool = True, dtype: str = "bf16") -> dict:
     """One linear's inputs: W fp32 [N, K]; X [M, K], A [r, K], B [N, r],
-    dY [M, N] as bf16 bits."""
+    dY [M, N] as bf16 bits (dtype="f16": fp16 bits, same draws)."""
+    to16 = to_f16_bits if dtype == "f16" else to_bf16_bits
     W = draw(rng, (n_out, k_in), 0.02)
-    X = to_bf16_bits(draw(rng, (m, k_in), 1.0))
-    A = to_bf16_bits(draw(rng, (r, k_in), float(1.0 / np.sqrt(k_in))))
-    B = to_bf16_bits(draw(rng, (n_out, r), 0.01))
+    X = to16(draw(rng, (m, k_in), 1.0))
+    A = to16(draw(rng, (r, k_in), float(1.0 / np.sqrt(k_in))))
+    B = to16(draw(rng, (n_out, r), 0.01))
     out = {"W": W, "X": X, "A": A, "B": B}
     if with_grad:
-        out["dY"] = to_bf16_bits(draw(rng, (m, n_out), 1.0))
+        out["dY"] = to16(draw(rng, (m, n_out), 1.0))
     return out
 
 
 def workload_linear(workload: str, index: int, m: int | None = None,
-                    with_grad: bool = True) -> dict:
+                    with_grad: bool = True, dtype: str = "bf16") -> dict:
     lin = LAYERS[workload][index]
     mm = TOKENS[workload] if m is None else m
     d = linear_inputs(lin.n_out, lin.k_in, mm, RANK[workload], rng_for(workload, index),
-                      with_grad=with_grad)
+                      with_grad=with_grad, dtype=dtype)
     d.update(name=lin.name, n_out=lin.n_out, k_in=lin.k_in, m=mm,
              r=RANK[workload], alpha=ALPHA[workload])
     return d

@@ -198,6 +198,28 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_
                      void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * fp16 instance of the path: the same operations with every 16-bit
+ * quantity in IEEE binary16 instead of bf16 -- the decoded weight
+ * (W_f16 = RNE_fp16(level[c] * fp32(q8 * s2))), X, A, B, Y, U~, dY, V~ and
+ * dX -- on v_mfma_f32_*_f16.  The pages compute in bf16 and name fp16 for
+ * GPUs without bf16 ([P1] "A complete run on a 12 GB-class GPU", the
+ * bnb_4bit_compute_dtype line).  The weight triple, dA, dB, the workspace
+ * sizes and every check and error are exactly those of qlora_dequant,
+ * qlora_linear_fwd and qlora_linear_bwd; the 16-bit arguments are binary16
+ * bit patterns.  A separate instantiation of the kernels, not a runtime
+ * switch inside them.
+ */
+int qlora_dequant_f16(const qlora_nf4_weight *w, uint16_t *W_f16, hipStream_t stream);
+int qlora_linear_fwd_f16(const qlora_nf4_weight *w, const uint16_t *X, int64_t M,
+                         const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
+                         uint16_t *Y, uint16_t *U_out, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+int qlora_linear_bwd_f16(const qlora_nf4_weight *w, const uint16_t *X, const uint16_t *dY,
+                         int64_t M, const uint16_t *A, const uint16_t *B, int32_t r,
+                         float alpha, const uint16_t *U, uint16_t *dX, float *dA, float *dB,
+                         void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Forward and backward with LoRA dropout of the adapter input.  The pages'
  * adapter configurations set lora_dropout = 0.05 ([P1] "A complete run on a
  * 12 GB-class GPU"; [P5] "Walking through the tooling") without defining

@@ -164,6 +164,97 @@ def test_quantize_dequant_full_size_sampled_groups(workload, index):
         assert np.array_equal(got, wb.ravel()), g
 
 
+# ----------------------------------------------------------- fp16 instance ----
+
+def dev_f16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.float16).cuda()
+
+
+def f64h(t):
+    if t.dtype == torch.float16:
+        return oracle.f16.f64_from_f16_bits(t.view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.double().cpu().numpy()
+
+
+def test_f16_dequant_bit_exact():
+    _need_gpu()
+    rng = np.random.default_rng(8)
+    for W in (_edge_weight(), (rng.standard_normal((136, 1984), dtype=np.float32) * np.float32(0.02))):
+        W = np.ascontiguousarray(W, dtype=np.float32)
+        q = oracle.quantize_nf4_dq(W)
+        _, hb = oracle.f16.dequant_f16(q["codes"], q["absmax_q8"], q["absmax_scale"], *W.shape)
+        w = gpu_quantize(W)
+        out = qlora.dequant(w, dtype=torch.float16)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), hb)
+
+
+F16_SHAPES = [
+    (16, 256, 256, 8, 16.0),
+    (100, 200, 192, 16, 32.0),
+    (300, 520, 640, 64, 128.0),
+    (17, 136, 320, 17, 5.0),
+    (257, 384, 512, 0, 0.0),
+    (5, 1000, 384, 16, 32.0),     # few-token kernel
+    (16, 4104, 320, 64, 128.0),   # few-token kernel, partial tile
+]
+
+
+@pytest.mark.parametrize("M,N,K,r,alpha", F16_SHAPES)
+def test_f16_forward_backward_parity(M, N, K, r, alpha):
+    _need_gpu()
+    rng = np.random.default_rng(M * 5 + N + 1)
+    d = synth.linear_inputs(N, K, M, r, rng, dtype="f16")
+    q = oracle.quantize_nf4_dq(d["W"])
+    _, hb = oracle.f16.dequant_f16(q["codes"], q["absmax_q8"], q["absmax_scale"], N, K)
+    Wh = oracle.f16.f64_from_f16_bits(hb)
+    Xh, dYh = oracle.f16.f64_from_f16_bits(d["X"]), oracle.f16.f64_from_f16_bits(d["dY"])
+    Ah = oracle.f16.f64_from_f16_bits(d["A"]) if r > 0 else np.zeros((0, K))
+    Bh = oracle.f16.f64_from_f16_bits(d["B"]) if r > 0 else np.zeros((N, 0))
+    w = gpu_quantize(d["W"])
+    X, dY = dev_f16(d["X"]), dev_f16(d["dY"])
+    A = dev_f16(d["A"]) if r > 0 else None
+    B = dev_f16(d["B"]) if r > 0 else None
+    Y, U = qlora.linear_fwd(w, X, A, B, r, alpha)
+    assert Y.dtype == torch.float16
+    dX, dA, dB = qlora.linear_bwd(w, X, dY, A, B, r, alpha, U)
+    torch.cuda.synchronize()
+    Yr, Ur = oracle.linear_fwd(Wh, Xh, Ah, Bh, alpha, r)
+    dXr, dAr, dBr = oracle.linear_bwd(Wh, Xh, dYh, Ah, Bh, alpha, r)
+    check_close(f64h(Y), Yr, "Y fp16")
+    check_close(f64h(dX), dXr, "dX fp16")
+    if r > 0 and alpha != 0:
+        check_close(f64h(U), oracle.lora_scale(alpha, r) * Ur, "U~ fp16")
+        check_close(f64(dA), dAr, "dA fp16")
+        check_close(f64(dB), dBr, "dB fp16")
+
+
+def test_f16_full_7b_linear_sampled():
+    """The 7B gate linear at 2048 tokens in fp16: Y and dX on 32 sampled
+    rows, dA and dB in full, against the oracle's fp16 weight."""
+    _need_gpu()
+    d = synth.workload_linear("7b", 4, dtype="f16")
+    N, K, M, r, alpha = d["n_out"], d["k_in"], d["m"], d["r"], d["alpha"]
+    q = oracle.quantize_nf4_dq(d["W"])
+    _, hb = oracle.f16.dequant_f16(q["codes"], q["absmax_q8"], q["absmax_scale"], N, K)
+    w = gpu_quantize(d["W"])
+    X, dY, A, B = dev_f16(d["X"]), dev_f16(d["dY"]), dev_f16(d["A"]), dev_f16(d["B"])
+    Y, U = qlora.linear_fwd(w, X, A, B, r, alpha)
+    dX, dA, dB = qlora.linear_bwd(w, X, dY, A, B, r, alpha, U)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(2).choice(M, 32, replace=False))
+    Wh = oracle.f16.f64_from_f16_bits(hb)
+    Xh, dYh = oracle.f16.f64_from_f16_bits(d["X"]), oracle.f16.f64_from_f16_bits(d["dY"])
+    Ah, Bh = oracle.f16.f64_from_f16_bits(d["A"]), oracle.f16.f64_from_f16_bits(d["B"])
+    Yr, _ = oracle.linear_fwd(Wh, Xh[rows], Ah, Bh, alpha, r)
+    dXr, _, _ = oracle.linear_bwd(Wh, Xh[rows], dYh[rows], Ah, Bh, alpha, r)
+    check_close(f64h(Y)[rows], Yr, "Y fp16 sampled")
+    check_close(f64h(dX)[rows], dXr, "dX fp16 sampled")
+    s = oracle.lora_scale(alpha, r)
+    check_close(f64(dA), s * ((dYh @ Bh).T @ Xh), "dA fp16")
+    check_close(f64(dB), s * (dYh.T @ (Xh @ Ah.T)), "dB fp16")
+
+
 # ------------------------------------------------------- format variants ----
 
 @pytest.mark.parametrize("fmt", ["nf4_dq", "nf4", "int4_dq", "int4"])
