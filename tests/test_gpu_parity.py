@@ -603,16 +603,59 @@ def test_full_7b_linear_sampled(index):
     check_close(f64(dB), dBr, "dB")
 
 
-@pytest.mark.parametrize("M", [1, 4, 16])
-def test_few_token_70b_gate_sampled_columns(M):
+def _full_linear_sampled(workload, index, nrows):
+    """One linear of a full-size decoder layer at its token count: Y and dX on
+    sampled rows, dA and dB in full, all against the oracle's quantization of
+    the whole weight."""
+    d = synth.workload_linear(workload, index)
+    N, K, M, r, alpha = d["n_out"], d["k_in"], d["m"], d["r"], d["alpha"]
+    q = oracle.quantize_nf4_dq(d["W"])
+    _, wb = oracle.dequant(q["codes"], q["absmax_q8"], q["absmax_scale"], N, K)
+    w = gpu_quantize(d["W"])
+    X, A, B, dY = _dev_inputs(d, r)
+    Y, U = qlora.linear_fwd(w, X, A, B, r, alpha)
+    dX, dA, dB = qlora.linear_bwd(w, X, dY, A, B, r, alpha, U)
+    torch.cuda.synchronize()
+    check_codec_exact(w, q)
+    rows = np.sort(np.random.default_rng(index + 100).choice(M, nrows, replace=False))
+    Wf = oracle.f64_from_bf16_bits(wb)
+    Xf, dYf = oracle.f64_from_bf16_bits(d["X"]), oracle.f64_from_bf16_bits(d["dY"])
+    Af, Bf = oracle.f64_from_bf16_bits(d["A"]), oracle.f64_from_bf16_bits(d["B"])
+    s = oracle.lora_scale(alpha, r)
+    check_close(f64(Y)[rows], Xf[rows] @ Wf.T + s * (Xf[rows] @ Af.T) @ Bf.T, f"{workload} Y rows")
+    check_close(f64(dX)[rows], dYf[rows] @ Wf + s * (dYf[rows] @ Bf) @ Af, f"{workload} dX rows")
+    check_close(f64(dA), s * ((dYf @ Bf).T @ Xf), f"{workload} dA")
+    check_close(f64(dB), s * (dYf.T @ (Xf @ Af.T)), f"{workload} dB")
+
+
+@pytest.mark.parametrize("index", [0, 1, 4, 6])  # q, k (3072 -> 1024), gate, down
+def test_full_3b_linear_sampled(index):
+    """3B-class decoder layer (width 3072, MLP 8192) at 2048 tokens."""
     _need_gpu()
-    d = synth.workload_linear("70b", 0, m=M, with_grad=False)
+    _full_linear_sampled("3b", index, 32)
+
+
+@pytest.mark.parametrize("index", [0, 1, 4, 6])  # q, k (4096 -> 1024), gate (-> 14336), down
+def test_full_8b_linear_sampled(index):
+    """8B-class decoder layer at batch 4 x seq 2048 = 8192 tokens (32 row
+    blocks: every band of the tile order)."""
+    _need_gpu()
+    _full_linear_sampled("8b", index, 24)
+
+
+@pytest.mark.parametrize("index,M", [(0, 1), (0, 4), (0, 16), (1, 1), (1, 16)])
+def test_few_token_70b_sampled_columns(index, M):
+    """The 70B gate (8192 -> 28672) and down (28672 -> 8192) weights at M = 1,
+    4, 16: 64 sampled output columns against rows of W the oracle quantizes
+    group by group."""
+    _need_gpu()
+    d = synth.workload_linear("70b", index, m=M, with_grad=False)
     N, K, r, alpha = d["n_out"], d["k_in"], d["r"], d["alpha"]
     w = gpu_quantize(d["W"])
     X, A, B = dev_bf16(d["X"]), dev_bf16(d["A"]), dev_bf16(d["B"])
     Y, _ = qlora.linear_fwd(w, X, A, B, r, alpha)
     torch.cuda.synchronize()
-    cols = np.sort(np.random.default_rng(M).choice(N, 64, replace=False))
+    cols = np.sort(np.random.default_rng(M + 10 * index).choice(N, 64, replace=False))
     flat = d["W"].ravel()
     bpr = K // 64  # blocks per row
     Wrows = []
