@@ -349,7 +349,8 @@ def test_forward_parity(M, N, K, r, alpha):
 # Few-token forward (M <= 16 runs a dedicated kernel): partial 16-row tiles
 # (n_out % 16 == 8), half 128-wide chunks (k_in % 128 == 64), ranks that are
 # not multiples of 8, and tile counts that select every work split (1 to 8
-# tiles per wave, 1 to 8 waves per reduction).
+# tiles per wave, 1 to 8 waves per reduction), a full 16-token tile with a
+# single tile per workgroup, a long reduction at M = 1, and ranks 1 and 17.
 FEW_SHAPES = [
     (1, 8, 64, 0, 0.0),
     (2, 264, 192, 3, 6.0),
@@ -360,6 +361,10 @@ FEW_SHAPES = [
     (3, 32768, 64, 5, 8.0),
     (16, 2048, 1088, 32, 64.0),
     (11, 512, 4096, 0, 0.0),
+    (16, 136, 2048, 16, 32.0),
+    (1, 8192, 8192, 16, 32.0),
+    (4, 520, 640, 17, 34.0),
+    (9, 1032, 960, 1, 2.0),
 ]
 
 
@@ -371,8 +376,10 @@ def test_few_token_forward_parity(M, N, K, r, alpha):
     X, A, B, _ = _dev_inputs(d, r)
     Y, U = qlora.linear_fwd(w, X, A, B, r, alpha)
     torch.cuda.synchronize()
-    Yr, _ = oracle.linear_fwd(wb, d["X"], d["A"], d["B"], alpha, r)
+    Yr, Ur = oracle.linear_fwd(wb, d["X"], d["A"], d["B"], alpha, r)
     check_close(f64(Y), Yr, "Y")
+    if r > 0:
+        check_close(f64(U), oracle.lora_scale(alpha, r) * Ur, "U~")
     Y2, _ = qlora.linear_fwd(w, X, A, B, r, alpha, return_u=False)
     torch.cuda.synchronize()
     assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16))
