@@ -36,7 +36,8 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kTileK = 256;       // weight columns per workgroup
 constexpr int kWaveRows = 16;     // rows per wave block
-constexpr int kSubBlocks = 4;     // 16-row blocks per wave (workgroup: 4 x 4 x 16 rows)
+constexpr int kSubBlocks = 2;     // 16-row blocks per wave (workgroup: 4 x 2 x 16 rows; 4 and 8 were
+                                  // 5-7 % and 15 % slower on the 70B shapes: fewer workgroups in flight)
 constexpr int kRowsPerWg = 4 * kWaveRows * kSubBlocks;
 // bf16 per row of the A copy: 8 words mod 32 banks between rows, so the 16
 // lanes of a transposing read (4 rows x 4 eight-byte pieces) hit 32 banks

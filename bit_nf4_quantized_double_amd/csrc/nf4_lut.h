@@ -112,19 +112,16 @@ __device__ __forceinline__ uint4 decode8_lut(const Lut& L, uint32_t d, const Lan
   return o;
 }
 
-// ---- parity-split tables ----------------------------------------------------
-// Variant for LutPartner::kRows16 in which the even row builds the table of
-// the even levels (0, 2, .., 14) and the odd row the odd levels: then table
-// "a" holds level 2i and table "b" level 2i + 1 at entry i, a code c is
-// looked up at entry c >> 1 in both, and bit 0 of c picks the result.  That
-// needs no per-half index adjustment.
-__device__ __forceinline__ void lane_levels_parity(const Nf4Consts& nf4, bool odd, float th[8]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) th[i] = odd ? nf4.level[2 * i + 1] : nf4.level[2 * i];
-}
+// ---- element-order lookup (no nibble spread) -------------------------------
+// With LutPartner::kRows16 tables ("a" = levels 0..7, "b" = levels 8..15 on
+// every lane) the 8 codes of a dword are looked up without first spreading
+// them into byte order: the low nibbles (elements 0, 2, 4, 6) and the high
+// nibbles (1, 3, 5, 7) are indexed separately, which leaves the decoded
+// values in the element order 0, 2, 4, 6, 1, 3, 5, 7.  The other MFMA
+// operand must carry the same order (x_order_even_odd).
 
-// Constants of the parity-split lookup, held in VGPRs so that each
-// (x & m) | c folds into one v_bitop3_b32 (one scalar operand at most).
+// Constants of the element-order lookup, held in VGPRs so that each
+// (x & m) | c folds into one v_and_or_b32 (one scalar operand at most).
 struct EoConsts {
   uint32_t m7;    // 0x07070707
   uint32_t m4;    // 0x04040404
@@ -137,8 +134,8 @@ __device__ __forceinline__ EoConsts eo_consts() {
   return k;
 }
 
-// 4 codes: entry indices (one per byte, 0..7) and selector (byte i =
-// i + 4 * (bit 0 of code i)) -> {w0,w1}, {w2,w3} as bf16 pairs.
+// 4 codes: entry indices (one per byte, 0..7) and selector (byte i = i, or
+// i + 4 to take table "b") -> {w0,w1}, {w2,w3} as bf16 pairs.
 __device__ __forceinline__ void lookup4_eo(const Lut& L, uint32_t idx, uint32_t sel, uint32_t& o01,
                                            uint32_t& o23) {
   const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(L.blo1, L.blo0, idx),
@@ -149,15 +146,15 @@ __device__ __forceinline__ void lookup4_eo(const Lut& L, uint32_t idx, uint32_t 
   o23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
 }
 
-// 8 codes (one dword, element 0 in the low nibble) -> 8 bf16 in the element
-// order 0, 2, 4, 6, 1, 3, 5, 7 (low-nibble codes, then high-nibble codes),
-// from a parity-split table.  The other MFMA operand must carry the same
-// order (x_order_even_odd).
-__device__ __forceinline__ uint4 decode8_lut_eo(const Lut& L, uint32_t d, const EoConsts& k) {
-  const uint32_t ie = (d >> 1) & k.m7;            // low nibbles: c >> 1
-  const uint32_t io = (d >> 5) & k.m7;            // high nibbles: c >> 1
-  const uint32_t se = ((d << 2) & k.m4) | k.base;  // bit 0 of the low nibble -> bit 2
-  const uint32_t so = ((d >> 2) & k.m4) | k.base;  // bit 0 of the high nibble -> bit 2
+// 8 codes (one dword, element 0 in the low nibble) -> 8 16-bit values in the
+// element order 0, 2, 4, 6, 1, 3, 5, 7, from kRows16 tables built with
+// lane_levels: a code c is looked up at entry c & 7 of both tables and bit 3
+// of c picks the result.  7 operations per 8 codes besides the 16 permutes.
+__device__ __forceinline__ uint4 decode8_lut_hl(const Lut& L, uint32_t d, const EoConsts& k) {
+  const uint32_t ie = d & k.m7;                    // low nibbles: c & 7
+  const uint32_t io = (d >> 4) & k.m7;             // high nibbles: c & 7
+  const uint32_t se = ((d >> 1) & k.m4) | k.base;  // bit 3 of the low nibble -> bit 2
+  const uint32_t so = ((d >> 5) & k.m4) | k.base;  // bit 3 of the high nibble -> bit 2
   uint4 o;
   lookup4_eo(L, ie, se, o.x, o.y);
   lookup4_eo(L, io, so, o.z, o.w);

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
     for (int j = 0; j < 4; ++j) xf[j] = buf_load16(src.X, ok ? o + 16u * j : kOOB);
   };
   // The decoded W fragments come out in the element order 0,2,4,6,1,3,5,7 of
-  // each 8-column group (decode8_lut_eo); the X fragment is put in the same
+  // each 8-column group (decode8_lut_hl); the X fragment is put in the same
   // order once per chunk and reused by every tile.
   auto order_x = [&](const uint4 (&xc)[4], uint4 (&xo)[4]) {
 #pragma unroll
@@ -138,9 +138,9 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
   };
 
   // lanes l and l ^ 16 share a block: the even row (g even) builds the
-  // entries of the even levels, the odd row those of the odd levels
+  // entries of levels 0..7, the odd row those of levels 8..15
   float th[8];
-  lane_levels_parity(a.nf4, g & 1, th);
+  lane_levels(a.nf4, g & 1, th);
   const EoConsts kc = eo_consts();
 
   f32x4 acc[TPW];
@@ -177,10 +177,10 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
       const SkSeg cs = rg[t];
       const float scale = SL ? sc[t] : (float)cs.q * cs.s2;  // a' = fp32(q8 * s2)
       const Lut L = build_lut<LutPartner::kRows16, E>(th, scale);
-      const uint4 w0 = decode8_lut_eo(L, cs.code.x, kc);
-      const uint4 w1 = decode8_lut_eo(L, cs.code.y, kc);
-      const uint4 w2 = decode8_lut_eo(L, cs.code.z, kc);
-      const uint4 w3 = decode8_lut_eo(L, cs.code.w, kc);
+      const uint4 w0 = decode8_lut_hl(L, cs.code.x, kc);
+      const uint4 w1 = decode8_lut_hl(L, cs.code.y, kc);
+      const uint4 w2 = decode8_lut_hl(L, cs.code.z, kc);
+      const uint4 w3 = decode8_lut_hl(L, cs.code.w, kc);
       rg[t] = load(t, i + RD);  // the same tile, RD chunks ahead
       __builtin_amdgcn_sched_barrier(0);
       acc[t] = E::mfma16(E::vec(w0), E::vec(xc[0]), acc[t]);
