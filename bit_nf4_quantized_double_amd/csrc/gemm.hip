@@ -56,14 +56,17 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 __device__ __forceinline__ uint32_t kt_off(uint32_t row, uint32_t chunk) {
   return row * 64u + ((chunk ^ swz(row)) << 3);
 }
-// NN W tile: 64 rows of BN bf16, padded by 16 elements; the 16-byte chunks of
-// the upper half of a row have bit 0 of their index flipped.  With 32 LDS
-// banks this makes both the producers' ds_write_b128 (4 threads per row at
-// 64-byte stride) and the consumers' transposing ds_read_b64_tr_b16
-// conflict-free.
-constexpr int kNNPitch = BN + 16;
+// NN W tile: 64 rows of BN bf16, padded by 32 elements; 16-byte chunk ch of
+// row n is stored at chunk ch ^ 2 (ch >> 3) ^ (n & 3).  Both the producers'
+// ds_write_b128 (4 threads per row at 64-byte stride) and the consumers'
+// transposing ds_read_b64_tr_b16 are then free of LDS bank conflicts
+// (measured with SQ_LDS_BANK_CONFLICT; a 16-element pad with only the upper
+// half-row flipped, conflict-free in a 32-bank model, cost 2 conflict cycles
+// per transposing read).
+constexpr int kNNPitch = BN + 32;
 __device__ __forceinline__ uint32_t nn_off(uint32_t row, uint32_t col) {
-  return row * kNNPitch + ((((col >> 3) ^ (col >> 6)) << 3) | (col & 7));
+  const uint32_t ch = col >> 3;
+  return row * kNNPitch + ((((ch ^ ((ch >> 3) << 1) ^ (row & 3)) & 15u) << 3) | (col & 7));
 }
 
 template <bool NN>
