@@ -39,6 +39,7 @@ namespace {
 
 constexpr int kSkWaves = 8;
 constexpr int kSkThreads = 64 * kSkWaves;
+constexpr int kSkMaxStageLoads = 8;  // 16-byte staged-scale loads per thread: sbytes <= 60 KB
 
 struct SkSeg {
   uint4 code;  // 32 codes
@@ -73,29 +74,59 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
   // first W row of this lane in tile 0 of the wave; tile t adds 16 rows
   const int n0 = (blockIdx.x * a.tiles + wa * TPW) * 16 + row;
 
-  // staged scales: q8 of the workgroup's rows [rowbase, rowbase + 16 tiles),
-  // all blocks of each row (nbr per row), then the s2 values they refer to
+  // staged scales: q8 of the workgroup's R = 16 tiles rows, all nbr blocks of
+  // each, then the s2 values they refer to.  When nbr % 4 == 0 the rows are
+  // stored qp = nbr + 4 bytes apart, so that the 16 rows one read
+  // instruction touches fall in 16 different LDS banks (rows a multiple of
+  // 128 bytes apart hit 2 banks: about 30 conflict cycles per read).
   const int nbr = a.K >> 6;
-  const uint32_t qbase = (uint32_t)blockIdx.x * (uint32_t)a.tiles * 16u * (uint32_t)nbr;  // first block
-  const uint32_t qbytes = (uint32_t)a.tiles * 16u * (uint32_t)nbr;                       // multiple of 16
+  const uint32_t R = (uint32_t)a.tiles * 16u;
+  const uint32_t qp = (nbr & 3) ? (uint32_t)nbr : (uint32_t)nbr + 4u;  // LDS row pitch in bytes
+  const uint32_t qbase = (uint32_t)blockIdx.x * R * (uint32_t)nbr;    // first block
+  const uint32_t qbytes = R * (uint32_t)nbr;                         // multiple of 16
   const uint32_t g_first = qbase >> 8;
   const uint8_t* const s_q8 = reinterpret_cast<const uint8_t*>(s_dyn);
-  const float* const s_s2 = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(s_dyn) + qbytes);
+  const float* const s_s2 = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(s_dyn) + R * qp);
   if (SL) {
     uint8_t* q8w = reinterpret_cast<uint8_t*>(s_dyn);
-    float* s2w = reinterpret_cast<float*>(q8w + qbytes);
+    float* s2w = reinterpret_cast<float*>(q8w + R * qp);
     const uint32_t ngs = ((qbase + qbytes - 1) >> 8) - g_first + 1;
-    for (uint32_t i = tid; i < qbytes / 16; i += kSkThreads)
-      *reinterpret_cast<uint4*>(q8w + 16 * i) = buf_load16(src.q8, qbase + 16 * i);
-    for (uint32_t i = tid; i < ngs; i += kSkThreads)
-      s2w[i] = __builtin_bit_cast(float, buf_load4(src.s2, (g_first + i) * 4));
+    uint4 qv[kSkMaxStageLoads];  // all staged loads in flight at once
+#pragma unroll
+    for (int u = 0; u < kSkMaxStageLoads; ++u) {
+      const uint32_t i = (uint32_t)tid + (uint32_t)u * kSkThreads;
+      qv[u] = buf_load16(src.q8, i < qbytes / 16 ? qbase + 16 * i : kOOB);
+    }
+    float sv = 0.f;
+    if ((uint32_t)tid < ngs) sv = __builtin_bit_cast(float, buf_load4(src.s2, (g_first + tid) * 4));
+#pragma unroll
+    for (int u = 0; u < kSkMaxStageLoads; ++u) {
+      const uint32_t i = (uint32_t)tid + (uint32_t)u * kSkThreads;
+      if (i < qbytes / 16) {
+        if (qp == (uint32_t)nbr) {
+          *reinterpret_cast<uint4*>(q8w + 16 * i) = qv[u];
+        } else {
+          // dwords 4 i .. 4 i + 3 of the rows: row r = 16 i / nbr, byte b (a multiple of 4)
+          uint32_t r = (16 * i) / (uint32_t)nbr, b = 16 * i - r * (uint32_t)nbr;
+          const uint32_t dw[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            *reinterpret_cast<uint32_t*>(q8w + r * qp + b) = dw[d];
+            b += 4;
+            if (b == (uint32_t)nbr) { b = 0; ++r; }
+          }
+        }
+      }
+    }
+    if ((uint32_t)tid < ngs) s2w[tid] = sv;
     __syncthreads();
   }
   // block scale a' = fp32(q8 * s2) of tile t, chunk c for this lane
   auto lds_scale = [&](int t, int c) {
     const int blk = min(2 * c + (g >> 1), nbr - 1);  // padding chunks: any finite scale
-    const uint32_t bl = (uint32_t)((wa * TPW + t) * 16 + row) * (uint32_t)nbr + (uint32_t)blk;
-    return (float)s_q8[bl] * s_s2[((qbase + bl) >> 8) - g_first];
+    const uint32_t rw = (uint32_t)((wa * TPW + t) * 16 + row);
+    const uint32_t bl = rw * (uint32_t)nbr + (uint32_t)blk;  // block index within the workgroup's rows
+    return (float)s_q8[rw * qp + (uint32_t)blk] * s_s2[((qbase + bl) >> 8) - g_first];
   };
   const uint32_t e0 = (uint32_t)n0 * (uint32_t)a.K + 32u * (uint32_t)g;  // weight index at chunk 0
 
@@ -326,7 +357,8 @@ hipError_t launch_skinny_fwd(SkinnyArgs a, hipStream_t st) {
   const size_t red = (size_t)a.tiles * nwk * 64 * sizeof(float4);
   // staged scales: q8 of 16 * tiles rows plus the s2 groups they span
   const size_t qbytes = (size_t)a.tiles * 16 * (size_t)(a.K / 64);
-  const size_t sbytes = qbytes + 4 * (qbytes / 256 + 2);
+  const size_t qpad = ((a.K / 64) & 3) ? 0 : (size_t)a.tiles * 16 * 4;  // row padding of the LDS copy
+  const size_t sbytes = qbytes + qpad + 4 * (qbytes / 256 + 2);
   const bool sl = a.K >= 64 && sbytes <= 60 * 1024;  // stays within the default 64 KB of dynamic LDS
   const size_t lds = std::max(red, sl ? sbytes : (size_t)0);
   switch (tpw * 16 + rd) {
