@@ -277,6 +277,36 @@ def main():
             "frac_fp16_mfma_peak": round(step_flops / (ms_h * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del h
 
+        # context, not a product path: the same layer's 14 products as plain
+        # dense bf16 GEMMs in torch.matmul (hipBLASLt) on a bf16 copy of each
+        # weight -- what the fused kernels are measured against
+        d = []
+        for e in lins:
+            W = (torch.randn((e["n"], e["k"]), device=dev) * 0.02).to(torch.bfloat16)
+            d.append(dict(W=W, Wt=W.t().contiguous(), Y=torch.empty_like(e["Y"]), dX=torch.empty_like(e["dX"])))
+
+        def step_dense():
+            for e, f in zip(lins, d):
+                torch.matmul(e["X"], f["Wt"], out=f["Y"])
+                torch.matmul(e["dY"], f["W"], out=f["dX"])
+
+        for _ in range(2):
+            step_dense()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(args.steps):
+            step_dense()
+        t1.record()
+        torch.cuda.synchronize()
+        ms_dn = t0.elapsed_time(t1) / max(1, args.steps)
+        dense_flops = sum(4.0 * M * e["n"] * e["k"] for e in lins)
+        secondary["context_dense_bf16_matmul_7b"] = {
+            "what": "the 7B layer's 14 GEMMs (Y = X W^T, dX = dY W) as dense bf16 torch.matmul "
+                    "(hipBLASLt) on a bf16 weight copy, no adapter and no NF4 decode",
+            "ms_per_step": round(ms_dn, 4), "TFLOP/s": round(dense_flops / (ms_dn * 1e-3) / 1e12, 2),
+            "frac_bf16_mfma_peak": round(dense_flops / (ms_dn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del d
+
     # ---------------------------------------------------- cpu baseline ----
     cpu = None
     if not args.no_cpu_baseline:
