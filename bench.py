@@ -277,6 +277,11 @@ def main():
             "frac_fp16_mfma_peak": round(step_flops / (ms_h * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del h
 
+        # the 3B layer (2048 tokens) and the 8B layer (8192 tokens): the same
+        # path at the pages' other training shapes
+        for wl in ("3b", "8b"):
+            secondary[f"layer_{wl}"] = bench_layer(torch, qlora, synth, dev, wl, max(3, args.steps // 4))
+
         # context, not a product path: the same layer's 14 products as plain
         # dense bf16 GEMMs in torch.matmul (hipBLASLt) on a bf16 copy of each
         # weight -- what the fused kernels are measured against
@@ -420,6 +425,53 @@ def bench_secondary(torch, qlora, synth, dev, evs, reps=10):
         del copies, w0
         torch.cuda.empty_cache()
     return res
+
+
+def bench_layer(torch, qlora, synth, dev, wl, steps):
+    """fwd+bwd of the 7 linears of a decoder layer at its token count on
+    device-generated N(0, 0.02^2) weights and N(0, 1) inputs."""
+    M, r, alpha = synth.TOKENS[wl], synth.RANK[wl], synth.ALPHA[wl]
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    lins = []
+    for lin in synth.LAYERS[wl]:
+        n, k = lin.n_out, lin.k_in
+        W = torch.randn((n, k), device=dev, generator=g) * 0.02
+        e = dict(n=n, k=k, w=qlora.quantize(W))
+        del W
+        bf = lambda *shape, sd=1.0: (torch.randn(shape, device=dev, generator=g) * sd).to(torch.bfloat16)
+        e.update(X=bf(M, k), A=bf(r, k, sd=k ** -0.5), B=bf(n, r, sd=0.01), dY=bf(M, n))
+        e.update(Y=torch.empty((M, n), dtype=torch.bfloat16, device=dev),
+                 U=torch.empty((M, r), dtype=torch.bfloat16, device=dev),
+                 dX=torch.empty((M, k), dtype=torch.bfloat16, device=dev),
+                 dA=torch.empty((r, k), dtype=torch.float32, device=dev),
+                 dB=torch.empty((n, r), dtype=torch.float32, device=dev),
+                 ws=qlora.new_workspace(qlora.QLORA_OP_BWD, M, n, k, r, dev),
+                 ws_fwd=qlora.new_workspace(qlora.QLORA_OP_FWD, M, n, k, r, dev))
+        lins.append(e)
+
+    def step():
+        for e in lins:
+            qlora.linear_fwd(e["w"], e["X"], e["A"], e["B"], r, alpha, Y=e["Y"], U=e["U"], ws=e["ws_fwd"])
+            qlora.linear_bwd(e["w"], e["X"], e["dY"], e["A"], e["B"], r, alpha, e["U"],
+                             dX=e["dX"], dA=e["dA"], dB=e["dB"], ws=e["ws"])
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    fl = sum(flops_linear(M, e["n"], e["k"], r) for e in lins)
+    del lins
+    torch.cuda.empty_cache()
+    return {"tokens": M, "steps": steps, "ms_per_step": round(ms, 4), "step_gflop": round(fl / 1e9, 2),
+            "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2),
+            "frac_bf16_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def bench_formats(torch, qlora, W, reps):
