@@ -105,7 +105,7 @@ def main():
                          "device-to-device copy of PMC_COPY_BYTES for counter calibration; no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the path runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the path is single-GPU: no sharding, no collectives)", file=sys.stderr)
         sys.exit(2)
 
