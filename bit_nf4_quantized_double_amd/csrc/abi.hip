@@ -117,22 +117,30 @@ int dropout_setup(int32_t r, float alpha, double p, uint64_t seed, qlora::DropMa
 struct BwdLayout {
   size_t u, v, part, cpart, total;  // part: U~ / V~ split-K partials; cpart: dA / dB row-chunk partials
   int nmc;
+  size_t req;   // bytes required (U~, V~ and the reduction partials)
+  size_t gemm;  // split-reduction tiles of the dX product, from `part` on
 };
 
 BwdLayout bwd_layout(int64_t M, int64_t n_out, int64_t k_in, int32_t r) {
   BwdLayout L{};
-  if (r <= 0 || M <= 0) return L;
-  const int mch = qlora::coldot_chunk_rows();
-  L.nmc = (int)((M + mch - 1) / mch);
-  const int64_t widest = n_out > k_in ? n_out : k_in;
-  L.u = 0;
-  L.v = L.u + round_up((size_t)M * r * 2);
-  L.part = L.v + round_up((size_t)M * r * 2);
-  // U~ and V~ split-K partials share one region (stream order); the dB and
-  // dA row-chunk partials share another (dB's are produced alongside V~'s)
-  const size_t part = std::max(qlora::rowdot_part_bytes(M, k_in, r), qlora::rowdot_part_bytes(M, n_out, r));
-  L.cpart = L.part + round_up(part);
-  L.total = L.cpart + round_up((size_t)L.nmc * r * widest * 4);
+  if (M <= 0) return L;
+  if (r > 0) {
+    const int mch = qlora::coldot_chunk_rows();
+    L.nmc = (int)((M + mch - 1) / mch);
+    const int64_t widest = n_out > k_in ? n_out : k_in;
+    L.u = 0;
+    L.v = L.u + round_up((size_t)M * r * 2);
+    L.part = L.v + round_up((size_t)M * r * 2);
+    // U~ and V~ split-K partials share one region (stream order); the dB and
+    // dA row-chunk partials share another (dB's are produced alongside V~'s)
+    const size_t part = std::max(qlora::rowdot_part_bytes(M, k_in, r), qlora::rowdot_part_bytes(M, n_out, r));
+    L.cpart = L.part + round_up(part);
+    L.req = L.cpart + round_up((size_t)L.nmc * r * widest * 4);
+  }
+  // the dX product's split-reduction tiles reuse everything from L.part on
+  // (dead by then); they need not fit: without room the product runs unsplit
+  L.gemm = round_up(qlora::gemm_part_bytes(M, k_in, n_out));
+  L.total = std::max(L.req, L.part + L.gemm);
   return L;
 }
 
@@ -175,8 +183,14 @@ void qlora_nf4_table(float out[16]) {
 
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, int32_t r) {
   if (M < 0 || n_out < 0 || k_in < 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
-  if (op == QLORA_OP_FWD)
-    return r > 0 && M > 0 ? round_up((size_t)M * r * 2) + round_up(qlora::rowdot_part_bytes(M, k_in, r)) : 0;
+  if (op == QLORA_OP_FWD) {
+    if (M == 0) return 0;
+    // [U~][U~ partials | split-reduction tiles of the main product]
+    const size_t u = r > 0 ? round_up((size_t)M * r * 2) : 0;
+    const size_t upart = r > 0 ? round_up(qlora::rowdot_part_bytes(M, k_in, r)) : 0;
+    const size_t gpart = M > qlora::skinny_max_tokens() ? round_up(qlora::gemm_part_bytes(M, n_out, k_in)) : 0;
+    return u + std::max(upart, gpart);
+  }
   if (op == QLORA_OP_BWD) return bwd_layout(M, n_out, k_in, r).total;
   return 0;
 }
@@ -256,9 +270,10 @@ static int linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t
   if (U_out && !aligned16(U_out)) return fail(QLORA_ERR_ALIGN, "U_out must be 16-byte aligned");
   uint16_t* U = nullptr;
   float* part = nullptr;
+  // workspace: [U~ when U_out is NULL][split-K partials of U~, later reused
+  // for the split-reduction tiles of the main product (optional)]
+  const size_t ubytes = r > 0 && !U_out ? round_up((size_t)M * r * 2) : 0;
   if (r > 0) {
-    // workspace: [U~ when U_out is NULL][split-K partials of U~]
-    const size_t ubytes = U_out ? 0 : round_up((size_t)M * r * 2);
     const size_t pbytes = qlora::rowdot_part_bytes(M, w->k_in, r);
     if (ubytes + pbytes > 0) {
       if (!ws || ws_bytes < ubytes + pbytes) return fail(QLORA_ERR_WORKSPACE, "forward workspace too small");
@@ -295,6 +310,9 @@ static int linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t
   g.out = Y; g.ld_out = w->n_out;
   g.nf4 = qlora::nf4_consts();
   g.f16 = f16;
+  const size_t gbytes = qlora::gemm_part_bytes(M, w->n_out, w->k_in);
+  if (gbytes && ws && aligned16(ws) && ws_bytes >= ubytes + gbytes)
+    g.part = reinterpret_cast<float*>(static_cast<char*>(ws) + ubytes);
   e = qlora::launch_gemm_fwd(g, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e, "forward GEMM launch");
 }
@@ -323,7 +341,7 @@ static int linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const u
   if (U && !aligned16(U)) return fail(QLORA_ERR_ALIGN, "U must be 16-byte aligned");
   const BwdLayout L = bwd_layout(M, N, K, r);
   if (r > 0 && M > 0) {
-    if (!ws || ws_bytes < L.total) return fail(QLORA_ERR_WORKSPACE, "backward workspace too small");
+    if (!ws || ws_bytes < L.req) return fail(QLORA_ERR_WORKSPACE, "backward workspace too small");
     if (!aligned16(ws)) return fail(QLORA_ERR_ALIGN, "workspace must be 16-byte aligned");
   }
 
@@ -373,6 +391,10 @@ static int linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const u
   g.nf4 = qlora::nf4_consts();
   g.drop = dm;
   g.f16 = f16;
+  // split-reduction tiles, from L.part on (U~ / V~ partials and dA / dB
+  // partials are consumed by now); without room the product runs unsplit
+  if (L.gemm && ws && aligned16(ws) && ws_bytes >= L.part + L.gemm)
+    g.part = reinterpret_cast<float*>(static_cast<char*>(ws) + L.part);
   e = qlora::launch_gemm_dx(g, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e, "dX GEMM launch");
 }

@@ -32,6 +32,12 @@
 // lookup table held as byte planes in registers and indexed with v_perm_b32;
 // the two lanes sharing a block each build half the table and swap halves
 // with one DPP move.  No LDS traffic for the lookup.
+//
+// Few output tiles (at most half as many as compute units): grid z splits the
+// reduction into ksplit ranges; each workgroup stores its fp32 tile and
+// k_splitk_reduce adds the tiles in split order and rounds once.
+#include <algorithm>
+
 #include "dropout.h"
 #include "gemm_args.h"
 #include "nf4_lut.h"
@@ -348,13 +354,20 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
   };
 
   const int nsteps = (a.R + 63) / 64;
-  // step count rounded up to even (an all-zero step adds nothing)
-  const int nst = (nsteps + 1) & ~1;
+  // Split reduction: this workgroup takes steps [s0, s0 + nloc) of the
+  // nsteps; every split loops over the same even step count nst (an all-zero
+  // step adds nothing).
+  const int kz = blockIdx.z;
+  const int spl = a.ksplit > 1 ? (nsteps + a.ksplit - 1) / a.ksplit : nsteps;
+  const int s0 = kz * spl;
+  const int nloc = max(0, min(spl, nsteps - s0));
+  const int nst = (spl + 1) & ~1;
+  const int kend = ((nsteps + 1) & ~1) * 64;  // >= R: loads there read zeros
   // All tiles walk the reduction in the same order, so the workgroups of
   // one XCD read the same activation / weight slices at about the same time
   // and share them in L2.
   auto kofs = [&](int step) {  // reduction offset of logical step; >= R past the end
-    return (step >= nst ? nst : step) * 64;
+    return step < nloc ? (s0 + step) * 64 : kend;
   };
   auto stage_of = [](int step) { return step % kActStages; };
 
@@ -428,7 +441,7 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
   // runs first, alone in the accumulators, which are masked before the main
   // reduction adds dY Wbf.  The producer of each slice draws the slice's
   // 64 x 128 keep bytes into activation stage 1 meanwhile.
-  const bool drop_first = NN && a.drop.thr != 0 && a.r > 0;
+  const bool drop_first = NN && a.drop.thr != 0 && a.r > 0 && kz == 0;
   if (drop_first) {
     adapter_step(w_buf0, act_ptr(0));
     uint8_t* keep = reinterpret_cast<uint8_t*>(act_ptr(1));
@@ -509,7 +522,26 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
 
   // ---- adapter step at the end (no dropout): W buffer 0 and activation
   // stage nst % 3 are no longer read
-  if (a.r > 0 && !drop_first) adapter_step(w_buf0, act_ptr(stage_of(nst)));
+  if (a.r > 0 && !drop_first && kz == 0) adapter_step(w_buf0, act_ptr(stage_of(nst)));
+
+  // ---- split reduction: this split's fp32 tile, added up by a second pass
+  if (a.part) {
+    if (!producer) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = c0 + 32 * j + (lane & 31);
+          if (col >= a.C) continue;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = row0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (row < a.M) a.part[((int64_t)kz * a.M + row) * a.C + col] = acc[i][j][v];
+          }
+        }
+    }
+    return;
+  }
 
   // ---- epilogue: fp32 -> bf16 (round to nearest even) ---------------------
   if (!producer) {
@@ -530,19 +562,55 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
   }
 }
 
+// out[m][c] = E(sum over z of part[z][m][c]), z in order; 8 columns per
+// thread (C % 8 == 0, rows of out 16-byte aligned).
+template <typename E>
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int ksplit, int M, int C,
+                                                       uint16_t* __restrict__ out, int64_t ld_out) {
+  const int c8 = C >> 3;
+  const int64_t n = (int64_t)M * c8;
+  const int64_t zs = (int64_t)M * C;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int m = (int)(i / c8), c = (int)(i - (int64_t)m * c8) * 8;
+    const float4* p = reinterpret_cast<const float4*>(part + (int64_t)m * C + c);
+    float4 lo = p[0], hi = p[1];
+    for (int z = 1; z < ksplit; ++z) {
+      const float4* q = reinterpret_cast<const float4*>(part + z * zs + (int64_t)m * C + c);
+      const float4 a = q[0], b = q[1];
+      lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
+      hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
+    }
+    *reinterpret_cast<uint4*>(out + (int64_t)m * ld_out + c) =
+        make_uint4(E::pack2(lo.x, lo.y), E::pack2(lo.z, lo.w), E::pack2(hi.x, hi.y), E::pack2(hi.z, hi.w));
+  }
+}
+
 thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
 
 template <bool NN>
-hipError_t launch(const GemmArgs& a, hipStream_t st) {
+hipError_t launch(GemmArgs a, hipStream_t st) {
   auto kern = a.f16 ? k_gemm_nf4<NN, F16> : k_gemm_nf4<NN, Bf16>;
   hipError_t e;
   hipEvent_t ev0, ev1;
   take_gemm_events(ev0, ev1);
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
-  dim3 grid((a.C + BN - 1) / BN, (a.M + BM - 1) / BM);
+  a.ksplit = a.part ? gemm_ksplit(a.M, a.C, a.R) : 1;
+  if (a.ksplit < 2) a.part = nullptr;
+  dim3 grid((a.C + BN - 1) / BN, (a.M + BM - 1) / BM, a.ksplit);
   hipLaunchKernelGGL(kern, grid, dim3(2 * kThreads), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.part) {
+    const int64_t n = (int64_t)a.M * (a.C / 8);
+    const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 2048));
+    if (a.f16)
+      hipLaunchKernelGGL(k_splitk_reduce<F16>, dim3(blocks), dim3(256), 0, st, a.part, a.ksplit, a.M, a.C, a.out,
+                         a.ld_out);
+    else
+      hipLaunchKernelGGL(k_splitk_reduce<Bf16>, dim3(blocks), dim3(256), 0, st, a.part, a.ksplit, a.M, a.C, a.out,
+                         a.ld_out);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
   return hipSuccess;
 }
@@ -558,6 +626,22 @@ void take_gemm_events(hipEvent_t& start, hipEvent_t& stop) {
 void time_next_gemm(hipEvent_t start, hipEvent_t stop) {
   if (start && stop) { t_ev_start = start; t_ev_stop = stop; }
   else { t_ev_start = t_ev_stop = nullptr; }
+}
+
+int gemm_ksplit(int64_t M, int64_t C, int64_t R) {
+  constexpr int64_t kCus = 256;  // MI355X compute units
+  const int64_t tiles = ((M + BM - 1) / BM) * ((C + BN - 1) / BN);
+  const int64_t nsteps = (R + 63) / 64;
+  if (tiles <= 0 || tiles * 2 > kCus || C % 8 != 0) return 1;
+  // at most 8 splits, a grid of at most one workgroup per compute unit, and
+  // at least 8 steps (512 reduction columns) per split
+  const int64_t ks = std::min<int64_t>(std::min<int64_t>(8, kCus / tiles), nsteps / 8);
+  return ks > 1 ? (int)ks : 1;
+}
+
+size_t gemm_part_bytes(int64_t M, int64_t C, int64_t R) {
+  const int ks = gemm_ksplit(M, C, R);
+  return ks > 1 ? (size_t)ks * (size_t)M * (size_t)C * 4u : 0;
 }
 
 hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st) { return launch<false>(a, st); }

@@ -24,6 +24,17 @@ struct GemmArgs {
   Nf4Consts nf4;
   DropMask drop;             // dX only: dropout of the adapter input (thr 0: none)
   bool f16;                  // element type of act, lora_*, out and the decoded W: fp16 (else bf16)
+  // Split reduction (set by the launcher): workgroup z of the grid takes
+  // reduction steps [z * spl, (z + 1) * spl) and stores its fp32 tile in
+  // part[z][M][C]; a second pass adds the ksplit tiles in order and rounds.
+  int ksplit;
+  float* part;
 };
+
+// Reduction splits for a product of M x C outputs over R: more than one only
+// when the grid of 256 x 128 tiles would leave at least half of the GPU's
+// 256 compute units idle.  The fp32 bytes the split needs (0 if unsplit).
+int gemm_ksplit(int64_t M, int64_t C, int64_t R);
+size_t gemm_part_bytes(int64_t M, int64_t C, int64_t R);
 
 }  // namespace qlora

@@ -162,7 +162,11 @@ int qlora_dequant(const qlora_nf4_weight *w, uint16_t *W_bf16, hipStream_t strea
  *          QLORA_OP_FWD, ...) bytes (always enough; may be NULL when that is
  *          0).  It holds U~ when U_out is NULL, followed by fp32 split-K
  *          partial sums of X A^T for large M * k_in; with U_out given the
- *          partials alone are needed.
+ *          partials alone are needed (with r == 0, nothing).  When the
+ *          output tiles of the main product are too few to fill the GPU,
+ *          the same region after U~ also holds fp32 partial products of a
+ *          reduction split; a workspace too small for them is not an error:
+ *          the product then runs unsplit (same result, same rounding).
  * r == 0 (or A/B NULL with r == 0) gives Y = X W_bf16^T.  M == 0 is a no-op.
  * The dequantized weight is never written to memory.  M <= 16 runs a
  * dedicated few-token kernel (bound by reading the packed weight); the
@@ -184,7 +188,12 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M,
  *              dX = dY W_bf16 + V~ A,  V~ = bf16(s * dY B)
  *   dA       device fp32 [r, k_in], written:  dA = V~^T X   (= s V^T X)
  *   dB       device fp32 [n_out, r], written: dB = dY^T U~  (= s dY^T U)
- *   ws       device workspace of qlora_workspace_bytes(QLORA_OP_BWD, ...).
+ *   ws       device workspace of qlora_workspace_bytes(QLORA_OP_BWD, ...),
+ *            16-byte aligned.  With r > 0 the part for U~, V~ and the token
+ *            reductions is required; the rest (fp32 partial products of a
+ *            reduction split of dX, used when its output tiles are too few
+ *            to fill the GPU) is optional, as in the forward: without it dX
+ *            is computed unsplit.  With r == 0 ws may be NULL.
  * Token reductions are deterministic (fixed-order partial sums, no float
  * atomics): repeated calls give bitwise-identical results.
  * r == 0 gives dX = dY W_bf16 and touches neither dA nor dB.  An empty
@@ -253,8 +262,10 @@ int qlora_linear_bwd_dropout(const qlora_nf4_weight *w, const uint16_t *X, const
 
 /* Workspace bytes needed by qlora_linear_fwd (op = QLORA_OP_FWD) or
  * qlora_linear_bwd (op = QLORA_OP_BWD) for these sizes: enough for any
- * U_out / U argument (U_out == NULL, U == NULL is the worst case).  Returns 0
- * for invalid arguments and when no workspace is needed (r == 0 or M == 0). */
+ * U_out / U argument (U_out == NULL, U == NULL is the worst case), including
+ * the optional room for a reduction split.  Returns 0 for invalid arguments
+ * and when no workspace is used (M == 0; r == 0 with output tiles enough to
+ * fill the GPU). */
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, int32_t r);
 
 /* Measurement aid.  The next fused-GEMM kernel launch made by the calling

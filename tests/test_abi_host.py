@@ -134,6 +134,12 @@ def test_workspace_sizes(L):
     assert b >= 2 * 2048 * 16 * 2 + 8 * 16 * 11008 * 4
     assert ws(2, 2048, 4096, 4096, 0) == 0
     assert ws(9, 1, 1, 64, 1) == 0
+    # few output tiles: optional room for a reduction split, also with r = 0
+    # (8 tiles of 256 x 128 over 32 steps of 64: 4 splits of fp32 130 x 1024)
+    assert ws(1, 130, 1024, 2048, 0) == 4 * 130 * 1024 * 4
+    assert ws(1, 130, 1024, 2048, 16) >= 130 * 16 * 2 + 4 * 130 * 1024 * 4
+    assert ws(2, 130, 1024, 2048, 0) == 2 * 130 * 2048 * 4  # dX: 16 tiles, 16 steps
+    assert ws(1, 16, 1024, 2048, 0) == 0  # few-token kernel: no split
     assert ws(1, 16, 64, 64, 65) == 0
 
 

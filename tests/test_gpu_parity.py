@@ -197,6 +197,7 @@ F16_SHAPES = [
     (257, 384, 512, 0, 0.0),
     (5, 1000, 384, 16, 32.0),     # few-token kernel
     (16, 4104, 320, 64, 128.0),   # few-token kernel, partial tile
+    (130, 1024, 2048, 16, 32.0),  # split reduction in both products
 ]
 
 
@@ -307,7 +308,12 @@ SHAPES = [
     (300, 520, 640, 64, 128.0),   # maximum rank
     (257, 384, 512, 0, 0.0),      # no adapter
     (33, 128, 128, 16, 0.0),      # alpha = 0
-    (130, 1024, 2048, 16, 32.0),  # several full tiles
+    (130, 1024, 2048, 16, 32.0),  # several full tiles; split reduction (fwd 4, dX 2)
+    (300, 2048, 2048, 16, 32.0),  # split reduction, 4 splits in both products
+    (50, 1000, 1088, 16, 32.0),   # 2 uneven forward splits (9 + 8 steps), ragged tails
+    (77, 136, 2240, 17, 5.0),     # forward split 4 ways, last split one step short
+    (40, 2200, 640, 16, 32.0),    # dX split 4 ways (9, 9, 9, 8 steps), ragged last step
+    (64, 264, 4096, 8, 16.0),     # forward split 8 ways over a partial column tile
 ]
 
 
@@ -409,6 +415,35 @@ def test_backward_parity(M, N, K, r, alpha):
         assert torch.equal(dA, dA2) and torch.equal(dB, dB2)
 
 
+def test_split_reduction_room_is_optional():
+    """Few output tiles: with room in the workspace the products split the
+    reduction; without it (r = 0 needs none) they run unsplit.  Both match
+    the oracle."""
+    _need_gpu()
+    M, N, K, r, alpha = 130, 1024, 2048, 0, 0.0
+    assert qlora.workspace_bytes(qlora.QLORA_OP_FWD, M, N, K, r) > 0
+    assert qlora.workspace_bytes(qlora.QLORA_OP_BWD, M, N, K, r) > 0
+    d, q, wb = _case(M, N, K, r, seed=5)
+    w = gpu_quantize(d["W"])
+    X, _, _, dY = _dev_inputs(d, r)
+    Ys, _ = qlora.linear_fwd(w, X, None, None, r, alpha)
+    dXs, _, _ = qlora.linear_bwd(w, X, dY, None, None, r, alpha)
+    L = qlora.lib()
+    cw = w._c()
+    Yu = torch.empty_like(Ys)
+    dXu = torch.empty_like(dXs)
+    assert L.qlora_linear_fwd(ctypes.byref(cw), X.data_ptr(), M, None, None, 0, 0.0, Yu.data_ptr(), None,
+                              None, 0, qlora._stream()) == 0
+    assert L.qlora_linear_bwd(ctypes.byref(cw), X.data_ptr(), dY.data_ptr(), M, None, None, 0, 0.0, None,
+                              dXu.data_ptr(), None, None, None, 0, qlora._stream()) == 0
+    torch.cuda.synchronize()
+    Yr, _ = oracle.linear_fwd(wb, d["X"], d["A"], d["B"], alpha, r)
+    dXr, _, _ = oracle.linear_bwd(wb, d["X"], d["dY"], d["A"], d["B"], alpha, r)
+    for got, ref, what in ((Ys, Yr, "Y split"), (Yu, Yr, "Y unsplit"), (dXs, dXr, "dX split"),
+                           (dXu, dXr, "dX unsplit")):
+        check_close(f64(got), ref, what)
+
+
 def test_backward_deterministic_and_weight_untouched():
     _need_gpu()
     d, q, wb = _case(513, 1024, 768, 16, seed=5)
@@ -473,6 +508,7 @@ DROP_SHAPES = [
     (5, 1000, 384, 16, 32.0, 0.05),
     (17, 136, 320, 17, 5.0, 0.3),
     (257, 384, 512, 8, 16.0, 0.5),
+    (300, 2048, 2048, 16, 32.0, 0.1),  # dX with the reduction split 4 ways
 ]
 
 
