@@ -54,6 +54,7 @@ class HipEvents:
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     # hipEventDisableSystemFence: the marker takes its timestamp without the
     # system-scope release (an L2 write-back) that a default event adds after
@@ -277,6 +278,11 @@ def main():
             "frac_fp16_mfma_peak": round(step_flops / (ms_h * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del h
 
+        # each linear alone: fwd + bwd call pairs timed one by one (10 warmup,
+        # 50 timed), median and p10 / p90; the layer figure from the sum of
+        # the medians, beside the back-to-back step above
+        secondary["per_linear_7b"] = bench_per_linear(lins, qlora, r, alpha, M, evs)
+
         # the 3B layer (2048 tokens) and the 8B layer (8192 tokens): the same
         # path at the pages' other training shapes
         for wl in ("3b", "8b"):
@@ -331,9 +337,49 @@ def main():
         "roofline": roofline,
         "gemm_kernels": other,
         "cpu_baseline": cpu,
+        "device": device_info(torch, dev),
         "secondary": secondary,
     }
     print(json.dumps(out))
+
+
+def bench_per_linear(lins, qlora, r, alpha, M, evs, warmup=10, reps=50):
+    """fwd + bwd of each linear of the layer timed per call with HIP events
+    on the launch stream: median, p10 and p90 in microseconds."""
+    import torch
+    out = {}
+    tot_fl, tot_ms = 0.0, 0.0
+    for e in lins:
+        def call():
+            qlora.linear_fwd(e["w"], e["X"], e["A"], e["B"], r, alpha, Y=e["Y"], U=e["U"], ws=e["ws_fwd"])
+            qlora.linear_bwd(e["w"], e["X"], e["dY"], e["A"], e["B"], r, alpha, e["U"],
+                             dX=e["dX"], dA=e["dA"], dB=e["dB"], ws=e["ws"])
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        stream = ctypes.c_void_p(qlora._stream())  # the stream the calls launch on
+        ev = [(evs.create(), evs.create()) for _ in range(reps)]
+        for a, b in ev:
+            if evs.hip.hipEventRecord(a, stream) != 0:
+                raise RuntimeError("hipEventRecord failed")
+            call()
+            if evs.hip.hipEventRecord(b, stream) != 0:
+                raise RuntimeError("hipEventRecord failed")
+        us = np.array([1e3 * evs.ms(a, b) for a, b in ev])
+        for a, b in ev:
+            evs.destroy(a)
+            evs.destroy(b)
+        med = float(np.median(us))
+        fl = flops_linear(M, e["n"], e["k"], r)
+        out[e["name"]] = {"shape": f"{M}x{e['n']}x{e['k']}", "median_us": round(med, 2),
+                          "p10_us": round(float(np.percentile(us, 10)), 2),
+                          "p90_us": round(float(np.percentile(us, 90)), 2),
+                          "TFLOP/s": round(fl / (med * 1e-6) / 1e12, 2)}
+        tot_fl += fl
+        tot_ms += med * 1e-3
+    out["layer_sum_of_medians"] = {"ms": round(tot_ms, 4), "TFLOP/s": round(tot_fl / (tot_ms * 1e-3) / 1e12, 2),
+                                   "frac_bf16_mfma_peak": round(tot_fl / (tot_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    return out
 
 
 def bench_secondary(torch, qlora, synth, dev, evs, reps=10):
@@ -536,7 +582,24 @@ def bench_cpu(host, r, alpha, m_sample=2048, min_seconds=10.0):
     return {"value": round(fl / sec / 1e12, 4), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"all 7 linears of the 7B layer at {m_sample} of 2048 tokens: oracle dequant + "
                       f"fwd + bwd in fp64 numpy, {passes} pass(es) in {sec:.1f} s",
-            "seconds": round(sec, 2), "cpu": platform.processor() or platform.machine()}
+            "seconds": round(sec, 2), "cpu": cpu_model()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def device_info(torch, dev):
+    p = torch.cuda.get_device_properties(dev)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2 ** 30, 1)}
 
 
 if __name__ == "__main__":
