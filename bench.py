@@ -287,6 +287,10 @@ def main():
         # path at the pages' other training shapes
         for wl in ("3b", "8b"):
             secondary[f"layer_{wl}"] = bench_layer(torch, qlora, synth, dev, wl, max(3, args.steps // 4))
+        # the 7B layer at 512 tokens: grids of 64-176 tiles, where the fused
+        # GEMMs split their reduction
+        secondary["layer_7b_512_tokens"] = bench_layer(torch, qlora, synth, dev, "7b", max(3, args.steps // 2),
+                                                       tokens=512)
 
         # context, not a product path: the same layer's 14 products as plain
         # dense bf16 GEMMs in torch.matmul (hipBLASLt) on a bf16 copy of each
@@ -473,10 +477,10 @@ def bench_secondary(torch, qlora, synth, dev, evs, reps=10):
     return res
 
 
-def bench_layer(torch, qlora, synth, dev, wl, steps):
-    """fwd+bwd of the 7 linears of a decoder layer at its token count on
-    device-generated N(0, 0.02^2) weights and N(0, 1) inputs."""
-    M, r, alpha = synth.TOKENS[wl], synth.RANK[wl], synth.ALPHA[wl]
+def bench_layer(torch, qlora, synth, dev, wl, steps, tokens=None):
+    """fwd+bwd of the 7 linears of a decoder layer at its token count (or
+    `tokens`) on device-generated N(0, 0.02^2) weights and N(0, 1) inputs."""
+    M, r, alpha = tokens or synth.TOKENS[wl], synth.RANK[wl], synth.ALPHA[wl]
     g = torch.Generator(device=dev)
     g.manual_seed(1234)
     lins = []
