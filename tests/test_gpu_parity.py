@@ -314,6 +314,8 @@ SHAPES = [
     (77, 136, 2240, 17, 5.0),     # forward split 4 ways, last split one step short
     (40, 2200, 640, 16, 32.0),    # dX split 4 ways (9, 9, 9, 8 steps), ragged last step
     (64, 264, 4096, 8, 16.0),     # forward split 8 ways over a partial column tile
+    (16, 2048, 1024, 16, 32.0),   # few-token forward; dX (GEMM) split 4 ways at 16 tokens
+    (1, 1024, 2048, 8, 16.0),     # one token: dX split 2 ways over a single row
 ]
 
 
