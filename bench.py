@@ -447,31 +447,31 @@ def bench_secondary(torch, qlora, synth, dev, evs, reps=10):
                                           "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
             del Am, Bm
         del out
-        if idx == 0:
-            rr, alpha = synth.RANK["70b"], synth.ALPHA["70b"]
-            for m in (1, 4, 16):
-                d = synth.linear_inputs(lin.n_out, lin.k_in, m, rr, synth.rng_for("70b", 10 + m),
-                                        with_grad=False)
-                X = torch.from_numpy(d["X"].view(np.int16)).view(torch.bfloat16).to(dev)
-                A = torch.from_numpy(d["A"].view(np.int16)).view(torch.bfloat16).to(dev)
-                B = torch.from_numpy(d["B"].view(np.int16)).view(torch.bfloat16).to(dev)
-                Y = torch.empty((m, lin.n_out), dtype=torch.bfloat16, device=dev)
-                U = torch.empty((m, rr), dtype=torch.bfloat16, device=dev)
-                ws = qlora.new_workspace(qlora.QLORA_OP_FWD, m, lin.n_out, lin.k_in, rr, dev)
-                for c in copies:
-                    qlora.linear_fwd(c, X, A, B, rr, alpha, Y=Y, U=U, ws=ws)
-                torch.cuda.synchronize()
-                a.record()
-                for i in range(reps * 3):
-                    qlora.linear_fwd(copies[i % 3], X, A, B, rr, alpha, Y=Y, U=U, ws=ws)
-                b.record()
-                torch.cuda.synchronize()
-                us = 1e3 * a.elapsed_time(b) / (reps * 3)
-                byts = (nw * PACKED_B_PER_W + 2 * m * (lin.k_in + lin.n_out)
-                        + 2 * rr * (lin.k_in + lin.n_out) + 2 * m * rr)
-                gbs = byts / (us * 1e-6) / 1e9
-                res[f"fwd_70b_gate_M{m}"] = {"us": round(us, 2), "GB/s": round(gbs, 1),
-                                             "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        # few-token forward on both weights
+        rr, alpha = synth.RANK["70b"], synth.ALPHA["70b"]
+        for m in (1, 4, 16):
+            d = synth.linear_inputs(lin.n_out, lin.k_in, m, rr, synth.rng_for("70b", 10 + m),
+                                    with_grad=False)
+            X = torch.from_numpy(d["X"].view(np.int16)).view(torch.bfloat16).to(dev)
+            A = torch.from_numpy(d["A"].view(np.int16)).view(torch.bfloat16).to(dev)
+            B = torch.from_numpy(d["B"].view(np.int16)).view(torch.bfloat16).to(dev)
+            Y = torch.empty((m, lin.n_out), dtype=torch.bfloat16, device=dev)
+            U = torch.empty((m, rr), dtype=torch.bfloat16, device=dev)
+            ws = qlora.new_workspace(qlora.QLORA_OP_FWD, m, lin.n_out, lin.k_in, rr, dev)
+            for c in copies:
+                qlora.linear_fwd(c, X, A, B, rr, alpha, Y=Y, U=U, ws=ws)
+            torch.cuda.synchronize()
+            a.record()
+            for i in range(reps * 3):
+                qlora.linear_fwd(copies[i % 3], X, A, B, rr, alpha, Y=Y, U=U, ws=ws)
+            b.record()
+            torch.cuda.synchronize()
+            us = 1e3 * a.elapsed_time(b) / (reps * 3)
+            byts = (nw * PACKED_B_PER_W + 2 * m * (lin.k_in + lin.n_out)
+                    + 2 * rr * (lin.k_in + lin.n_out) + 2 * m * rr)
+            gbs = byts / (us * 1e-6) / 1e9
+            res[f"fwd_70b_{lin.name}_M{m}"] = {"us": round(us, 2), "GB/s": round(gbs, 1),
+                                               "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
         del copies, w0
         torch.cuda.empty_cache()
     return res
