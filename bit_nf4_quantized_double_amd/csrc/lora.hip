@@ -214,6 +214,36 @@ __global__ __launch_bounds__(256) void k_rowdot_finalize(const float* __restrict
   rowdot_finalize_body<E>(part, nsplit, n, scale, out, blockIdx.x, gridDim.x);
 }
 
+// The same sum for few outputs and many splits: 8 lanes per output, lane t
+// adding splits t, t + 8, t + 16, ... in order, then the 8 sums combined in a
+// fixed butterfly; lane t == 0 stores.  A handful of memory latencies
+// instead of nsplit / 8 of them.
+template <typename E>
+__global__ __launch_bounds__(256) void k_rowdot_finalize8(const float* __restrict__ part, int nsplit, int64_t n,
+                                                          float scale, uint16_t* __restrict__ out) {
+  const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i = gi >> 3;
+  const int t = (int)(gi & 7);
+  const bool ok = i < n;
+  float s = 0.f;
+  int k = t;
+  for (; k + 56 < nsplit; k += 64) {  // 8 loads in flight
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = ok ? part[(int64_t)(k + 8 * j) * n + i] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += v[j];
+  }
+  for (; k < nsplit; k += 8) s += ok ? part[(int64_t)k * n + i] : 0.f;
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 4);
+  if (ok && t == 0) {
+    const uint32_t pk = E::pack2(scale * s, 0.f);
+    out[i] = (uint16_t)(pk & 0xFFFFu);
+  }
+}
+
 // ---------------------------------------------------------------- coldot ----
 // Workgroup: 128 columns x one chunk of rows; the 4 waves take interleaved
 // 32-row steps and are summed in LDS in a fixed order.  Each lane loads an
@@ -399,6 +429,11 @@ hipError_t rowdot_dispatch(const uint16_t* in, int M, int Kd, const uint16_t* wt
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
   const int64_t n = (int64_t)M * r;
+  if (n <= 4096 && nsplit >= 16) {
+    hipLaunchKernelGGL(k_rowdot_finalize8<E>, dim3((int)((8 * n + 255) / 256)), dim3(256), 0, st, part, nsplit, n,
+                       scale, out);
+    return hipGetLastError();
+  }
   const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 2048));
   hipLaunchKernelGGL(k_rowdot_finalize<E>, dim3(blocks), dim3(256), 0, st, part, nsplit, n, scale, out);
   return hipGetLastError();
