@@ -188,7 +188,8 @@ size_t qlora_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, int
     // [U~][U~ partials | split-reduction tiles of the main product]
     const size_t u = r > 0 ? round_up((size_t)M * r * 2) : 0;
     const size_t upart = r > 0 ? round_up(qlora::rowdot_part_bytes(M, k_in, r)) : 0;
-    const size_t gpart = M > qlora::skinny_max_tokens() ? round_up(qlora::gemm_part_bytes(M, n_out, k_in)) : 0;
+    const size_t gpart = round_up(M > qlora::skinny_max_tokens() ? qlora::gemm_part_bytes(M, n_out, k_in)
+                                                                  : qlora::skinny_part_bytes(M, n_out, k_in));
     return u + std::max(upart, gpart);
   }
   if (op == QLORA_OP_BWD) return bwd_layout(M, n_out, k_in, r).total;
@@ -300,6 +301,11 @@ static int linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t
     k.M = (int)M; k.N = (int)w->n_out; k.K = (int)w->k_in; k.r = r;
     k.nf4 = qlora::nf4_consts();
     k.f16 = f16;
+    // split partial sums after U~ (the U~ partials are consumed by then);
+    // without room the kernel runs unsplit
+    const size_t kbytes = qlora::skinny_part_bytes(M, w->n_out, w->k_in);
+    if (kbytes && ws && aligned16(ws) && ws_bytes >= ubytes + kbytes)
+      k.part = reinterpret_cast<float*>(static_cast<char*>(ws) + ubytes);
     e = qlora::launch_skinny_fwd(k, stream);
     return e == hipSuccess ? QLORA_OK : hip_fail(e, "few-token forward launch");
   }

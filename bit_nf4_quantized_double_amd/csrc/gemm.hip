@@ -600,17 +600,8 @@ hipError_t launch(GemmArgs a, hipStream_t st) {
   hipLaunchKernelGGL(kern, grid, dim3(2 * kThreads), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.part) {
-    const int64_t n = (int64_t)a.M * (a.C / 8);
-    const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 2048));
-    if (a.f16)
-      hipLaunchKernelGGL(k_splitk_reduce<F16>, dim3(blocks), dim3(256), 0, st, a.part, a.ksplit, a.M, a.C, a.out,
-                         a.ld_out);
-    else
-      hipLaunchKernelGGL(k_splitk_reduce<Bf16>, dim3(blocks), dim3(256), 0, st, a.part, a.ksplit, a.M, a.C, a.out,
-                         a.ld_out);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  if (a.part && (e = launch_splitk_reduce(a.part, a.ksplit, a.M, a.C, a.out, a.ld_out, a.f16, st)) != hipSuccess)
+    return e;
   if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
   return hipSuccess;
 }
@@ -642,6 +633,18 @@ int gemm_ksplit(int64_t M, int64_t C, int64_t R) {
 size_t gemm_part_bytes(int64_t M, int64_t C, int64_t R) {
   const int ks = gemm_ksplit(M, C, R);
   return ks > 1 ? (size_t)ks * (size_t)M * (size_t)C * 4u : 0;
+}
+
+// out = E(sum over z of part[z]) for an fp32 [ksplit][M][C] partial buffer
+// (C % 8 == 0, out rows 16-byte aligned); also the second pass of the
+// few-token kernel's reduction split.
+hipError_t launch_splitk_reduce(const float* part, int ksplit, int M, int C, uint16_t* out, int64_t ld_out, bool f16,
+                                hipStream_t st) {
+  const int64_t n = (int64_t)M * (C / 8);
+  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 2048));
+  if (f16) hipLaunchKernelGGL(k_splitk_reduce<F16>, dim3(blocks), dim3(256), 0, st, part, ksplit, M, C, out, ld_out);
+  else hipLaunchKernelGGL(k_splitk_reduce<Bf16>, dim3(blocks), dim3(256), 0, st, part, ksplit, M, C, out, ld_out);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st) { return launch<false>(a, st); }

@@ -37,4 +37,9 @@ struct GemmArgs {
 int gemm_ksplit(int64_t M, int64_t C, int64_t R);
 size_t gemm_part_bytes(int64_t M, int64_t C, int64_t R);
 
+// out = E(sum over z of part[z]) for fp32 partial sums [ksplit][M][C], z in
+// order (C % 8 == 0, rows of out 16-byte aligned).
+hipError_t launch_splitk_reduce(const float* part, int ksplit, int M, int C, uint16_t* out, int64_t ld_out, bool f16,
+                                hipStream_t st);
+
 }  // namespace qlora

@@ -34,6 +34,8 @@
 namespace qlora {
 
 void take_gemm_events(hipEvent_t& start, hipEvent_t& stop);  // gemm.hip
+hipError_t launch_splitk_reduce(const float* part, int ksplit, int M, int C, uint16_t* out, int64_t ld_out, bool f16,
+                                hipStream_t st);  // gemm.hip
 
 namespace {
 
@@ -63,6 +65,11 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
   const int wa = wave >> a.nwk_log2, wb = wave & (nwk - 1);
   const int row = lane & 15, g = lane >> 4;
   const int nch = (a.K + 127) >> 7;
+  // reduction split across workgroups: grid row kz takes chunks
+  // [cbase, cbase + nchl) of the nch
+  const int kz = blockIdx.y;
+  const int cbase = kz * a.kchunks;
+  const int nchl = min(a.kchunks, nch - cbase);
 
   const uint32_t nw = (uint32_t)a.N * (uint32_t)a.K;  // < 2^32 (checked on the host)
   SkSrcs src;
@@ -134,10 +141,11 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
   // the end of the codes (reads zeros, or -- if the index wraps -- some other
   // row's finite weights, into an output row that is never stored), and
   // columns past k_in (the tail of the last chunk, padding chunks) read the
-  // next row's finite weights, which meet X == 0 there (X loads are range
-  // checked).  Either way nothing reaches a stored output.
+  // next row's finite weights, and padding chunks of a split the next
+  // split's, which meet X == 0 there (X loads are range checked).  Either way
+  // nothing reaches a stored output.
   auto load = [&](int t, int i) {
-    const int c = wb + (i << a.nwk_log2);
+    const int c = cbase + wb + (i << a.nwk_log2);
     const uint32_t e = e0 + (uint32_t)t * 16u * (uint32_t)a.K + (uint32_t)c * 128u;
     SkSeg s;
     s.code = buf_load16(src.codes, e >> 1);
@@ -154,8 +162,8 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
   const bool xrow = row < a.M;
   const uint32_t xoff0 = (uint32_t)row * (uint32_t)a.K * 2u + 64u * (uint32_t)g;
   auto load_x = [&](int i, uint4 xf[4]) {
-    const int c = wb + (i << a.nwk_log2);
-    const bool ok = xrow && (c < nch) && (c * 128 + 32 * g < a.K);
+    const int cl = wb + (i << a.nwk_log2), c = cbase + cl;
+    const bool ok = xrow && (cl < nchl) && (c * 128 + 32 * g < a.K);
     const uint32_t o = xoff0 + (uint32_t)c * 256u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) xf[j] = buf_load16(src.X, ok ? o + 16u * j : kOOB);
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
     load_x(i + 1, xn);
     float sc[TPW];
     if (SL) {
-      const int c = wb + (i << a.nwk_log2);
+      const int c = cbase + wb + (i << a.nwk_log2);
 #pragma unroll
       for (int t = 0; t < TPW; ++t) sc[t] = lds_scale(t, c);
     }
@@ -232,7 +240,7 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
 
   // adapter term U~ B^T, once per output tile (by the b == 0 wave): W-side
   // operand B[n][j], token-side operand U~[m][j], 32 ranks per MFMA
-  if (wb == 0 && a.r > 0) {
+  if (wb == 0 && a.r > 0 && kz == 0) {
     const bool vec = (a.r & 7) == 0;
     for (int j0 = 0; j0 < a.r; j0 += 32) {
       const int j = j0 + 8 * g;
@@ -289,7 +297,9 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
     // fragment element v of lane l: W row 4 (l >> 4) + v of the tile, token l & 15
     const int m = l & 15;
     const int n = (blockIdx.x * a.tiles + tt) * 16 + 4 * (l >> 4);
-    if (m < a.M && n < a.N) {  // n_out % 8 == 0: the 4 rows are all in range
+    if (m < a.M && n < a.N && a.part) {  // this split's fp32 partial sums
+      *reinterpret_cast<float4*>(a.part + ((int64_t)kz * a.M + m) * a.N + n) = s;
+    } else if (m < a.M && n < a.N) {  // n_out % 8 == 0: the 4 rows are all in range
       uint2 o;
       o.x = E::pack2(s.x, s.y);
       o.y = E::pack2(s.z, s.w);
@@ -299,7 +309,7 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
 }
 
 template <int TPW, int RD>
-hipError_t sk_launch(const SkinnyArgs& a, int grid, size_t lds, bool sl, hipStream_t st) {
+hipError_t sk_launch(const SkinnyArgs& a, dim3 grid, size_t lds, bool sl, hipStream_t st) {
   hipEvent_t ev0, ev1;
   take_gemm_events(ev0, ev1);
   hipError_t e;
@@ -312,6 +322,7 @@ hipError_t sk_launch(const SkinnyArgs& a, int grid, size_t lds, bool sl, hipStre
     else hipLaunchKernelGGL((k_skinny_fwd<TPW, RD, false, Bf16>), dim3(grid), dim3(kSkThreads), lds, st, a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.part && (e = launch_splitk_reduce(a.part, (int)grid.y, a.M, a.N, a.Y, a.N, a.f16, st)) != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
   return hipSuccess;
 }
@@ -326,6 +337,26 @@ int skinny_max_tokens() { return 16; }
 // tiles, each split over nwk = 8 / nwt waves along the reduction.  The
 // prefetch depth RD (chunks ahead) keeps about 8 code loads in flight per
 // lane.  LDS: tiles * nwk KB <= 64 KB.
+// Reduction split across workgroups: with 8 tokens or more, a weight whose
+// tiles number at most 2 per compute unit (few outputs, a long reduction)
+// would have every workgroup read all of X for those 2 tiles.  Instead a
+// workgroup takes 8 tiles over 1 / ks of the reduction (at least 16 chunks
+// of 128), when that still gives a workgroup per compute unit; the ks fp32
+// partial sums are added in split order by a second pass.
+int skinny_ksplit(int64_t M, int64_t N, int64_t K) {
+  constexpr int64_t kCus = 256;  // MI355X compute units
+  const int64_t ntiles = (N + 15) / 16, nch = (K + 127) / 128;
+  if (M < 8 || M > 16 || ntiles == 0 || (ntiles + kCus - 1) / kCus > 2) return 1;
+  const int64_t groups = (ntiles + 7) / 8;
+  const int64_t ks = std::min(kCus / groups, nch / 16);
+  return ks > 1 && groups * ks >= kCus ? (int)ks : 1;
+}
+
+size_t skinny_part_bytes(int64_t M, int64_t N, int64_t K) {
+  const int ks = skinny_ksplit(M, N, K);
+  return ks > 1 ? (size_t)ks * (size_t)M * (size_t)N * 4u : 0;
+}
+
 hipError_t launch_skinny_fwd(SkinnyArgs a, hipStream_t st) {
   const int ntiles = (a.N + 15) / 16;
   const int nch = (a.K + 127) / 128;
@@ -337,7 +368,10 @@ hipError_t launch_skinny_fwd(SkinnyArgs a, hipStream_t st) {
       if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) num_cu = v;
     }
   }
-  const int tpg = std::max(1, (ntiles + num_cu - 1) / num_cu);
+  const int ks = a.part ? skinny_ksplit(a.M, a.N, a.K) : 1;
+  if (ks < 2) a.part = nullptr;
+  a.kchunks = (nch + ks - 1) / ks;
+  const int tpg = ks > 1 ? 8 : std::max(1, (ntiles + num_cu - 1) / num_cu);
   int tpw = std::min(tpg, 8);
   int nwt = 1;
   while (nwt * tpw < tpg && nwt < kSkWaves) nwt *= 2;
@@ -345,7 +379,7 @@ hipError_t launch_skinny_fwd(SkinnyArgs a, hipStream_t st) {
   int nwk_log2 = 0;
   while ((nwt << (nwk_log2 + 1)) <= kSkWaves) ++nwk_log2;
   const int nwk = 1 << nwk_log2;
-  int nci = (nch + nwk - 1) / nwk;
+  int nci = (a.kchunks + nwk - 1) / nwk;
   int rd = tpw >= 5 ? 1 : (tpw >= 3 ? 2 : (tpw == 2 ? 4 : 8));
   while (rd > 2 && nci % rd) rd /= 2;
   const int unroll = std::max(rd, 2);
@@ -353,7 +387,7 @@ hipError_t launch_skinny_fwd(SkinnyArgs a, hipStream_t st) {
   a.tiles = nwt * tpw;
   a.nwk_log2 = nwk_log2;
   a.nci = nci;
-  const int grid = (ntiles + a.tiles - 1) / a.tiles;
+  const dim3 grid((ntiles + a.tiles - 1) / a.tiles, ks);
   const size_t red = (size_t)a.tiles * nwk * 64 * sizeof(float4);
   // staged scales: q8 of 16 * tiles rows plus the s2 groups they span
   const size_t qbytes = (size_t)a.tiles * 16 * (size_t)(a.K / 64);

@@ -163,10 +163,13 @@ int qlora_dequant(const qlora_nf4_weight *w, uint16_t *W_bf16, hipStream_t strea
  *          0).  It holds U~ when U_out is NULL, followed by fp32 split-K
  *          partial sums of X A^T for large M * k_in; with U_out given the
  *          partials alone are needed (with r == 0, nothing).  When the
- *          output tiles of the main product are too few to fill the GPU,
- *          the same region after U~ also holds fp32 partial products of a
- *          reduction split; a workspace too small for them is not an error:
- *          the product then runs unsplit (same result, same rounding).
+ *          output tiles of the main product are too few to fill the GPU
+ *          (or, with 8 to 16 tokens, the few-token kernel has at most 2
+ *          output tiles per compute unit over a long reduction), the same
+ *          region after U~ also holds fp32 partial products of a reduction
+ *          split; a workspace too small for them is not an error: the
+ *          product then runs unsplit (same contract; only the fp32
+ *          summation order differs).
  * r == 0 (or A/B NULL with r == 0) gives Y = X W_bf16^T.  M == 0 is a no-op.
  * The dequantized weight is never written to memory.  M <= 16 runs a
  * dedicated few-token kernel (bound by reading the packed weight); the

@@ -140,6 +140,9 @@ def test_workspace_sizes(L):
     assert ws(1, 130, 1024, 2048, 16) >= 130 * 16 * 2 + 4 * 130 * 1024 * 4
     assert ws(2, 130, 1024, 2048, 0) == 2 * 130 * 2048 * 4  # dX: 16 tiles, 16 steps
     assert ws(1, 16, 1024, 2048, 0) == 0  # few-token kernel: no split
+    # few-token kernel over a long reduction: 4 splits of fp32 16 x 8192
+    assert ws(1, 16, 8192, 28672, 0) == 4 * 16 * 8192 * 4
+    assert ws(1, 4, 8192, 28672, 0) == 0  # under 8 tokens: unsplit
     assert ws(1, 16, 64, 64, 65) == 0
 
 

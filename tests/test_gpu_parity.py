@@ -373,6 +373,8 @@ FEW_SHAPES = [
     (1, 8192, 8192, 16, 32.0),
     (4, 520, 640, 17, 34.0),
     (9, 1032, 960, 1, 2.0),
+    (16, 8192, 8192, 16, 32.0),   # reduction split 4 ways across workgroups (8 tiles each)
+    (9, 8192, 8256, 17, 34.0),    # split 17 + 17 + 17 + 14 chunks, half a chunk at the end
 ]
 
 
