@@ -198,6 +198,7 @@ F16_SHAPES = [
     (5, 1000, 384, 16, 32.0),     # few-token kernel
     (16, 4104, 320, 64, 128.0),   # few-token kernel, partial tile
     (130, 1024, 2048, 16, 32.0),  # split reduction in both products
+    (16, 8192, 8192, 16, 32.0),   # few-token split across workgroups; dX split 4 ways
 ]
 
 
@@ -513,6 +514,7 @@ DROP_SHAPES = [
     (17, 136, 320, 17, 5.0, 0.3),
     (257, 384, 512, 8, 16.0, 0.5),
     (300, 2048, 2048, 16, 32.0, 0.1),  # dX with the reduction split 4 ways
+    (9, 8192, 8256, 17, 34.0, 0.1),    # few-token forward split across workgroups
 ]
 
 
