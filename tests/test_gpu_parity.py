@@ -874,3 +874,52 @@ def test_quantize_bf16_input_bit_exact():
     w = qlora.quantize(dev_bf16(Wb).reshape(d["W"].shape))
     torch.cuda.synchronize()
     check_codec_exact(w, q)
+
+
+# ------------------------------------------------------------ HIP graphs ----
+
+@pytest.mark.parametrize("M,N,K,r,alpha", [(300, 2048, 2048, 16, 32.0), (16, 8192, 8192, 16, 32.0)])
+def test_graph_capture_replays_match_eager(M, N, K, r, alpha):
+    """The library allocates nothing and issues only kernels, so a forward +
+    backward can be captured in a HIP graph.  Every replay (with eager work
+    and synchronisation in between) must reproduce the eager results bit for
+    bit, the split-reduction passes included."""
+    _need_gpu()
+    d, q, wb = _case(M, N, K, r, seed=M + N + K)
+    w = gpu_quantize(d["W"])
+    X, A, B, dY = _dev_inputs(d, r)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    U = torch.empty((M, r), dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    dA = torch.empty((r, K), dtype=torch.float32, device="cuda")
+    dB = torch.empty((N, r), dtype=torch.float32, device="cuda")
+    wsf = qlora.new_workspace(qlora.QLORA_OP_FWD, M, N, K, r, "cuda")
+    wsb = qlora.new_workspace(qlora.QLORA_OP_BWD, M, N, K, r, "cuda")
+
+    def run():
+        qlora.linear_fwd(w, X, A, B, r, alpha, Y=Y, U=U, ws=wsf)
+        qlora.linear_bwd(w, X, dY, A, B, r, alpha, U, dX=dX, dA=dA, dB=dB, ws=wsb)
+
+    run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (Y, U, dX, dA, dB)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (Y, U, dX, dA, dB):
+            t.fill_(float(rep + 1))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want, what in zip((Y, U, dX, dA, dB), ref, ("Y", "U~", "dX", "dA", "dB")):
+            assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got,
+                               want.view(torch.int16) if want.dtype == torch.bfloat16 else want), (rep, what)
+    check_close(f64(ref[0]), oracle.linear_fwd(wb, d["X"], d["A"], d["B"], alpha, r)[0], "Y (graph case)")
