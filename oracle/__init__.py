@@ -55,7 +55,7 @@ from .nf4_dq import (  # noqa: F401
     bits_per_weight,
     quantize_groups,
 )
-from .qlora_linear import lora_scale, linear_fwd, linear_bwd  # noqa: F401
+from .qlora_linear import lora_scale, linear_fwd, linear_bwd, adapter_grads  # noqa: F401
 from .merge import bf16_bits_from_f64, merge, requantize, requant_drift  # noqa: F401
 from .dropout import (  # noqa: F401
     philox4x32_10,

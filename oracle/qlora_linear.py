@@ -69,14 +69,28 @@ def linear_fwd(W_bf, X, A, B, alpha: float, r: int):
     return Y, U
 
 
-def linear_bwd(W_bf, X, dY, A, B, alpha: float, r: int):
-    """Returns (dX fp64 [M, K], dA fp64 [r, K], dB fp64 [N, r])."""
-    W = _f64(W_bf)
+def adapter_grads(X, dY, A, B, alpha: float, r: int):
+    """The adapter's gradients alone: (dA fp64 [r, K], dB fp64 [N, r]).
+
+    dA = s V^T X and dB = s dY^T U with V = dY B and U = X A^T; they need no
+    weight, so a test can take them over every token of a large layer
+    without forming dX.  ``linear_bwd`` returns exactly these.
+    """
     Xf, dYf, Af, Bf = _f64(X), _f64(dY), _f64(A), _f64(B)
     s = lora_scale(alpha, r)
     U = Xf @ Af.T
     V = dYf @ Bf
-    dX = dYf @ W + s * (V @ Af)
     dA = s * (V.T @ Xf)
     dB = s * (dYf.T @ U)
+    return dA, dB
+
+
+def linear_bwd(W_bf, X, dY, A, B, alpha: float, r: int):
+    """Returns (dX fp64 [M, K], dA fp64 [r, K], dB fp64 [N, r])."""
+    W = _f64(W_bf)
+    dYf, Af, Bf = _f64(dY), _f64(A), _f64(B)
+    s = lora_scale(alpha, r)
+    V = dYf @ Bf
+    dX = dYf @ W + s * (V @ Af)
+    dA, dB = adapter_grads(X, dY, A, B, alpha, r)
     return dX, dA, dB

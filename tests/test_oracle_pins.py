@@ -430,3 +430,21 @@ def test_quantize_groups_equals_full_quantize():
         assert np.array_equal(part[g]["codes"], full["codes"][b0 * 32:b1 * 32])
         assert np.array_equal(part[g]["absmax_q8"], full["absmax_q8"][b0:b1])
         assert part[g]["absmax_scale"][0] == full["absmax_scale"][g]
+
+
+def test_adapter_grads_are_the_backward_ones():
+    """``adapter_grads`` is the dA, dB that ``linear_bwd`` returns (pinned
+    there by finite differences), and the backward rows of a token subset
+    are the same rows of the full backward (each row of dX depends on its
+    own token only), which the full-size GPU tests rely on."""
+    W, X, A, B, dY = _tiny(M=6, N=8, K=128, r=3, seed=9)
+    alpha, r = 6.0, 3
+    dX, dA, dB = oracle.linear_bwd(W, X, dY, A, B, alpha, r)
+    gA, gB = oracle.adapter_grads(X, dY, A, B, alpha, r)
+    assert np.array_equal(gA, dA) and np.array_equal(gB, dB)
+    rows = np.array([1, 4])
+    dXs, _, _ = oracle.linear_bwd(W, X[rows], dY[rows], A, B, alpha, r)
+    np.testing.assert_allclose(dXs, dX[rows], rtol=1e-13, atol=1e-13)
+    Ys, _ = oracle.linear_fwd(W, X[rows], A, B, alpha, r)
+    Y, _ = oracle.linear_fwd(W, X, A, B, alpha, r)
+    np.testing.assert_allclose(Ys, Y[rows], rtol=1e-13, atol=1e-13)
