@@ -98,13 +98,18 @@ __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ W, uint3
 
   if (valid) {
     // x = w / am (IEEE division) decides each code.  The fast pass takes x
-    // as w * fp32(1 / am), within 2^-22 relative of the quotient: that picks
-    // the table cell (a neighbouring cell gives the same answer) and decides
-    // the comparison with the candidate threshold t unless x lies within
-    // 2^-20 |t| of t.  A block with any weight that close is coded again
-    // with the quotient itself (about one block in 3000 for normal data).  A block whose
-    // absmax is so small that 1 / am would overflow is scaled by 2^64 first
-    // (exact: every quotient is unchanged).
+    // as w * fp32(1 / am), within 2^-22 relative of the quotient while the
+    // quotient is a normal number: that picks the table cell (a neighbouring
+    // cell gives the same answer) and decides the comparison with the
+    // candidate threshold t unless x lies within max(2^-20 |t|, 2^-100) of t.
+    // The absolute floor matters only for a threshold at exactly 0 (the
+    // evenly spaced table): there the quotient may underflow to +-0 while
+    // the product rounds to the smallest subnormal (w = 3 * 2^-149, am = 6),
+    // so any x' within 2^-100 of 0 is decided by the quotient.  A block with
+    // any weight that close is coded again with the quotient itself (about
+    // one block in 3000 for normal data).  A block whose absmax is so small
+    // that 1 / am would overflow is scaled by 2^64 first (exact: every
+    // quotient is unchanged).
     float amq = am;
     if (am < 0x1p-100f) {
 #pragma unroll
@@ -113,7 +118,7 @@ __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ W, uint3
     }
     const float rcp = amq > 0.f ? 1.0f / amq : 0.f;
     uint32_t packed[8];
-    float nd = 1.f;  // min over the block of |x - t| - 2^-20 |t|; <= 0: some x is close to its t
+    float nd = 1.f;  // min over the block of |x - t| - max(2^-20 |t|, 2^-100); <= 0: some x is close to its t
 #pragma unroll
     for (int h = 0; h < 4; ++h) {  // 16 weights per batch: all 16 table reads in flight
       float x[16];
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ W, uint3
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         x[i] = w[16 * h + i] * rcp;
-        const int cell = min(max((int)(x[i] * 128.f + 128.f), 0), 255);
+        const int cell = min(max((int)__builtin_fmaf(x[i], 128.f, 128.f), 0), 255);  // x * 128 is exact
         ct[i] = s_ct[cell];
       }
 #pragma unroll
@@ -131,7 +136,7 @@ __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ W, uint3
         for (int e = 0; e < 8; ++e) {
           const int i = 8 * dd + e;
           const float t = __uint_as_float(ct[i].x);
-          nd = fminf(nd, fabsf(x[i] - t) - fabsf(t) * 0x1p-20f);
+          nd = fminf(nd, fabsf(x[i] - t) - fmaxf(fabsf(t) * 0x1p-20f, 0x1p-100f));
           word |= (ct[i].y + (x[i] > t ? 1u : 0u)) << (4 * e);
         }
         packed[2 * h + dd] = word;
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ W, uint3
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float x = amq > 0.f ? w[8 * d + e] / amq : 0.f;  // IEEE division
-          const int cell = min(max((int)(x * 128.f + 128.f), 0), 255);
+          const int cell = min(max((int)__builtin_fmaf(x, 128.f, 128.f), 0), 255);
           const uint2 ct = s_ct[cell];
           word |= (ct.y + (x > __uint_as_float(ct.x) ? 1u : 0u)) << (4 * e);
         }

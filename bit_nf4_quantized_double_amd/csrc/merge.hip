@@ -154,7 +154,8 @@ __global__ __launch_bounds__(256) void k_merge(const uint4* __restrict__ codes, 
       for (int i = 0; i < 4; ++i) {
         const f32x4& t = acc[2 * d + (i >> 1)];
         const float w0 = bf16_to_f32((uint16_t)(wv[i] & 0xFFFFu)), w1 = bf16_to_f32((uint16_t)(wv[i] >> 16));
-        o[i] = pack_bf16x2(w0 + s * t[2 * (i & 1)], w1 + s * t[2 * (i & 1) + 1]);
+        // w + s * t with one rounding (fused multiply-add), then bf16 RNE
+        o[i] = pack_bf16x2(__builtin_fmaf(s, t[2 * (i & 1)], w0), __builtin_fmaf(s, t[2 * (i & 1) + 1], w1));
       }
       *reinterpret_cast<uint4*>(sw + row * kOPitch + kl + 8 * d) = make_uint4(o[0], o[1], o[2], o[3]);
     }
