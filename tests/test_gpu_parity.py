@@ -133,6 +133,60 @@ def test_quantize_zero_group_bit_exact():
     check_codec_exact(gpu_quantize(W), q, wb)
 
 
+@pytest.mark.parametrize("fmt", ["nf4_dq", "nf4", "int4_dq", "int4"])
+def test_quantize_near_threshold_bit_exact(fmt):
+    """Blocks whose absmax is not a power of two (so 1 / absmax is inexact),
+    holding weights at fp32(theta_i * a), fp32(T_i * a) and 1..4 ulps around
+    them for every threshold of the format's table; under the evenly spaced
+    tables also the block whose quotient underflows to 0 beside a zero
+    threshold.  Codes, block scales and the decoded bf16 weight bit-exact."""
+    from oracle import formats
+    import crafted
+    _need_gpu()
+    rng = np.random.default_rng(17)
+    table = formats.format_table(fmt)
+    blocks = crafted.near_threshold_blocks(table, crafted.absmax_set(rng, 60), rng)
+    if fmt.startswith("int4"):
+        blocks = np.concatenate([blocks, crafted.zero_threshold_underflow_block()[None, :]])
+    W = np.ascontiguousarray(crafted.as_weight(blocks))
+    n, k = W.shape
+    q = formats.quantize_format(W, fmt)
+    _, wb = formats.dequant_format(q, n, k, fmt)
+    w = qlora.quantize_format(torch.from_numpy(W).cuda(), fmt)
+    out = qlora.dequant_format(w)
+    torch.cuda.synchronize()
+    assert np.array_equal(w.codes.cpu().numpy(), q["codes"]), "codes"
+    if fmt.endswith("_dq"):
+        assert np.array_equal(w.scales.cpu().numpy(), q["absmax_q8"]), "q8"
+        assert np.array_equal(w.absmax_scale.cpu().numpy().view(np.uint32),
+                              q["absmax_scale"].view(np.uint32)), "s2"
+    else:
+        assert np.array_equal(w.scales.cpu().numpy().view(np.uint32), q["absmax"].view(np.uint32)), "absmax"
+    assert np.array_equal(host_bits(out), wb), "dequantized bf16"
+    if fmt == "nf4_dq":  # the main codec entry point on the same weight
+        qm = oracle.quantize_nf4_dq(W)
+        check_codec_exact(gpu_quantize(W), qm, wb)
+
+
+def test_quantize_bf16_near_threshold_bit_exact():
+    """The bf16-input codec (re-quantizing a merged weight) on bf16 weights a
+    few bf16 ulps around every NF4 threshold of bf16 absmaxes that are not
+    powers of two: bit-exact against the oracle's codec of the widened
+    values."""
+    import crafted
+    _need_gpu()
+    rng = np.random.default_rng(19)
+    blocks = crafted.near_threshold_blocks(oracle.nf4_table(), crafted.absmax_set(rng, 60), rng, bf16=True)
+    W = np.ascontiguousarray(crafted.as_weight(blocks))
+    bits = oracle.bf16_bits_from_f32(W)
+    Wf = (bits.astype(np.uint32) << 16).view(np.float32)  # the padding blocks rounded too
+    q = oracle.quantize_nf4_dq(Wf)
+    _, wb = oracle.dequant(q["codes"], q["absmax_q8"], q["absmax_scale"], *W.shape)
+    w = qlora.quantize(dev_bf16(bits))
+    torch.cuda.synchronize()
+    check_codec_exact(w, q, wb)
+
+
 @pytest.mark.parametrize("workload,index", [("7b", 4), ("7b", 6), ("70b", 0), ("70b", 1)])
 def test_quantize_dequant_full_size_sampled_groups(workload, index):
     """Full-size weights quantized and dequantized on the GPU; 64 sampled
@@ -252,9 +306,9 @@ def test_f16_full_7b_linear_sampled():
     dXr, _, _ = oracle.linear_bwd(Wh, Xh[rows], dYh[rows], Ah, Bh, alpha, r)
     check_close(f64h(Y)[rows], Yr, "Y fp16 sampled")
     check_close(f64h(dX)[rows], dXr, "dX fp16 sampled")
-    s = oracle.lora_scale(alpha, r)
-    check_close(f64(dA), s * ((dYh @ Bh).T @ Xh), "dA fp16")
-    check_close(f64(dB), s * (dYh.T @ (Xh @ Ah.T)), "dB fp16")
+    dAr, dBr = oracle.adapter_grads(Xh, dYh, Ah, Bh, alpha, r)
+    check_close(f64(dA), dAr, "dA fp16")
+    check_close(f64(dB), dBr, "dB fp16")
 
 
 # ------------------------------------------------------- format variants ----
@@ -503,6 +557,87 @@ def test_autograd_module_matches_entry_points():
     check_close(f64(mod.B.grad.float()), dBr, "module dB")
 
 
+@pytest.mark.parametrize("p", [0.0, 0.05])
+def test_autograd_module_fp16(p):
+    """The nn.Module in the fp16 instance (adapter held in fp16, X and the
+    incoming gradient fp16), without and with LoRA dropout: its results are
+    bit for bit those of the entry points, and match the oracle's fp16
+    forward and backward."""
+    _need_gpu()
+    M, N, K, r, alpha = 64, 256, 256, 16, 32.0
+    rng = np.random.default_rng(23)
+    d = synth.linear_inputs(N, K, M, r, rng, dtype="f16")
+    Wt = torch.from_numpy(d["W"]).cuda()
+    A16, B16 = dev_f16(d["A"]), dev_f16(d["B"])
+    mod = qlora.QLoRALinear(Wt, r=r, alpha=alpha, A=A16.float(), B=B16.float(), lora_dropout=p,
+                            dtype=torch.float16)
+    assert mod.A.dtype == torch.float16 and mod.B.dtype == torch.float16
+    X = dev_f16(d["X"]).requires_grad_(True)
+    torch.manual_seed(5)
+    Y = mod(X)
+    dY = dev_f16(d["dY"])
+    Y.backward(dY)
+    torch.cuda.synchronize()
+    assert Y.dtype == torch.float16 and X.grad.dtype == torch.float16
+    # the seed the module drew for this step
+    torch.manual_seed(5)
+    seed = int(torch.randint(0, 2**62, (1,)).item()) if p else 0
+    Ye, Ue = qlora.linear_fwd(mod.w, X.detach(), A16, B16, r, alpha, dropout_p=p, seed=seed)
+    dXe, dAe, dBe = qlora.linear_bwd(mod.w, X.detach(), dY, A16, B16, r, alpha, Ue, dropout_p=p, seed=seed)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.detach().view(torch.int16), Ye.view(torch.int16))
+    assert torch.equal(X.grad.view(torch.int16), dXe.view(torch.int16))
+    assert torch.equal(mod.A.grad, dAe.to(torch.float16)) and torch.equal(mod.B.grad, dBe.to(torch.float16))
+    q = oracle.quantize_nf4_dq(d["W"])
+    _, hb = oracle.f16.dequant_f16(q["codes"], q["absmax_q8"], q["absmax_scale"], N, K)
+    Wh = oracle.f16.f64_from_f16_bits(hb)
+    Xh, dYh = oracle.f16.f64_from_f16_bits(d["X"]), oracle.f16.f64_from_f16_bits(d["dY"])
+    Ah, Bh = oracle.f16.f64_from_f16_bits(d["A"]), oracle.f16.f64_from_f16_bits(d["B"])
+    mask = oracle.dropout_mask(M, K, p, seed) if p else np.ones((M, K), dtype=bool)
+    Yr, _ = oracle.linear_fwd_dropout(Wh, Xh, Ah, Bh, alpha, r, mask, p)
+    dXr, dAr, dBr = oracle.linear_bwd_dropout(Wh, Xh, dYh, Ah, Bh, alpha, r, mask, p)
+    check_close(f64h(Y.detach()), Yr, "module Y fp16")
+    check_close(f64h(X.grad), dXr, "module dX fp16")
+    check_close(f64(dAe), dAr, "module dA fp16")
+    check_close(f64(dBe), dBr, "module dB fp16")
+
+
+F16_DROP_SHAPES = [
+    # GEMM path with ragged tiles; few-token path; dX split 4 ways
+    (100, 200, 192, 16, 32.0, 0.05),
+    (5, 1000, 384, 16, 32.0, 0.05),
+    (300, 2048, 2048, 17, 34.0, 0.1),
+]
+
+
+@pytest.mark.parametrize("M,N,K,r,alpha,p", F16_DROP_SHAPES)
+def test_f16_dropout_forward_backward_parity(M, N, K, r, alpha, p):
+    """LoRA dropout in the fp16 instance against the oracle's dropped layer
+    on the fp16 values."""
+    _need_gpu()
+    rng = np.random.default_rng(M * 3 + N)
+    d = synth.linear_inputs(N, K, M, r, rng, dtype="f16")
+    q = oracle.quantize_nf4_dq(d["W"])
+    _, hb = oracle.f16.dequant_f16(q["codes"], q["absmax_q8"], q["absmax_scale"], N, K)
+    Wh = oracle.f16.f64_from_f16_bits(hb)
+    Xh, dYh = oracle.f16.f64_from_f16_bits(d["X"]), oracle.f16.f64_from_f16_bits(d["dY"])
+    Ah, Bh = oracle.f16.f64_from_f16_bits(d["A"]), oracle.f16.f64_from_f16_bits(d["B"])
+    w = gpu_quantize(d["W"])
+    X, dY, A, B = dev_f16(d["X"]), dev_f16(d["dY"]), dev_f16(d["A"]), dev_f16(d["B"])
+    seed = _drop_seed(M, N) ^ 0xF16
+    Y, U = qlora.linear_fwd(w, X, A, B, r, alpha, dropout_p=p, seed=seed)
+    dX, dA, dB = qlora.linear_bwd(w, X, dY, A, B, r, alpha, U, dropout_p=p, seed=seed)
+    torch.cuda.synchronize()
+    mask = oracle.dropout_mask(M, K, p, seed)
+    Yr, Ur = oracle.linear_fwd_dropout(Wh, Xh, Ah, Bh, alpha, r, mask, p)
+    dXr, dAr, dBr = oracle.linear_bwd_dropout(Wh, Xh, dYh, Ah, Bh, alpha, r, mask, p)
+    check_close(f64h(Y), Yr, "Y fp16 dropout")
+    check_close(f64h(U), oracle.lora_scale(alpha, r) * Ur, "U~ fp16 dropout")
+    check_close(f64h(dX), dXr, "dX fp16 dropout")
+    check_close(f64(dA), dAr, "dA fp16 dropout")
+    check_close(f64(dB), dBr, "dB fp16 dropout")
+
+
 # ------------------------------------------------------------ LoRA dropout ----
 
 DROP_SHAPES = [
@@ -636,18 +771,14 @@ def test_full_7b_linear_sampled(index):
     torch.cuda.synchronize()
     check_codec_exact(w, q)
     rows = np.sort(np.random.default_rng(index).choice(M, 48, replace=False))
-    Wf = oracle.f64_from_bf16_bits(wb)
-    Xf = oracle.f64_from_bf16_bits(d["X"])
-    dYf = oracle.f64_from_bf16_bits(d["dY"])
-    Af = oracle.f64_from_bf16_bits(d["A"])
-    Bf = oracle.f64_from_bf16_bits(d["B"])
-    s = oracle.lora_scale(alpha, r)
-    Yr = Xf[rows] @ Wf.T + s * (Xf[rows] @ Af.T) @ Bf.T
+    # the oracle's forward and backward on the sampled token rows (each row
+    # of Y and dX depends on its own token only), its adapter gradients over
+    # every token
+    Yr, _ = oracle.linear_fwd(wb, d["X"][rows], d["A"], d["B"], alpha, r)
     check_close(f64(Y)[rows], Yr, "Y rows")
-    dXr = dYf[rows] @ Wf + s * (dYf[rows] @ Bf) @ Af
+    dXr, _, _ = oracle.linear_bwd(wb, d["X"][rows], d["dY"][rows], d["A"], d["B"], alpha, r)
     check_close(f64(dX)[rows], dXr, "dX rows")
-    dAr = s * ((dYf @ Bf).T @ Xf)
-    dBr = s * (dYf.T @ (Xf @ Af.T))
+    dAr, dBr = oracle.adapter_grads(d["X"], d["dY"], d["A"], d["B"], alpha, r)
     check_close(f64(dA), dAr, "dA")
     check_close(f64(dB), dBr, "dB")
 
@@ -667,14 +798,13 @@ def _full_linear_sampled(workload, index, nrows):
     torch.cuda.synchronize()
     check_codec_exact(w, q)
     rows = np.sort(np.random.default_rng(index + 100).choice(M, nrows, replace=False))
-    Wf = oracle.f64_from_bf16_bits(wb)
-    Xf, dYf = oracle.f64_from_bf16_bits(d["X"]), oracle.f64_from_bf16_bits(d["dY"])
-    Af, Bf = oracle.f64_from_bf16_bits(d["A"]), oracle.f64_from_bf16_bits(d["B"])
-    s = oracle.lora_scale(alpha, r)
-    check_close(f64(Y)[rows], Xf[rows] @ Wf.T + s * (Xf[rows] @ Af.T) @ Bf.T, f"{workload} Y rows")
-    check_close(f64(dX)[rows], dYf[rows] @ Wf + s * (dYf[rows] @ Bf) @ Af, f"{workload} dX rows")
-    check_close(f64(dA), s * ((dYf @ Bf).T @ Xf), f"{workload} dA")
-    check_close(f64(dB), s * (dYf.T @ (Xf @ Af.T)), f"{workload} dB")
+    Yr, _ = oracle.linear_fwd(wb, d["X"][rows], d["A"], d["B"], alpha, r)
+    dXr, _, _ = oracle.linear_bwd(wb, d["X"][rows], d["dY"][rows], d["A"], d["B"], alpha, r)
+    dAr, dBr = oracle.adapter_grads(d["X"], d["dY"], d["A"], d["B"], alpha, r)
+    check_close(f64(Y)[rows], Yr, f"{workload} Y rows")
+    check_close(f64(dX)[rows], dXr, f"{workload} dX rows")
+    check_close(f64(dA), dAr, f"{workload} dA")
+    check_close(f64(dB), dBr, f"{workload} dB")
 
 
 @pytest.mark.parametrize("index", [0, 1, 4, 6])  # q, k (3072 -> 1024), gate, down
@@ -718,12 +848,9 @@ def test_few_token_70b_sampled_columns(index, M):
         gb0 = groups[0] * 256
         _, wbr = oracle.dequant(codes, q8, s2, 1, codes.size * 2, first_block=gb0)
         Wrows.append(wbr.ravel()[(b0 - gb0) * 64:(b0 - gb0 + bpr) * 64])
-    Wsel = oracle.f64_from_bf16_bits(np.stack(Wrows))
-    Xf = oracle.f64_from_bf16_bits(d["X"])
-    Af = oracle.f64_from_bf16_bits(d["A"])
-    Bf = oracle.f64_from_bf16_bits(d["B"])
-    s = oracle.lora_scale(alpha, r)
-    Yr = Xf @ Wsel.T + s * (Xf @ Af.T) @ Bf[cols].T
+    # the oracle's forward on the sampled output features: their rows of the
+    # dequantized weight and of B
+    Yr, _ = oracle.linear_fwd(np.stack(Wrows), d["X"], d["A"], d["B"][cols], alpha, r)
     check_close(f64(Y)[:, cols], Yr, "Y sampled columns")
 
 
