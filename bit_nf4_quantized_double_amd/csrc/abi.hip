@@ -2,6 +2,7 @@
 // layout, and the launch sequence of each operation on the caller's stream.
 // Declarations and the contract of every entry point: include/qlora.h.
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstring>
@@ -39,6 +40,25 @@ hipError_t launch_vt_and_db(const uint16_t* dY, int M, int N, const uint16_t* B,
                             float s, uint16_t* V, float* vpart, float* cpart, float* dB, bool f16, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_zero_u16(uint16_t* p, int64_t n, hipStream_t st);
+}  // namespace qlora
+
+namespace qlora {
+
+int device_compute_units() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cached[kMaxDev];  // 0: not queried yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDev) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+  if (dev < kMaxDev) cached[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
 }  // namespace qlora
 
 namespace {
@@ -139,7 +159,7 @@ BwdLayout bwd_layout(int64_t M, int64_t n_out, int64_t k_in, int32_t r) {
   }
   // the dX product's split-reduction tiles reuse everything from L.part on
   // (dead by then); they need not fit: without room the product runs unsplit
-  L.gemm = round_up(qlora::gemm_part_bytes(M, k_in, n_out));
+  L.gemm = round_up(qlora::gemm_part_bytes(M, k_in, n_out, qlora::device_compute_units()));
   L.total = std::max(L.req, L.part + L.gemm);
   return L;
 }
@@ -181,6 +201,30 @@ void qlora_nf4_table(float out[16]) {
   std::memcpy(out, c.level, sizeof(c.level));
 }
 
+int qlora_plan(int op, int64_t M, int64_t n_out, int64_t k_in, int compute_units, int64_t out[4]) {
+  if (!out) return fail(QLORA_ERR_INVALID_ARG, "out is NULL");
+  if ((op != QLORA_OP_FWD && op != QLORA_OP_BWD) || M < 0 || n_out < 0 || k_in < 0)
+    return fail(QLORA_ERR_INVALID_ARG, "invalid plan arguments");
+  const int cus = compute_units > 0 ? compute_units : qlora::device_compute_units();
+  if (op == QLORA_OP_FWD && M <= qlora::skinny_max_tokens()) {
+    const qlora::SkinnySplit sp = qlora::skinny_split(M, n_out, k_in, cus);
+    out[0] = 2;
+    out[1] = sp.ks;
+    out[2] = sp.kchunks;
+    out[3] = (k_in + 127) / 128;
+    return QLORA_OK;
+  }
+  // the fused GEMM: forward reduces over k_in into n_out columns, dX over n_out into k_in
+  const int64_t C = op == QLORA_OP_FWD ? n_out : k_in, R = op == QLORA_OP_FWD ? k_in : n_out;
+  const int64_t nsteps = (R + 63) / 64;
+  const int ks = qlora::gemm_ksplit(M, C, R, cus);
+  out[0] = 1;
+  out[1] = ks;
+  out[2] = (nsteps + ks - 1) / ks;
+  out[3] = nsteps;
+  return QLORA_OK;
+}
+
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, int32_t r) {
   if (M < 0 || n_out < 0 || k_in < 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
   if (op == QLORA_OP_FWD) {
@@ -188,8 +232,9 @@ size_t qlora_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, int
     // [U~][U~ partials | split-reduction tiles of the main product]
     const size_t u = r > 0 ? round_up((size_t)M * r * 2) : 0;
     const size_t upart = r > 0 ? round_up(qlora::rowdot_part_bytes(M, k_in, r)) : 0;
-    const size_t gpart = round_up(M > qlora::skinny_max_tokens() ? qlora::gemm_part_bytes(M, n_out, k_in)
-                                                                  : qlora::skinny_part_bytes(M, n_out, k_in));
+    const int cus = qlora::device_compute_units();
+    const size_t gpart = round_up(M > qlora::skinny_max_tokens() ? qlora::gemm_part_bytes(M, n_out, k_in, cus)
+                                                                  : qlora::skinny_part_bytes(M, n_out, k_in, cus));
     return u + std::max(upart, gpart);
   }
   if (op == QLORA_OP_BWD) return bwd_layout(M, n_out, k_in, r).total;
@@ -303,7 +348,7 @@ static int linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t
     k.f16 = f16;
     // split partial sums after U~ (the U~ partials are consumed by then);
     // without room the kernel runs unsplit
-    const size_t kbytes = qlora::skinny_part_bytes(M, w->n_out, w->k_in);
+    const size_t kbytes = qlora::skinny_part_bytes(M, w->n_out, w->k_in, qlora::device_compute_units());
     if (kbytes && ws && aligned16(ws) && ws_bytes >= ubytes + kbytes)
       k.part = reinterpret_cast<float*>(static_cast<char*>(ws) + ubytes);
     e = qlora::launch_skinny_fwd(k, stream);
@@ -316,7 +361,7 @@ static int linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t
   g.out = Y; g.ld_out = w->n_out;
   g.nf4 = qlora::nf4_consts();
   g.f16 = f16;
-  const size_t gbytes = qlora::gemm_part_bytes(M, w->n_out, w->k_in);
+  const size_t gbytes = qlora::gemm_part_bytes(M, w->n_out, w->k_in, qlora::device_compute_units());
   if (gbytes && ws && aligned16(ws) && ws_bytes >= ubytes + gbytes)
     g.part = reinterpret_cast<float*>(static_cast<char*>(ws) + ubytes);
   e = qlora::launch_gemm_fwd(g, stream);
@@ -452,6 +497,27 @@ int qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t* X, const
   const int st = dropout_setup(r, alpha, dropout_p, seed, &dm, &s);
   if (st) return st;
   return linear_bwd_impl(w, X, dY, M, A, B, r, alpha, dm, s, U, dX, dA, dB, ws, ws_bytes, false, stream);
+}
+
+int qlora_linear_fwd_dropout_f16(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, const uint16_t* A,
+                                 const uint16_t* B, int32_t r, float alpha, double dropout_p, uint64_t seed,
+                                 uint16_t* Y, uint16_t* U_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  qlora::DropMask dm{};
+  float s = 0.f;
+  const int st = dropout_setup(r, alpha, dropout_p, seed, &dm, &s);
+  if (st) return st;
+  return linear_fwd_impl(w, X, M, A, B, r, alpha, dm, s, Y, U_out, ws, ws_bytes, true, stream);
+}
+
+int qlora_linear_bwd_dropout_f16(const qlora_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t M,
+                                 const uint16_t* A, const uint16_t* B, int32_t r, float alpha, double dropout_p,
+                                 uint64_t seed, const uint16_t* U, uint16_t* dX, float* dA, float* dB, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  qlora::DropMask dm{};
+  float s = 0.f;
+  const int st = dropout_setup(r, alpha, dropout_p, seed, &dm, &s);
+  if (st) return st;
+  return linear_bwd_impl(w, X, dY, M, A, B, r, alpha, dm, s, U, dX, dA, dB, ws, ws_bytes, true, stream);
 }
 
 int qlora_format_table(int format, float out[16]) {

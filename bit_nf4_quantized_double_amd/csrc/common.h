@@ -38,6 +38,12 @@ struct QuantSearch {
 
 const QuantSearch& quant_search();  // host, built once
 
+// Compute units of the calling thread's current device: queried once per
+// device and cached; 256 (an MI355X) when no device can be queried, as on a
+// host without a GPU.  Work splits and the workspace sizes that hold their
+// partial sums are both derived from it, so the two always agree.
+int device_compute_units();
+
 // Format variants: 16 evenly spaced levels -1 + 2 i / 15 with the same
 // round-down midpoint thresholds, and their code search (host, built once).
 const Nf4Consts& int4_consts();

@@ -594,7 +594,7 @@ hipError_t launch(GemmArgs a, hipStream_t st) {
   hipEvent_t ev0, ev1;
   take_gemm_events(ev0, ev1);
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
-  a.ksplit = a.part ? gemm_ksplit(a.M, a.C, a.R) : 1;
+  a.ksplit = a.part ? gemm_ksplit(a.M, a.C, a.R, device_compute_units()) : 1;
   if (a.ksplit < 2) a.part = nullptr;
   dim3 grid((a.C + BN - 1) / BN, (a.M + BM - 1) / BM, a.ksplit);
   hipLaunchKernelGGL(kern, grid, dim3(2 * kThreads), 0, st, a);
@@ -619,19 +619,19 @@ void time_next_gemm(hipEvent_t start, hipEvent_t stop) {
   else { t_ev_start = t_ev_stop = nullptr; }
 }
 
-int gemm_ksplit(int64_t M, int64_t C, int64_t R) {
-  constexpr int64_t kCus = 256;  // MI355X compute units
+int gemm_ksplit(int64_t M, int64_t C, int64_t R, int cus) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((C + BN - 1) / BN);
   const int64_t nsteps = (R + 63) / 64;
-  if (tiles <= 0 || tiles * 2 > kCus || C % 8 != 0) return 1;
+  if (cus <= 0 || tiles <= 0 || tiles * 2 > cus || C % 8 != 0) return 1;
   // at most 8 splits, a grid of at most one workgroup per compute unit, and
-  // at least 8 steps (512 reduction columns) per split
-  const int64_t ks = std::min<int64_t>(std::min<int64_t>(8, kCus / tiles), nsteps / 8);
+  // at least 8 steps (512 reduction columns) per split -- so no split is
+  // empty: ceil(nsteps / ks) >= 8 >= ks
+  const int64_t ks = std::min<int64_t>(std::min<int64_t>(8, cus / tiles), nsteps / 8);
   return ks > 1 ? (int)ks : 1;
 }
 
-size_t gemm_part_bytes(int64_t M, int64_t C, int64_t R) {
-  const int ks = gemm_ksplit(M, C, R);
+size_t gemm_part_bytes(int64_t M, int64_t C, int64_t R, int cus) {
+  const int ks = gemm_ksplit(M, C, R, cus);
   return ks > 1 ? (size_t)ks * (size_t)M * (size_t)C * 4u : 0;
 }
 

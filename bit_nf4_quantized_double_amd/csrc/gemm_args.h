@@ -31,11 +31,12 @@ struct GemmArgs {
   float* part;
 };
 
-// Reduction splits for a product of M x C outputs over R: more than one only
-// when the grid of 256 x 128 tiles would leave at least half of the GPU's
-// 256 compute units idle.  The fp32 bytes the split needs (0 if unsplit).
-int gemm_ksplit(int64_t M, int64_t C, int64_t R);
-size_t gemm_part_bytes(int64_t M, int64_t C, int64_t R);
+// Reduction splits for a product of M x C outputs over R on a device with
+// `cus` compute units: more than one only when the grid of 256 x 128 tiles
+// would leave at least half of them idle.  The fp32 bytes the split needs
+// (0 if unsplit).
+int gemm_ksplit(int64_t M, int64_t C, int64_t R, int cus);
+size_t gemm_part_bytes(int64_t M, int64_t C, int64_t R, int cus);
 
 // out = E(sum over z of part[z]) for fp32 partial sums [ksplit][M][C], z in
 // order (C % 8 == 0, rows of out 16-byte aligned).

@@ -343,34 +343,34 @@ int skinny_max_tokens() { return 16; }
 // workgroup takes 8 tiles over 1 / ks of the reduction (at least 16 chunks
 // of 128), when that still gives a workgroup per compute unit; the ks fp32
 // partial sums are added in split order by a second pass.
-int skinny_ksplit(int64_t M, int64_t N, int64_t K) {
-  constexpr int64_t kCus = 256;  // MI355X compute units
+SkinnySplit skinny_split(int64_t M, int64_t N, int64_t K, int cus) {
   const int64_t ntiles = (N + 15) / 16, nch = (K + 127) / 128;
-  if (M < 8 || M > 16 || ntiles == 0 || (ntiles + kCus - 1) / kCus > 2) return 1;
+  SkinnySplit sp{1, (int)nch};
+  if (cus <= 0 || M < 8 || M > 16 || ntiles == 0 || (ntiles + cus - 1) / cus > 2) return sp;
   const int64_t groups = (ntiles + 7) / 8;
-  const int64_t ks = std::min(kCus / groups, nch / 16);
-  return ks > 1 && groups * ks >= kCus ? (int)ks : 1;
+  const int64_t ks = std::min<int64_t>(cus / groups, nch / 16);
+  if (ks < 2 || groups * ks < cus) return sp;
+  // chunks per split, then the splits those chunks actually need (none empty)
+  const int64_t kc = (nch + ks - 1) / ks;
+  sp.kchunks = (int)kc;
+  sp.ks = (int)((nch + kc - 1) / kc);
+  return sp;
 }
 
-size_t skinny_part_bytes(int64_t M, int64_t N, int64_t K) {
-  const int ks = skinny_ksplit(M, N, K);
+size_t skinny_part_bytes(int64_t M, int64_t N, int64_t K, int cus) {
+  const int ks = skinny_split(M, N, K, cus).ks;
   return ks > 1 ? (size_t)ks * (size_t)M * (size_t)N * 4u : 0;
 }
 
 hipError_t launch_skinny_fwd(SkinnyArgs a, hipStream_t st) {
   const int ntiles = (a.N + 15) / 16;
   const int nch = (a.K + 127) / 128;
-  int num_cu = 256;
-  {
-    int dev = 0;
-    if (hipGetDevice(&dev) == hipSuccess) {
-      int v = 0;
-      if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) num_cu = v;
-    }
-  }
-  const int ks = a.part ? skinny_ksplit(a.M, a.N, a.K) : 1;
-  if (ks < 2) a.part = nullptr;
-  a.kchunks = (nch + ks - 1) / ks;
+  const int num_cu = device_compute_units();
+  SkinnySplit sp = skinny_split(a.M, a.N, a.K, num_cu);
+  if (!a.part || sp.ks < 2) sp = SkinnySplit{1, nch};
+  if (sp.ks < 2) a.part = nullptr;
+  const int ks = sp.ks;
+  a.kchunks = sp.kchunks;
   const int tpg = ks > 1 ? 8 : std::max(1, (ntiles + num_cu - 1) / num_cu);
   int tpw = std::min(tpg, 8);
   int nwt = 1;

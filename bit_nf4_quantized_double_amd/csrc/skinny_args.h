@@ -24,10 +24,15 @@ struct SkinnyArgs {
 };
 
 int skinny_max_tokens();
-// Reduction splits across workgroups for these sizes (1: unsplit) and the
-// fp32 bytes their partial sums take (0 if unsplit).
-int skinny_ksplit(int64_t M, int64_t N, int64_t K);
-size_t skinny_part_bytes(int64_t M, int64_t N, int64_t K);
+// Reduction split across workgroups for these sizes on a device with `cus`
+// compute units: ks splits of kchunks 128-wide chunks each (ks = 1:
+// unsplit), every split non-empty: (ks - 1) * kchunks < chunks <= ks * kchunks.
+struct SkinnySplit {
+  int ks, kchunks;
+};
+SkinnySplit skinny_split(int64_t M, int64_t N, int64_t K, int cus);
+// fp32 bytes the split's partial sums take (0 if unsplit)
+size_t skinny_part_bytes(int64_t M, int64_t N, int64_t K, int cus);
 hipError_t launch_skinny_fwd(SkinnyArgs a, hipStream_t st);
 
 }  // namespace qlora

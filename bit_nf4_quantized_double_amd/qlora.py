@@ -67,10 +67,18 @@ def lib() -> ctypes.CDLL:
         "qlora_linear_bwd_dropout": (ctypes.c_int, [W, _vp, _vp, _c_i64, _vp, _vp, _c_i32, ctypes.c_float,
                                                     ctypes.c_double, ctypes.c_uint64,
                                                     _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+        "qlora_linear_fwd_dropout_f16": (ctypes.c_int, [W, _vp, _c_i64, _vp, _vp, _c_i32, ctypes.c_float,
+                                                        ctypes.c_double, ctypes.c_uint64,
+                                                        _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+        "qlora_linear_bwd_dropout_f16": (ctypes.c_int, [W, _vp, _vp, _c_i64, _vp, _vp, _c_i32, ctypes.c_float,
+                                                        ctypes.c_double, ctypes.c_uint64,
+                                                        _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
         "qlora_quantize_format": (ctypes.c_int, [ctypes.c_int, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
         "qlora_dequant_format": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp]),
         "qlora_format_table": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_float)]),
         "qlora_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_i32]),
+        "qlora_plan": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_i64, ctypes.c_int,
+                                      ctypes.POINTER(_c_i64)]),
         "qlora_nf4_table": (None, [ctypes.POINTER(ctypes.c_float)]),
         "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "qlora_last_error": (ctypes.c_char_p, []),
@@ -138,6 +146,14 @@ def nf4_table() -> list:
 
 def workspace_bytes(op: int, M: int, n_out: int, k_in: int, r: int) -> int:
     return int(lib().qlora_workspace_bytes(op, M, n_out, k_in, r))
+
+
+def plan(op: int, M: int, n_out: int, k_in: int, compute_units: int = 0) -> dict:
+    """The library's work split for the main product (qlora_plan)."""
+    out = (_c_i64 * 4)()
+    _check(lib().qlora_plan(op, M, n_out, k_in, compute_units, out), "qlora_plan")
+    return {"kernel": {1: "gemm", 2: "few_token"}[out[0]], "splits": out[1], "per_split": out[2],
+            "total": out[3]}
 
 
 def _empty_u8(n, device):
@@ -305,9 +321,10 @@ def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor | None, B: torch.T
     cw = w._c()
     head = (ctypes.byref(cw), _dev(X, et, "X"), M, _opt(A, et, "A"), _opt(B, et, "B"), r, float(alpha))
     tail = (_dev(Y, et, "Y"), _opt(U, et, "U"), None if wst is None else wst.data_ptr(), wsn, _stream())
-    if et == torch.float16:
-        if dropout_p:
-            raise NotImplementedError("LoRA dropout is exposed for the bf16 instance only")
+    if et == torch.float16 and dropout_p:
+        st = lib().qlora_linear_fwd_dropout_f16(*head, float(dropout_p), int(seed) & (2**64 - 1), *tail)
+        _check(st, "qlora_linear_fwd_dropout_f16")
+    elif et == torch.float16:
         st = lib().qlora_linear_fwd_f16(*head, *tail)
         _check(st, "qlora_linear_fwd_f16")
     elif dropout_p:
@@ -346,9 +363,10 @@ def linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor 
     tail = (_opt(U, et, "U"), _dev(dX, et, "dX"),
             _opt(dA, torch.float32, "dA"), _opt(dB, torch.float32, "dB"),
             None if wst is None else wst.data_ptr(), wsn, _stream())
-    if et == torch.float16:
-        if dropout_p:
-            raise NotImplementedError("LoRA dropout is exposed for the bf16 instance only")
+    if et == torch.float16 and dropout_p:
+        st = lib().qlora_linear_bwd_dropout_f16(*head, float(dropout_p), int(seed) & (2**64 - 1), *tail)
+        _check(st, "qlora_linear_bwd_dropout_f16")
+    elif et == torch.float16:
         st = lib().qlora_linear_bwd_f16(*head, *tail)
         _check(st, "qlora_linear_bwd_f16")
     elif dropout_p:
@@ -375,7 +393,8 @@ class QLoRALinearFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dY):
         X2, A, B, U = ctx.saved_tensors
-        dY2 = dY.reshape(-1, ctx.w.n_out).contiguous().to(torch.bfloat16)
+        # the gradient arrives in the output's dtype, which is X's (bf16 or fp16)
+        dY2 = dY.reshape(-1, ctx.w.n_out).contiguous().to(X2.dtype)
         dX, dA, dB = linear_bwd(ctx.w, X2, dY2, A, B, ctx.r, ctx.alpha, U,
                                 dropout_p=ctx.dropout_p, seed=ctx.seed)
         gA = dA.to(A.dtype) if (A is not None and ctx.needs_input_grad[1]) else None
@@ -384,11 +403,19 @@ class QLoRALinearFunction(torch.autograd.Function):
 
 
 class QLoRALinear(torch.nn.Module):
-    """nn.Linear replacement: frozen NF4 weight + trainable bf16 adapter."""
+    """nn.Linear replacement: frozen NF4 weight + trainable 16-bit adapter.
+
+    ``dtype`` is the compute dtype: bf16 (the pages' choice) or fp16 (the one
+    they name for GPUs without bf16).  The adapter parameters are held in
+    it, and inputs must come in it.
+    """
 
     def __init__(self, weight_fp32: torch.Tensor, r: int = 16, alpha: float = 32.0,
-                 A: torch.Tensor | None = None, B: torch.Tensor | None = None, lora_dropout: float = 0.0):
+                 A: torch.Tensor | None = None, B: torch.Tensor | None = None, lora_dropout: float = 0.0,
+                 dtype=torch.bfloat16):
         super().__init__()
+        if dtype not in (torch.bfloat16, torch.float16):
+            raise TypeError("the compute dtype is bf16 or fp16")
         self.lora_dropout = float(lora_dropout)
         n_out, k_in = weight_fp32.shape
         self.w = quantize(weight_fp32.contiguous())
@@ -398,8 +425,8 @@ class QLoRALinear(torch.nn.Module):
             A = torch.randn(r, k_in, device=dev) / (k_in ** 0.5)
         if B is None:
             B = torch.zeros(n_out, r, device=dev)
-        self.A = torch.nn.Parameter(A.to(torch.bfloat16).contiguous())
-        self.B = torch.nn.Parameter(B.to(torch.bfloat16).contiguous())
+        self.A = torch.nn.Parameter(A.to(dtype).contiguous())
+        self.B = torch.nn.Parameter(B.to(dtype).contiguous())
 
     def forward(self, X):
         # a fresh mask per training step (the seed is drawn from torch's host

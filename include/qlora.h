@@ -262,6 +262,18 @@ int qlora_linear_bwd_dropout(const qlora_nf4_weight *w, const uint16_t *X, const
                              float alpha, double dropout_p, uint64_t seed, const uint16_t *U,
                              uint16_t *dX, float *dA, float *dB, void *ws, size_t ws_bytes,
                              hipStream_t stream);
+/* The same two operations in the fp16 instance (see qlora_linear_fwd_f16):
+ * every 16-bit argument is a binary16 bit pattern, U~ and V~ are rounded to
+ * binary16; the mask, s_d, the workspace and the errors are as above. */
+int qlora_linear_fwd_dropout_f16(const qlora_nf4_weight *w, const uint16_t *X, int64_t M,
+                                 const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
+                                 double dropout_p, uint64_t seed, uint16_t *Y, uint16_t *U_out,
+                                 void *ws, size_t ws_bytes, hipStream_t stream);
+int qlora_linear_bwd_dropout_f16(const qlora_nf4_weight *w, const uint16_t *X, const uint16_t *dY,
+                                 int64_t M, const uint16_t *A, const uint16_t *B, int32_t r,
+                                 float alpha, double dropout_p, uint64_t seed, const uint16_t *U,
+                                 uint16_t *dX, float *dA, float *dB, void *ws, size_t ws_bytes,
+                                 hipStream_t stream);
 
 /* Workspace bytes needed by qlora_linear_fwd (op = QLORA_OP_FWD) or
  * qlora_linear_bwd (op = QLORA_OP_BWD) for these sizes: enough for any
@@ -270,6 +282,20 @@ int qlora_linear_bwd_dropout(const qlora_nf4_weight *w, const uint16_t *X, const
  * and when no workspace is used (M == 0; r == 0 with output tiles enough to
  * fill the GPU). */
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, int32_t r);
+
+/* Host function: the work split the library chooses for the main product
+ * of op at these sizes on a device with `compute_units` compute units
+ * (<= 0: the calling thread's current device; 256 when none can be
+ * queried).  op = QLORA_OP_FWD: the forward product; QLORA_OP_BWD: the dX
+ * product.  Writes out[0] = the kernel (1: fused GEMM, reduction in 64-deep
+ * steps; 2: few-token forward, reduction in 128-wide chunks), out[1] = the
+ * splits of the reduction across workgroups (1: unsplit), out[2] = steps or
+ * chunks per split, out[3] = steps or chunks in all; every split is
+ * non-empty: (out[1] - 1) * out[2] < out[3] <= out[1] * out[2].  The split
+ * runs only when the workspace has room for its partial sums
+ * (qlora_workspace_bytes counts them).  Returns QLORA_OK, or
+ * QLORA_ERR_INVALID_ARG for an unknown op, negative sizes or out == NULL. */
+int qlora_plan(int op, int64_t M, int64_t n_out, int64_t k_in, int compute_units, int64_t out[4]);
 
 /* Measurement aid.  The next fused-GEMM kernel launch made by the calling
  * thread (the forward kernel inside qlora_linear_fwd -- the GEMM, or for

@@ -206,3 +206,50 @@ def test_format_entry_points_validation(L):
     assert q(0, FAKE, 64, 64, FAKE, FAKE, None, 0) == INVALID
     assert q(2, FAKE, 64, 64, FAKE, FAKE, None, 0) == INVALID
     assert d(0, 64, 64, FAKE, FAKE, FAKE_MIS, FAKE, 0) == ALIGN
+
+
+def test_plan_splits_are_never_empty(L):
+    """Work splits of the few-token kernel and of the fused GEMM over a sweep
+    of sizes and compute-unit counts (a whole MI355X and partitions of it):
+    every split holds at least one chunk or step and together they cover the
+    reduction."""
+    checked = 0
+    for cus in (256, 304, 128, 80, 32, 8):
+        for M in (1, 4, 8, 9, 16, 17, 64, 100, 256, 300, 512, 2048):
+            for N in (8, 64, 520, 1024, 4096, 8192, 11008, 28672):
+                for K in (64, 1024, 4096, 8256, 11008, 28672, 65600):
+                    for op in (1, 2):
+                        p = qlora.plan(op, M, N, K, cus)
+                        assert p["splits"] >= 1 and p["per_split"] >= 1
+                        assert (p["splits"] - 1) * p["per_split"] < p["total"] <= p["splits"] * p["per_split"], \
+                            (op, M, N, K, cus, p)
+                        assert p["kernel"] == ("few_token" if op == 1 and M <= 16 else "gemm")
+                        checked += 1
+    assert checked == 6 * 12 * 8 * 7 * 2
+
+
+def test_plan_few_token_example_without_empty_split(L):
+    """N = 1024, K = 65600, M = 16 on 256 compute units: 513 chunks of 128.
+    32 splits of 17 chunks would leave the last one empty; the planner
+    settles on 31 splits."""
+    p = qlora.plan(1, 16, 1024, 65600, 256)
+    assert p["kernel"] == "few_token" and p["total"] == 513
+    assert p["per_split"] == 17 and p["splits"] == 31
+
+
+def test_plan_and_workspace_agree(L):
+    """The workspace counts the split's partial sums for the device it sizes
+    for (here: no device, so 256 compute units)."""
+    for M, N, K in ((16, 8192, 28672), (16, 1024, 65600), (300, 2048, 2048), (130, 1024, 2048)):
+        p = qlora.plan(1, M, N, K, 0)
+        ws = qlora.workspace_bytes(1, M, N, K, 0)
+        if p["splits"] > 1:
+            assert ws >= p["splits"] * M * N * 4
+        assert p == qlora.plan(1, M, N, K, 256)
+
+
+def test_plan_rejects_bad_arguments(L):
+    out = (ctypes.c_int64 * 4)()
+    assert L.qlora_plan(3, 16, 64, 64, 0, out) == INVALID
+    assert L.qlora_plan(1, -1, 64, 64, 0, out) == INVALID
+    assert L.qlora_plan(1, 16, 64, 64, 0, None) == INVALID
