@@ -6,6 +6,7 @@
 #include <climits>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/qlora.h"
@@ -41,6 +42,13 @@ hipError_t launch_vt_and_db(const uint16_t* dY, int M, int N, const uint16_t* B,
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_zero_u16(uint16_t* p, int64_t n, hipStream_t st);
 }  // namespace qlora
+
+// Workspace of qlora_linear_fwd_noalloc: one array per GPU, held until the
+// process ends.  Host code never passes `scratch` itself to a kernel (on the
+// host it is only a stand-in for the device symbol); it passes the device
+// address hipGetSymbolAddress gives for the current device.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
 namespace qlora {
 
@@ -455,6 +463,47 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, co
                      size_t ws_bytes, hipStream_t stream) {
   return linear_fwd_impl(w, X, M, A, B, r, alpha, qlora::DropMask{}, lora_scale(alpha, r), Y, U_out, ws, ws_bytes,
                          false, stream);
+}
+
+// Device address of `scratch` on the calling thread's current device,
+// looked up once per device (with that device current) and cached.
+static int noalloc_scratch(void** out) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDev) return fail(QLORA_ERR_INVALID_ARG, "device index beyond the no-alloc scratch table");
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(QLORA_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return QLORA_OK;
+}
+
+int qlora_linear_fwd_noalloc(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, const uint16_t* A,
+                             const uint16_t* B, int32_t r, float alpha, uint16_t* Y, uint16_t* U_out,
+                             hipStream_t stream) {
+  int st = check_weight(w);
+  if (st) return st;
+  if ((st = check_adapter(r, A, B))) return st;
+  if ((st = check_rows(M, w->n_out, w->k_in))) return st;
+  const size_t need = qlora_workspace_bytes(QLORA_OP_FWD, M, w->n_out, w->k_in, r);
+  if (need > kNoAllocScratchBytes)
+    return fail(QLORA_ERR_WORKSPACE, "the forward at these sizes needs " + std::to_string(need) +
+                                         " workspace bytes, beyond the no-alloc scratch of " +
+                                         std::to_string(kNoAllocScratchBytes));
+  if (M == 0 || w->n_out == 0) return QLORA_OK;
+  void* ws = nullptr;
+  if ((st = noalloc_scratch(&ws))) return st;
+  return linear_fwd_impl(w, X, M, A, B, r, alpha, qlora::DropMask{}, lora_scale(alpha, r), Y, U_out, ws,
+                         kNoAllocScratchBytes, false, stream);
 }
 
 int qlora_linear_fwd_f16(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, const uint16_t* A,

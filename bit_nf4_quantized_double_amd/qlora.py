@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
                                             _vp, _vp, _vp, ctypes.c_size_t, _vp]),
         "qlora_linear_bwd": (ctypes.c_int, [W, _vp, _vp, _c_i64, _vp, _vp, _c_i32, ctypes.c_float,
                                             _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+        "qlora_linear_fwd_noalloc": (ctypes.c_int, [W, _vp, _c_i64, _vp, _vp, _c_i32, ctypes.c_float,
+                                                    _vp, _vp, _vp]),
         "qlora_linear_fwd_dropout": (ctypes.c_int, [W, _vp, _c_i64, _vp, _vp, _c_i32, ctypes.c_float,
                                                     ctypes.c_double, ctypes.c_uint64,
                                                     _vp, _vp, _vp, ctypes.c_size_t, _vp]),
@@ -333,6 +335,19 @@ def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor | None, B: torch.T
     else:
         st = lib().qlora_linear_fwd(*head, *tail)
         _check(st, "qlora_linear_fwd")
+    return Y, U
+
+
+def linear_fwd_noalloc(w: NF4Weight, X: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None,
+                       r: int, alpha: float, Y: torch.Tensor, U: torch.Tensor | None = None):
+    """qlora_linear_fwd_noalloc: the bf16 forward into caller-provided Y (and
+    U~), with the library's fixed scratch as workspace (nothing allocated)."""
+    cw = w._c()
+    st = lib().qlora_linear_fwd_noalloc(ctypes.byref(cw), _dev(X, torch.bfloat16, "X"), X.shape[0],
+                                        _opt(A, torch.bfloat16, "A"), _opt(B, torch.bfloat16, "B"), r,
+                                        float(alpha), _dev(Y, torch.bfloat16, "Y"), _opt(U, torch.bfloat16, "U"),
+                                        _stream())
+    _check(st, "qlora_linear_fwd_noalloc")
     return Y, U
 
 

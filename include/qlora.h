@@ -210,6 +210,25 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_
                      void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * qlora_linear_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, results and
+ * errors as qlora_linear_fwd given a workspace of qlora_workspace_bytes
+ * (bit for bit: the same kernels and work splits),
+ * with the workspace taken from a fixed 64 MiB array the library holds on
+ * each GPU it runs on (until the process ends).  Sizes whose forward needs
+ * more (qlora_workspace_bytes(QLORA_OP_FWD, ...) > 64 MiB, e.g. more than
+ * about 2.9 M tokens-times-k_in elements) return QLORA_ERR_WORKSPACE before
+ * anything is enqueued.  The call allocates nothing and issues only kernel
+ * launches.  Every call on one GPU shares that GPU's array and nothing in it
+ * needs to start at zero; calls that overlap on one GPU (concurrent streams
+ * or threads) race on it, so serialise them.
+ */
+int qlora_linear_fwd_noalloc(const qlora_nf4_weight *w, const uint16_t *X, int64_t M,
+                             const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
+                             uint16_t *Y, uint16_t *U_out, hipStream_t stream);
+
+/*
  * fp16 instance of the path: the same operations with every 16-bit
  * quantity in IEEE binary16 instead of bf16 -- the decoded weight
  * (W_f16 = RNE_fp16(level[c] * fp32(q8 * s2))), X, A, B, Y, U~, dY, V~ and
