@@ -31,14 +31,15 @@ hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_dx(const GemmArgs& a, hipStream_t st);
 void time_next_gemm(hipEvent_t start, hipEvent_t stop);
 hipError_t launch_lora_down(const uint16_t* X, int M, int K, const uint16_t* A, int r, float s, uint16_t* U,
-                            float* part, DropMask drop, bool f16, hipStream_t st);
+                            float* part, DropMask drop, bool f16, uint16_t* Xt, hipStream_t st);
 size_t rowdot_part_bytes(int64_t M, int64_t Kd, int r);
 int coldot_chunk_rows();
 hipError_t launch_coldot(const uint16_t* v, int r, const uint16_t* in, int M, int C, float* part,
                          DropMask drop, bool f16, hipStream_t st);
 hipError_t launch_finalize(const float* part, int nmc, int r, int C, float* out, bool trans, hipStream_t st);
 hipError_t launch_vt_and_db(const uint16_t* dY, int M, int N, const uint16_t* B, const uint16_t* U, int r,
-                            float s, uint16_t* V, float* vpart, float* cpart, float* dB, bool f16, hipStream_t st);
+                            float s, uint16_t* V, float* vpart, float* cpart, float* dB, bool f16, uint16_t* dYt,
+                            hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_zero_u16(uint16_t* p, int64_t n, hipStream_t st);
 }  // namespace qlora
@@ -118,8 +119,13 @@ int check_rows(int64_t M, int64_t n_out, int64_t k_in) {
   if (M < 0) return fail(QLORA_ERR_INVALID_ARG, "M < 0");
   if (M > INT_MAX) return fail(QLORA_ERR_SHAPE, "M exceeds INT_MAX");
   const int64_t widest = n_out > k_in ? n_out : k_in;
-  // every activation / output buffer stays within 2^31 bytes (32-bit buffer offsets)
+  // every activation / output buffer stays within 2^31 bytes (32-bit buffer
+  // offsets), the fragment-tiled activation copies (rows padded to 32,
+  // columns to 64) included
   if (widest > 0 && M > ((int64_t)1 << 30) / widest) return fail(QLORA_ERR_SHAPE, "M * width exceeds 2^30 elements");
+  const int64_t mpad = (M + 31) / 32 * 32, wpad = (widest + 63) / 64 * 64;
+  if (widest > 0 && mpad > ((int64_t)1 << 30) / wpad)
+    return fail(QLORA_ERR_SHAPE, "M * width, padded to whole MFMA fragments, exceeds 2^30 elements");
   return QLORA_OK;
 }
 
@@ -143,22 +149,27 @@ int dropout_setup(int32_t r, float alpha, double p, uint64_t seed, qlora::DropMa
 }
 
 struct BwdLayout {
-  size_t u, v, part, cpart, total;  // part: U~ / V~ split-K partials; cpart: dA / dB row-chunk partials
+  size_t u, v, dyt, part, cpart, total;  // part: U~ / V~ split-K partials; cpart: dA / dB row-chunk partials
   int nmc;
-  size_t req;   // bytes required (U~, V~ and the reduction partials)
+  size_t req;   // bytes required (U~, V~, the tiled dY and the reduction partials)
   size_t gemm;  // split-reduction tiles of the dX product, from `part` on
 };
 
+// [U~][V~][fragment-tiled dY][U~ / V~ partials][dA / dB partials]; U~ and V~
+// only with an adapter (r > 0)
 BwdLayout bwd_layout(int64_t M, int64_t n_out, int64_t k_in, int32_t r) {
   BwdLayout L{};
   if (M <= 0) return L;
+  const size_t urow = r > 0 ? round_up((size_t)M * r * 2) : 0;
+  L.u = 0;
+  L.v = urow;
+  L.dyt = 2 * urow;
+  L.part = L.dyt + round_up(qlora::tiled_bytes(M, n_out));
+  L.req = L.part;
   if (r > 0) {
     const int mch = qlora::coldot_chunk_rows();
     L.nmc = (int)((M + mch - 1) / mch);
     const int64_t widest = n_out > k_in ? n_out : k_in;
-    L.u = 0;
-    L.v = L.u + round_up((size_t)M * r * 2);
-    L.part = L.v + round_up((size_t)M * r * 2);
     // U~ and V~ split-K partials share one region (stream order); the dB and
     // dA row-chunk partials share another (dB's are produced alongside V~'s)
     const size_t part = std::max(qlora::rowdot_part_bytes(M, k_in, r), qlora::rowdot_part_bytes(M, n_out, r));
@@ -237,13 +248,15 @@ size_t qlora_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, int
   if (M < 0 || n_out < 0 || k_in < 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
   if (op == QLORA_OP_FWD) {
     if (M == 0) return 0;
-    // [U~][U~ partials | split-reduction tiles of the main product]
+    // [U~][fragment-tiled X (GEMM path)][U~ partials | split-reduction tiles of the main product]
+    const bool gemm_path = M > qlora::skinny_max_tokens();
     const size_t u = r > 0 ? round_up((size_t)M * r * 2) : 0;
+    const size_t xt = gemm_path ? round_up(qlora::tiled_bytes(M, k_in)) : 0;
     const size_t upart = r > 0 ? round_up(qlora::rowdot_part_bytes(M, k_in, r)) : 0;
     const int cus = qlora::device_compute_units();
-    const size_t gpart = round_up(M > qlora::skinny_max_tokens() ? qlora::gemm_part_bytes(M, n_out, k_in, cus)
-                                                                  : qlora::skinny_part_bytes(M, n_out, k_in, cus));
-    return u + std::max(upart, gpart);
+    const size_t gpart = round_up(gemm_path ? qlora::gemm_part_bytes(M, n_out, k_in, cus)
+                                            : qlora::skinny_part_bytes(M, n_out, k_in, cus));
+    return u + xt + std::max(upart, gpart);
   }
   if (op == QLORA_OP_BWD) return bwd_layout(M, n_out, k_in, r).total;
   return 0;
@@ -324,26 +337,31 @@ static int linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t
   if (U_out && !aligned16(U_out)) return fail(QLORA_ERR_ALIGN, "U_out must be 16-byte aligned");
   uint16_t* U = nullptr;
   float* part = nullptr;
-  // workspace: [U~ when U_out is NULL][split-K partials of U~, later reused
-  // for the split-reduction tiles of the main product (optional)]
+  uint16_t* Xt = nullptr;
+  // workspace: [U~ when U_out is NULL][fragment-tiled X, on the GEMM path]
+  // [split-K partials of U~, later reused for the split-reduction tiles of
+  // the main product (optional)]
+  const bool gemm_path = M > qlora::skinny_max_tokens();
   const size_t ubytes = r > 0 && !U_out ? round_up((size_t)M * r * 2) : 0;
-  if (r > 0) {
-    const size_t pbytes = qlora::rowdot_part_bytes(M, w->k_in, r);
-    if (ubytes + pbytes > 0) {
-      if (!ws || ws_bytes < ubytes + pbytes) return fail(QLORA_ERR_WORKSPACE, "forward workspace too small");
-      if (!aligned16(ws)) return fail(QLORA_ERR_ALIGN, "workspace must be 16-byte aligned");
-    }
-    char* base = static_cast<char*>(ws);
-    U = U_out ? U_out : reinterpret_cast<uint16_t*>(base);
-    if (pbytes) part = reinterpret_cast<float*>(base + ubytes);
+  const size_t xbytes = gemm_path ? round_up(qlora::tiled_bytes(M, w->k_in)) : 0;
+  const size_t pbytes = r > 0 ? qlora::rowdot_part_bytes(M, w->k_in, r) : 0;
+  if (ubytes + xbytes + pbytes > 0) {
+    if (!ws || ws_bytes < ubytes + xbytes + pbytes) return fail(QLORA_ERR_WORKSPACE, "forward workspace too small");
+    if (!aligned16(ws)) return fail(QLORA_ERR_ALIGN, "workspace must be 16-byte aligned");
   }
+  char* base = static_cast<char*>(ws);
+  if (r > 0) U = U_out ? U_out : reinterpret_cast<uint16_t*>(base);
+  if (xbytes) Xt = reinterpret_cast<uint16_t*>(base + ubytes);
+  if (pbytes) part = reinterpret_cast<float*>(base + ubytes + xbytes);
   hipError_t e;
   if (r > 0 && w->k_in > 0) {
-    e = qlora::launch_lora_down(X, (int)M, (int)w->k_in, A, r, s, U, part, dm, f16, stream);
+    // U~, and on the GEMM path the tiled X, in one pass over X
+    e = qlora::launch_lora_down(X, (int)M, (int)w->k_in, A, r, s, U, part, dm, f16, Xt, stream);
     if (e != hipSuccess) return hip_fail(e, "lora_down launch");
-  } else if (r > 0) {
-    // k_in == 0: X A^T is an empty sum
-    if ((e = qlora::launch_zero_u16(U, M * r, stream)) != hipSuccess) return hip_fail(e, "zero U");
+  } else {
+    if (r > 0 && (e = qlora::launch_zero_u16(U, M * r, stream)) != hipSuccess) return hip_fail(e, "zero U");
+    if (Xt && (e = qlora::launch_tile_act(X, (int)M, (int)w->k_in, true, Xt, stream)) != hipSuccess)
+      return hip_fail(e, "tile X launch");
   }
   if (M <= qlora::skinny_max_tokens()) {
     // few tokens: bound by reading the packed weight; decode straight into
@@ -358,20 +376,19 @@ static int linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t
     // without room the kernel runs unsplit
     const size_t kbytes = qlora::skinny_part_bytes(M, w->n_out, w->k_in, qlora::device_compute_units());
     if (kbytes && ws && aligned16(ws) && ws_bytes >= ubytes + kbytes)
-      k.part = reinterpret_cast<float*>(static_cast<char*>(ws) + ubytes);
+      k.part = reinterpret_cast<float*>(base + ubytes);
     e = qlora::launch_skinny_fwd(k, stream);
     return e == hipSuccess ? QLORA_OK : hip_fail(e, "few-token forward launch");
   }
   qlora::GemmArgs g{};
-  g.act = X; g.ld_act = w->k_in; g.M = (int)M; g.R = (int)w->k_in; g.C = (int)w->n_out;
+  g.act_t = Xt; g.kbp = qlora::tiled_kbp(w->k_in); g.M = (int)M; g.R = (int)w->k_in; g.C = (int)w->n_out;
   g.codes = w->codes; g.q8 = w->absmax_q8; g.s2 = w->absmax_scale; g.K = (int)w->k_in;
   g.lora_act = U; g.lora_w = B; g.r = r;
   g.out = Y; g.ld_out = w->n_out;
   g.nf4 = qlora::nf4_consts();
   g.f16 = f16;
   const size_t gbytes = qlora::gemm_part_bytes(M, w->n_out, w->k_in, qlora::device_compute_units());
-  if (gbytes && ws && aligned16(ws) && ws_bytes >= ubytes + gbytes)
-    g.part = reinterpret_cast<float*>(static_cast<char*>(ws) + ubytes);
+  if (gbytes && ws && ws_bytes >= ubytes + xbytes + gbytes) g.part = reinterpret_cast<float*>(base + ubytes + xbytes);
   e = qlora::launch_gemm_fwd(g, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e, "forward GEMM launch");
 }
@@ -399,7 +416,7 @@ static int linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const u
   }
   if (U && !aligned16(U)) return fail(QLORA_ERR_ALIGN, "U must be 16-byte aligned");
   const BwdLayout L = bwd_layout(M, N, K, r);
-  if (r > 0 && M > 0) {
+  if (M > 0 && N > 0 && K > 0) {
     if (!ws || ws_bytes < L.req) return fail(QLORA_ERR_WORKSPACE, "backward workspace too small");
     if (!aligned16(ws)) return fail(QLORA_ERR_ALIGN, "workspace must be 16-byte aligned");
   }
@@ -422,6 +439,7 @@ static int linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const u
   uint16_t* Ut = nullptr;
   uint16_t* Vt = nullptr;
   float* part = nullptr;
+  uint16_t* dYt = reinterpret_cast<uint16_t*>(base + L.dyt);
   if (r > 0) {
     Vt = reinterpret_cast<uint16_t*>(base + L.v);
     part = reinterpret_cast<float*>(base + L.part);
@@ -429,21 +447,25 @@ static int linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const u
       Ut = const_cast<uint16_t*>(U);
     } else {
       Ut = reinterpret_cast<uint16_t*>(base + L.u);
-      if ((e = qlora::launch_lora_down(X, (int)M, (int)K, A, r, s, Ut, part, dm, f16, stream)) != hipSuccess)
+      if ((e = qlora::launch_lora_down(X, (int)M, (int)K, A, r, s, Ut, part, dm, f16, nullptr, stream)) != hipSuccess)
         return hip_fail(e, "lora_down launch");
     }
-    // V~ = bf16(s dY B) and dB = dY^T U~ (stored [N x r]): both read dY
+    // V~ = bf16(s dY B) and dB = dY^T U~ (stored [N x r]): both read dY; the
+    // V~ pass also writes the tiled dY the dX product reads
     float* cpart = reinterpret_cast<float*>(base + L.cpart);
-    if ((e = qlora::launch_vt_and_db(dY, (int)M, (int)N, B, Ut, r, s, Vt, part, cpart, dB, f16, stream)) != hipSuccess)
+    if ((e = qlora::launch_vt_and_db(dY, (int)M, (int)N, B, Ut, r, s, Vt, part, cpart, dB, f16, dYt, stream)) !=
+        hipSuccess)
       return hip_fail(e, "V~ / dB launch");
     // dA = V~^T (mask * X)  ([r x K])
     if ((e = qlora::launch_coldot(Vt, r, X, (int)M, (int)K, cpart, dm, f16, stream)) != hipSuccess)
       return hip_fail(e, "dA partials launch");
     if ((e = qlora::launch_finalize(cpart, L.nmc, r, (int)K, dA, false, stream)) != hipSuccess)
       return hip_fail(e, "dA finalize launch");
+  } else if ((e = qlora::launch_tile_act(dY, (int)M, (int)N, false, dYt, stream)) != hipSuccess) {
+    return hip_fail(e, "tile dY launch");
   }
   qlora::GemmArgs g{};
-  g.act = dY; g.ld_act = N; g.M = (int)M; g.R = (int)N; g.C = (int)K;
+  g.act_t = dYt; g.kbp = qlora::tiled_kbp(N); g.M = (int)M; g.R = (int)N; g.C = (int)K;
   g.codes = w->codes; g.q8 = w->absmax_q8; g.s2 = w->absmax_scale; g.K = (int)K;
   g.lora_act = Vt; g.lora_w = A; g.r = r;
   g.out = dX; g.ld_out = K;
@@ -452,8 +474,7 @@ static int linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const u
   g.f16 = f16;
   // split-reduction tiles, from L.part on (U~ / V~ partials and dA / dB
   // partials are consumed by now); without room the product runs unsplit
-  if (L.gemm && ws && aligned16(ws) && ws_bytes >= L.part + L.gemm)
-    g.part = reinterpret_cast<float*>(static_cast<char*>(ws) + L.part);
+  if (L.gemm && ws && ws_bytes >= L.part + L.gemm) g.part = reinterpret_cast<float*>(base + L.part);
   e = qlora::launch_gemm_dx(g, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e, "dX GEMM launch");
 }

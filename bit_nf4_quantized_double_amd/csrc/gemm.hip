@@ -8,16 +8,17 @@
 // Wbf is never materialised.  Each 64-deep reduction step a workgroup reads
 // the packed codes of the W tile it needs, decodes them to bf16
 // (round-to-nearest-even of level * block scale) in registers and stores the
-// tile in LDS, where all four waves read it as the MFMA B operand.  The rank-r
-// adapter term is one extra reduction step into the same accumulators.
+// tile in LDS, where all four consumer waves read it as the MFMA B operand.
+// The rank-r adapter term is one extra reduction step into the same
+// accumulators.
 //
-// Workgroup tile 256 (rows) x 128 (columns), 4 waves stacked along the rows;
-// each wave owns 64 rows x 128 columns = 2 x 4 tiles of
+// Workgroup tile 256 (rows) x 128 (columns), 4 consumer waves stacked along
+// the rows; each owns 64 rows x 128 columns = 2 x 4 tiles of
 // v_mfma_f32_32x32x16_bf16.  A wave's activation rows are private to it: it
-// copies them with coalesced buffer_load ... lds (8 lanes per 128-byte row
-// slice, straight into a wave-private LDS ring, no VGPR round trip) and reads
-// them back in MFMA operand layout.  The decoded W tile is double-buffered
-// and shared by the four waves (one barrier per step).
+// loads them from the fragment-tiled copy of X or dY (gemm_args.h), one
+// coalesced 1 KB load per MFMA operand, into registers two steps ahead.  The
+// decoded W tile is the only thing in LDS (a 4-deep ring; one barrier per two
+// steps).
 //
 //   NT (forward): W tile = 128 rows n x 64 k, stored [n][k], read with
 //                 ds_read_b128.
@@ -82,7 +83,7 @@ struct Tile {
 
 // ---- global -> register loads (raw buffer loads: out of range reads 0) ----
 struct Srcs {
-  __amdgpu_buffer_rsrc_t act, codes, q8, s2;
+  __amdgpu_buffer_rsrc_t codes, q8, s2;
   __amdgpu_buffer_rsrc_t lora_act, lora_w;  // U~ or V~ [M x r]; B [C x r] (NT) or A [r x K] (NN)
 };
 
@@ -92,7 +93,6 @@ __device__ __forceinline__ Srcs make_srcs(const GemmArgs& a) {
   // W is [n_out x k_in]: n_out = C (forward) or R (dX)
   const uint64_t wn = (uint64_t)a.K * (uint64_t)(NN ? a.R : a.C);
   const uint32_t nb = (uint32_t)(wn >> 6);
-  s.act = make_rsrc(a.act, (uint32_t)((uint64_t)a.M * a.ld_act * 2));
   s.codes = make_rsrc(a.codes, (uint32_t)(wn >> 1));
   s.q8 = make_rsrc(a.q8, nb);
   s.s2 = make_rsrc(a.s2, ((nb + 255) >> 8) * 4);
@@ -123,12 +123,31 @@ struct CodeSeg {
   float s2;    // second-level scale of its group
 };
 
+// The W-tile segment (row n of W, 32 weights from reduction offset k) that
+// producer thread tid decodes.  NT: 128 rows x 64; lanes l and l ^ 16 of a
+// producer wave hold the two halves of one 64-weight block (a 16-lane row
+// swap exchanges their halves of the block's table).  NN: 64 rows x 128;
+// threads tid and tid ^ 1 share a block (a quad swap exchanges them).
+template <bool NN>
+__device__ __forceinline__ void seg_of(int tid, int& row, int& half) {
+  if (NN) {
+    row = tid >> 2;
+    half = tid & 3;  // 32-weight segment of the 128-wide row
+  } else {
+    const int w = tid >> 6, l = tid & 63;
+    row = 32 * w + (l & 15) + 16 * (l >> 5);
+    half = (l >> 4) & 1;
+  }
+}
+
 template <bool NN>
 __device__ __forceinline__ CodeSeg load_codes(const GemmArgs& a, const Srcs& src, int c0, int r0, int tid) {
+  int row, half;
+  seg_of<NN>(tid, row, half);
   int n, k;
   bool ok;
-  if (NN) { n = r0 + (tid >> 2); k = c0 + (tid & 3) * 32; ok = n < a.R && k < a.C; }
-  else    { n = c0 + (tid >> 1); k = r0 + (tid & 1) * 32; ok = n < a.C && k < a.R; }
+  if (NN) { n = r0 + row; k = c0 + half * 32; ok = n < a.R && k < a.C; }
+  else    { n = c0 + row; k = r0 + half * 32; ok = n < a.C && k < a.R; }
   const uint32_t e = (uint32_t)n * (uint32_t)a.K + (uint32_t)k;  // weight index
   CodeSeg cs;  // out of range: all zero, which decodes to zeros
   cs.code = buf_load16(src.codes, ok ? (e >> 1) : kOOB);
@@ -137,72 +156,52 @@ __device__ __forceinline__ CodeSeg load_codes(const GemmArgs& a, const Srcs& src
   return cs;
 }
 
-template <bool NN, typename E>
-__device__ __forceinline__ void decode_store(uint16_t* s, const CodeSeg& cs, const float th[8],
-                                             const LaneMask& lm, int tid) {
-  const Lut L = build_lut<LutPartner::kXor1, E>(th, (float)cs.q * cs.s2);  // a' = fp32(q8 * s2)
-  const uint4 w0 = decode8_lut(L, cs.code.x, lm);
-  const uint4 w1 = decode8_lut(L, cs.code.y, lm);
-  const uint4 w2 = decode8_lut(L, cs.code.z, lm);
-  const uint4 w3 = decode8_lut(L, cs.code.w, lm);
-  if (NN) {
-    const int row = tid >> 2, c = (tid & 3) * 32;
-    *reinterpret_cast<uint4*>(s + nn_off(row, c + 0)) = w0;
-    *reinterpret_cast<uint4*>(s + nn_off(row, c + 8)) = w1;
-    *reinterpret_cast<uint4*>(s + nn_off(row, c + 16)) = w2;
-    *reinterpret_cast<uint4*>(s + nn_off(row, c + 24)) = w3;
-  } else {
-    const int row = tid >> 1, c = (tid & 1) * 4;
-    *reinterpret_cast<uint4*>(s + kt_off(row, c + 0)) = w0;
-    *reinterpret_cast<uint4*>(s + kt_off(row, c + 1)) = w1;
-    *reinterpret_cast<uint4*>(s + kt_off(row, c + 2)) = w2;
-    *reinterpret_cast<uint4*>(s + kt_off(row, c + 3)) = w3;
-  }
-}
-
-// ---- activations: coalesced copies into a wave-private LDS ring ----------
-// One stage = the wave's 64 rows x 64 reduction columns (8 KB), row r at
-// byte r * 128 with chunk lc stored at physical chunk lc ^ swz(r).
-constexpr uint32_t kActStage = 64 * 128;
-constexpr int kActStages = 3;
-
-// Byte offsets of the 8 rows this lane copies (row 8j + (lane >> 3) of the
-// wave's 64 rows for copy instruction j; kOOB past the last row).
-struct ActRows {
-  uint32_t off[8];
+// Per-lane decode constants: the half of the levels this lane's table share
+// covers, and the lookup masks.
+struct DecodeConsts {
+  float th[8];
+  LaneMask lm;   // NN lookup (byte-spread order)
+  EoConsts eo;   // NT lookup (element order)
 };
 
-__device__ __forceinline__ ActRows act_rows(const GemmArgs& a, int row0, int lane) {
-  ActRows ar;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int m = row0 + 8 * j + (lane >> 3);
-    ar.off[j] = m < a.M ? (uint32_t)m * (uint32_t)a.ld_act * 2u : kOOB;
-  }
-  return ar;
+template <bool NN>
+__device__ __forceinline__ DecodeConsts decode_consts(const Nf4Consts& nf4, int tid) {
+  DecodeConsts dc;
+  int row, half;
+  seg_of<NN>(tid, row, half);
+  const bool odd = NN ? (half & 1) : half;  // the lane building levels 8..15
+  lane_levels(nf4, odd, dc.th);
+  dc.lm = lane_mask(odd);
+  dc.eo = eo_consts();
+  return dc;
 }
 
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
-// Issue the 8 coalesced copies of one step (reduction columns r0..r0+63) into
-// the LDS stage at byte offset `stage`.  Lane l of copy j lands at stage +
-// 1024 j + 16 l = row (8j + l / 8), physical chunk l % 8.
-__device__ __forceinline__ void copy_act(const GemmArgs& a, const Srcs& src, const ActRows& rows, lds_u8* stage,
-                                         int r0, int lane) {
-  const uint32_t pc = lane & 7, rl = lane >> 3;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t lc = pc ^ ((rl ^ (uint32_t)j) & 7u);  // logical chunk = pc ^ swz(8j + rl)
-    const int k = r0 + 8 * (int)lc;
-    const uint32_t off = k < a.R ? rows.off[j] + 2u * (uint32_t)k : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.act, stage + 1024u * j, 16, off, 0, 0, 0);
+// Decode 32 weights and store them in the W tile.  NT: the element-order
+// lookup (16 permutes + 7 operations per 8 codes) leaves each group of 8
+// reduction columns in the order 0, 2, 4, 6, 1, 3, 5, 7 -- the tiled X copy
+// the forward reads carries the same order, so the products pair up.  NN:
+// the byte-spread lookup keeps the natural column order (the output
+// columns).
+template <bool NN, typename E>
+__device__ __forceinline__ void decode_store(uint16_t* s, const CodeSeg& cs, const DecodeConsts& dc, int tid) {
+  int row, half;
+  seg_of<NN>(tid, row, half);
+  const float scale = (float)cs.q * cs.s2;  // a' = fp32(q8 * s2)
+  if (NN) {
+    const Lut L = build_lut<LutPartner::kXor1, E>(dc.th, scale);
+    const int c = half * 32;
+    *reinterpret_cast<uint4*>(s + nn_off(row, c + 0)) = decode8_lut(L, cs.code.x, dc.lm);
+    *reinterpret_cast<uint4*>(s + nn_off(row, c + 8)) = decode8_lut(L, cs.code.y, dc.lm);
+    *reinterpret_cast<uint4*>(s + nn_off(row, c + 16)) = decode8_lut(L, cs.code.z, dc.lm);
+    *reinterpret_cast<uint4*>(s + nn_off(row, c + 24)) = decode8_lut(L, cs.code.w, dc.lm);
+  } else {
+    const Lut L = build_lut<LutPartner::kRows16, E>(dc.th, scale);
+    const int c = half * 4;
+    *reinterpret_cast<uint4*>(s + kt_off(row, c + 0)) = decode8_lut_hl(L, cs.code.x, dc.eo);
+    *reinterpret_cast<uint4*>(s + kt_off(row, c + 1)) = decode8_lut_hl(L, cs.code.y, dc.eo);
+    *reinterpret_cast<uint4*>(s + kt_off(row, c + 2)) = decode8_lut_hl(L, cs.code.z, dc.eo);
+    *reinterpret_cast<uint4*>(s + kt_off(row, c + 3)) = decode8_lut_hl(L, cs.code.w, dc.eo);
   }
-}
-
-// A operand for MFMA sub-step ks, rows 32 i .. 32 i + 31 of the wave's slice.
-__device__ __forceinline__ uint4 load_afrag(const uint16_t* st, int i, int ks, int lane) {
-  const uint32_t r = 32 * i + (lane & 31);
-  return *reinterpret_cast<const uint4*>(st + r * 64u + (((2u * ks + (lane >> 5)) ^ swz(r)) << 3));
 }
 
 // B operand for MFMA sub-step ks, columns col0..col0+31.
@@ -224,60 +223,20 @@ __device__ __forceinline__ uint4 load_bfrag(const uint16_t* s, int col0, int ks,
   }
 }
 
-// One reduction step of MFMAs: A operand from the wave's activation stage,
-// B operand from the shared W tile.  If cs is given, the next W tile is
-// decoded into s_next alongside: MFMA sub-step ks is paired with code dword ks
-// of this thread's 32 weights, so the decode VALU work issues while the matrix
-// core runs (sub-steps are fenced so the compiler keeps that pairing).  B
-// operands of sub-step ks + 1 are read during sub-step ks.
-template <bool NN>
-__device__ __forceinline__ void store_w8(uint16_t* s_next, const uint4& w, int q, int tid) {
-  if (NN) *reinterpret_cast<uint4*>(s_next + nn_off(tid >> 2, (tid & 3) * 32 + 8 * q)) = w;
-  else *reinterpret_cast<uint4*>(s_next + kt_off(tid >> 1, (tid & 1) * 4 + q)) = w;
-}
+// ---- A operand: fragments of the tiled activation copy ---------------------
+// A wave's 64 rows are two 32-row fragment blocks; a 64-deep step of them is
+// 2 x 4 fragments, each one coalesced 16-byte-per-lane load into the
+// registers the MFMA reads.  Rows past M (whole blocks past the copy) and
+// steps past the reduction read zeros.
+struct AFrags {
+  uint4 f[4][2];  // [sub-step ks][row half i]
+};
 
-template <bool NN, bool DECODE, typename E>
-__device__ __forceinline__ void mma_step(f32x16 (&acc)[2][4], const uint16_t* act, const uint16_t* sw,
-                                         uint16_t* s_next, const CodeSeg& cs, const float th[8],
-                                         const LaneMask& lm, int tid, int lane) {
-  uint4 nb[4], na[2];
+// B operands of one 16-deep sub-step from the W tile in LDS.
+template <bool NN>
+__device__ __forceinline__ void read_b(const uint16_t* sw, int ks, int lane, uint4 (&b)[4]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) nb[j] = load_bfrag<NN>(sw, 32 * j, 0, lane);
-#pragma unroll
-  for (int i = 0; i < 2; ++i) na[i] = load_afrag(act, i, 0, lane);
-  Lut L;
-  if (DECODE) L = build_lut<LutPartner::kXor1, E>(th, (float)cs.q * cs.s2);  // a' = fp32(q8 * s2)
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    uint4 bf[4], af[2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bf[j] = nb[j];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) af[i] = na[i];
-    if (ks < 3) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) nb[j] = load_bfrag<NN>(sw, 32 * j, ks + 1, lane);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) na[i] = load_afrag(act, i, ks + 1, lane);
-    }
-    if (DECODE) {
-      const uint32_t d = ks == 0 ? cs.code.x : ks == 1 ? cs.code.y : ks == 2 ? cs.code.z : cs.code.w;
-      store_w8<NN>(s_next, decode8_lut(L, d, lm), ks, tid);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = E::mfma32(E::vec(af[i]), E::vec(bf[j]), acc[i][j]);
-    if (DECODE) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // then up to 4 VALU
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
+  for (int j = 0; j < 4; ++j) b[j] = load_bfrag<NN>(sw, 32 * j, ks, lane);
 }
 
 // s_waitcnt with only a vmcnt limit (gfx9 encoding: vmcnt in bits 3:0 and
@@ -288,12 +247,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Step hand-off barrier of the main loop.  A plain __syncthreads() carries a
-// workgroup release fence, which would also drain the activation copies
-// still in flight for later steps; here each wave first waits only for its
-// own LDS operations (lgkmcnt(0): decoded-tile stores, operand reads), and
-// producers additionally wait for the copies the next step needs before
-// calling this (wait_vmcnt).
+// Hand-off barrier of the main loop: each wave first waits for its own LDS
+// operations only (lgkmcnt(0): decoded-tile stores, operand reads), not for
+// the global loads it has in flight for later steps (a plain
+// __syncthreads() would drain those too).
 __device__ __forceinline__ void step_barrier() {
   __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0) only
   __builtin_amdgcn_s_barrier();
@@ -317,25 +274,49 @@ __device__ __forceinline__ void tile_coords(int& tm, int& tn) {
   tm = band * RB + within % rows;
 }
 
+// Steps per barrier phase and the W ring: producers decode the two steps of
+// phase p + 1 while consumers multiply those of phase p.
+constexpr int kPhase = 2;
+constexpr int kWBufs = 2 * kPhase;
+// Output staging of the epilogue: each consumer wave's 64 x 128 tile, rows
+// padded to 136 elements so the two rows one 16-bit store instruction
+// touches fall in different LDS banks.
+constexpr int kOutPitch = BN + 8;
+constexpr int kOutElems = 4 * 64 * kOutPitch;
+
+template <bool NN>
+struct Lds {
+  static constexpr int kRing = kWBufs * Tile<NN>::kElems;
+  static constexpr int kMain = kRing > kOutElems ? kRing : kOutElems;  // ring, then output staging
+  static constexpr int kAdapter = Tile<NN>::kElems;                    // adapter W-side operand
+};
+
+// A-operand fragments in flight: NT two steps ahead; NN one (its transposing
+// B reads need more registers, and two steps would spill).
+template <bool NN>
+struct ARing {
+  static constexpr int kSteps = NN ? 1 : 2;
+};
+
 // Wave-specialised workgroup of 8 waves, two per SIMD:
-//   waves 0-3 (consumers) run only the MFMAs of their 64 x 128 output slice;
-//   waves 4-7 (producers) copy activations for consumer (wave - 4) into its
-//   LDS ring, load codes and decode the next W tile.
-// The SIMD co-issues a producer's VALU work with its consumer's MFMAs, so the
-// decode runs in the matrix core's shadow without hand interleaving.  One
-// barrier per 64-deep step hands tile s + 1 (and activation stage s + 1) from
-// producers to consumers.
-//
-// Producer pipeline at step s: load codes of step s + 2 (2-slot register
-// ring), copy activations of step s + 2 (3-stage LDS ring), decode codes of
-// step s + 1 into W buffer (s + 1) % 2, then wait for the copies of step s + 1.
+//   waves 0-3 (consumers) run the MFMAs of their 64 x 128 output slice; they
+//   load their activation fragments themselves from the tiled copy (one or
+//   two steps ahead, in registers) and read the shared decoded W tile from
+//   LDS;
+//   waves 4-7 (producers) load codes (four steps ahead) and decode W tiles
+//   into a 4-deep LDS ring.
+// The SIMD co-issues a producer's VALU decode with its consumer's MFMAs.  The
+// LDS carries only the decoded weight: 16 KB written and 64 KB read per
+// 64-deep step, against 48 KB and 96 KB when the activations were staged
+// there too -- LDS writes run at about 64 B per clock per CU on this GPU and
+// were the bottleneck.  One barrier per two steps.  The adapter term goes
+// first, from its own LDS region filled during the prologue, so its loads
+// overlap the first decode; the output leaves through LDS as coalesced
+// 16-byte stores.
 template <bool NN, typename E>
 __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
-  // Two distinct LDS objects: the compiler can then tell that the producers'
-  // stores of decoded W tiles never alias the activation copies in flight
-  // (otherwise it drains every copy before each such store).
-  __shared__ __attribute__((aligned(16))) uint16_t s_w[2 * Tile<NN>::kElems];
-  __shared__ __attribute__((aligned(16))) uint8_t s_act[4 * kActStages * kActStage];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[Lds<NN>::kMain];
+  __shared__ __attribute__((aligned(16))) uint16_t s_ad[Lds<NN>::kAdapter];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool producer = wave >= 4;
   const int slice = wave & 3;               // consumer slice this wave works on / feeds
@@ -344,32 +325,29 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
   tile_coords(tm, tn);
   const int m0 = tm * BM, c0 = tn * BN;
   const int row0 = m0 + 64 * slice;
-  uint16_t* const w_buf0 = s_w;
-  uint16_t* const w_buf1 = s_w + Tile<NN>::kElems;
-  auto act_lds = [&](int st) {
-    return (lds_u8*)s_act + ((uint32_t)slice * kActStages + st) * kActStage;
-  };
-  auto act_ptr = [&](int st) {
-    return reinterpret_cast<uint16_t*>(s_act + ((uint32_t)slice * kActStages + st) * kActStage);
-  };
+  auto wbuf = [&](int step) { return s_w + (step & (kWBufs - 1)) * Tile<NN>::kElems; };
 
   const int nsteps = (a.R + 63) / 64;
   // Split reduction: this workgroup takes steps [s0, s0 + nloc) of the
-  // nsteps; every split loops over the same even step count nst (an all-zero
-  // step adds nothing).
+  // nsteps; every split loops over the same step count nst, a multiple of 2
+  // phases (all-zero steps add nothing).
   const int kz = blockIdx.z;
   const int spl = a.ksplit > 1 ? (nsteps + a.ksplit - 1) / a.ksplit : nsteps;
   const int s0 = kz * spl;
   const int nloc = max(0, min(spl, nsteps - s0));
-  const int nst = (spl + 1) & ~1;
-  const int kend = ((nsteps + 1) & ~1) * 64;  // >= R: loads there read zeros
+  const int nst = (spl + 2 * kPhase - 1) & ~(2 * kPhase - 1);
+  const int kend = ((nsteps + 1) & ~1) * 64;  // >= R: code loads there read zeros
   // All tiles walk the reduction in the same order, so the workgroups of
   // one XCD read the same activation / weight slices at about the same time
   // and share them in L2.
   auto kofs = [&](int step) {  // reduction offset of logical step; >= R past the end
     return step < nloc ? (s0 + step) * 64 : kend;
   };
-  auto stage_of = [](int step) { return step % kActStages; };
+  // The adapter term (split 0 only): r extra reduction columns
+  // j = 16 ks + 8 h + e.  With LoRA dropout on dX it is masked before the
+  // main reduction adds dY Wbf (mask * (V~ A)).
+  const bool adapter = a.r > 0 && kz == 0;
+  const bool drop_first = NN && a.drop.thr != 0 && adapter;
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -379,17 +357,20 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // ---- adapter step: r extra reduction columns j = 16 ks + 8 h + e --------
-  // (sw: a W buffer, sa: this slice's activation stage, both free)
-  auto adapter_step = [&](uint16_t* sw, uint16_t* sa) {
-    __syncthreads();
-    if (producer) {
-      const Srcs src = make_srcs<NN>(a);
-      // All loads of the fill are issued before any LDS store (16-byte
-      // chunks of 8 ranks; out of range reads zero), so the fill costs one
-      // memory latency, not one per element.
-      const bool vec = (a.r & 7) == 0;
-      // W-side operand: NT: B[n][j] -> sw[col][j]; NN: A[j][c] -> sw[j][col]
+  const Srcs src = make_srcs<NN>(a);
+  const bool vec = (a.r & 7) == 0;
+
+  if (producer) {
+    const DecodeConsts dc = decode_consts<NN>(a.nf4, ptid);
+    // codes of step s in slot s % 4, loaded four steps before their decode;
+    // each slot is 3 loads, so before decoding step s the loads of steps
+    // s + 1 .. s + 3 may still be in flight (vmcnt <= 9)
+    CodeSeg cr[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cr[u] = load_codes<NN>(a, src, c0, kofs(u), ptid);
+    if (adapter) {
+      // the adapter's W-side operand into its region (NT: B[n][j] ->
+      // s_ad[col][j]; NN: A[j][c] -> s_ad[j][col]); loads in flight together
       uint4 wv[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -402,53 +383,21 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
           wv[u] = load_e16x8(src.lora_w, (uint32_t)j * (uint32_t)a.K + (uint32_t)c, j < a.r && c < a.C, 8, true);
         }
       }
-      // token-side operand: U~ / V~ rows of this producer's consumer slice
-      uint4 av[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int idx = lane + 64 * u;  // 0 .. 511: row idx >> 3, chunk idx & 7
-        const int rr = idx >> 3, jc = idx & 7, m = row0 + rr;
-        av[u] = load_e16x8(src.lora_act, (uint32_t)m * (uint32_t)a.r + 8u * jc, m < a.M, a.r - 8 * jc, vec);
-      }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int idx = ptid + u * kThreads;
-        if (!NN) {
-          const int col = idx >> 3, jc = idx & 7;
-          *reinterpret_cast<uint4*>(sw + kt_off(col, jc)) = wv[u];
-        } else {
-          const int j = idx >> 4, cc = idx & 15;
-          *reinterpret_cast<uint4*>(sw + nn_off(j, 8 * cc)) = wv[u];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t idx = lane + 64u * u, rr = idx >> 3, jc = idx & 7;
-        *reinterpret_cast<uint4*>(sa + rr * 64u + ((jc ^ swz(rr)) << 3)) = av[u];
+        if (!NN) *reinterpret_cast<uint4*>(s_ad + kt_off(idx >> 3, idx & 7)) = wv[u];
+        else *reinterpret_cast<uint4*>(s_ad + nn_off(idx >> 4, 8 * (idx & 15))) = wv[u];
       }
     }
-    __syncthreads();
-    if (!producer) {
-      const CodeSeg none{};
-      const float th0[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      const LaneMask lm0{0, 0, 0};
-      mma_step<NN, false, E>(acc, sa, sw, sw, none, th0, lm0, 0, lane);
-    }
-  };
-
-  // ---- dX with LoRA dropout: the adapter's part of dX passes through the
-  // dropout mask of the adapter input, mask * (V~ A).  The adapter step then
-  // runs first, alone in the accumulators, which are masked before the main
-  // reduction adds dY Wbf.  The producer of each slice draws the slice's
-  // 64 x 128 keep bytes into activation stage 1 meanwhile.
-  const bool drop_first = NN && a.drop.thr != 0 && a.r > 0 && kz == 0;
-  if (drop_first) {
-    adapter_step(w_buf0, act_ptr(0));
-    uint8_t* keep = reinterpret_cast<uint8_t*>(act_ptr(1));
-    if (producer) {
+    if (drop_first) {
+      // keep bytes of the consumer slice this producer feeds, 64 x 128, into
+      // W buffers 2-3 (not decoded into before the mask is applied)
+      uint8_t* keep = reinterpret_cast<uint8_t*>(wbuf(2)) + slice * (64 * BN);
+      const int plane = tid & 63;
 #pragma unroll 4
       for (int t = 0; t < 32; ++t) {  // (row, 4-column group) pairs q = lane + 64 t
-        const int q = lane + 64 * t, rl = q >> 5, g = q & 31;
+        const int q = plane + 64 * t, rl = q >> 5, g = q & 31;
         const uint64_t e = (uint64_t)(row0 + rl) * (uint64_t)a.C + (uint64_t)(c0 + 4 * g);
         const uint64_t ctr = e >> 2;
         const uint4 u = philox4x32_10(make_uint4((uint32_t)ctr, (uint32_t)(ctr >> 32), 0u, 0u), a.drop.k0, a.drop.k1);
@@ -457,72 +406,136 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
         *reinterpret_cast<uint32_t*>(keep + 4 * q) = kb;  // byte rl * 128 + 4 g + i
       }
     }
-    __syncthreads();
-    if (!producer) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int rl = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), cl = 32 * j + (lane & 31);
-            if (!keep[rl * 128 + cl]) acc[i][j][v] = 0.f;
-          }
-    }
-    __syncthreads();  // stages 0 / 1 and W buffer 0 are refilled below
-  }
-
-  if (producer) {
-    const bool odd = lane & 1;
-    float th[8];
-    lane_levels(a.nf4, odd, th);
-    const LaneMask lm = lane_mask(odd);
-    const Srcs src = make_srcs<NN>(a);
-    const ActRows rows = act_rows(a, row0, lane);
-
-    // Issue order inside a step: code loads first, then activation copies,
-    // so that waiting for the codes of step s + 1 (decoded at step s) never
-    // waits for the copies issued after them (vmcnt retires in order).
-    CodeSeg c0s = load_codes<NN>(a, src, c0, kofs(0), ptid);
-    copy_act(a, src, rows, act_lds(stage_of(0)), kofs(0), lane);
-    CodeSeg c1s = load_codes<NN>(a, src, c0, kofs(1), ptid);
-    copy_act(a, src, rows, act_lds(stage_of(1)), kofs(1), lane);
-    decode_store<NN, E>(w_buf0, c0s, th, lm, ptid);
-    // copies of step 0 done: younger are the codes (3) and copies (8) of step 1
-    wait_vmcnt<11>();
-    __syncthreads();
-
-    auto body = [&](int step, CodeSeg& load_slot, const CodeSeg& dec, uint16_t* w_next) {
-      load_slot = load_codes<NN>(a, src, c0, kofs(step + 2), ptid);
-      __builtin_amdgcn_sched_barrier(0);  // keep all code loads ahead of the copies
-      copy_act(a, src, rows, act_lds(stage_of(step + 2)), kofs(step + 2), lane);
-      decode_store<NN, E>(w_next, dec, th, lm, ptid);
-      // copies of step s + 1 done: younger are the codes (3) and copies (8)
-      // of step s + 2
-      wait_vmcnt<11>();
-      step_barrier();
+    auto dec = [&](int step, CodeSeg& slot) {
+      wait_vmcnt<9>();
+      decode_store<NN, E>(wbuf(step), slot, dc, ptid);
+      __builtin_amdgcn_sched_barrier(0);
+      slot = load_codes<NN>(a, src, c0, kofs(step + 4), ptid);
     };
-    for (int step = 0; step < nst; step += 2) {
-      body(step, c0s, c1s, w_buf1);
-      body(step + 1, c1s, c0s, w_buf0);
+    dec(0, cr[0]);
+    dec(1, cr[1]);
+    step_barrier();  // steps 0 and 1 decoded; adapter operand (and keep bytes) staged
+    if (drop_first) step_barrier();  // consumers applied the mask: W buffers 2-3 free
+    for (int step = 0; step < nst; step += 2 * kPhase) {
+      // phase of steps (step, step + 1): decode steps + 2, + 3
+      if (step + 2 < nst) { dec(step + 2, cr[2]); dec(step + 3, cr[3]); }
+      step_barrier();
+      // phase of steps (step + 2, step + 3): decode steps + 4, + 5
+      if (step + 4 < nst) { dec(step + 4, cr[0]); dec(step + 5, cr[1]); }
+      step_barrier();
     }
-    wait_vmcnt<0>();  // nothing left in flight into the activation ring
+    wait_vmcnt<0>();
   } else {
-    __syncthreads();  // tile 0 and activations of step 0 are ready
-    const CodeSeg none{};
-    const float th0[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    const LaneMask lm0{0, 0, 0};
-    for (int step = 0; step < nst; step += 2) {
-      mma_step<NN, false, E>(acc, act_ptr(stage_of(step)), w_buf0, w_buf1, none, th0, lm0, 0, lane);
+    constexpr int DA = ARing<NN>::kSteps;
+    const int mbp = tiled_mbp(a.M);
+    const __amdgpu_buffer_rsrc_t ract = make_rsrc(a.act_t, (uint32_t)tiled_bytes(a.M, a.R));
+    // byte offsets of this lane in the two fragment blocks of the wave's rows
+    const int mb0 = row0 >> 5;
+    uint32_t abase[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      abase[i] = mb0 + i < mbp ? (uint32_t)(mb0 + i) * (uint32_t)a.kbp * 1024u + 16u * (uint32_t)lane : kOOB;
+    auto load_a = [&](int step, int ks, uint4 (&dst)[2]) {
+      const bool ok = step < nloc;
+      const uint32_t kb = 4u * (uint32_t)(s0 + step) + (uint32_t)ks;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) dst[i] = buf_load16(ract, ok && abase[i] != kOOB ? abase[i] + kb * 1024u : kOOB);
+    };
+    AFrags ar[DA];  // A fragments of steps s .. s + DA - 1 (step s in ar[s % DA])
+#pragma unroll
+    for (int d = 0; d < DA; ++d)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) load_a(d, ks, ar[d].f[ks]);
+
+    if (adapter) {
+      // token-side rows (U~ or V~, [M x r]) straight into MFMA A operands
+      const int nks = (a.r + 15) >> 4;  // 16-rank sub-steps that hold ranks
+      uint4 uf[4][2];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int m = row0 + 32 * i + (lane & 31), j = 16 * ks + 8 * (lane >> 5);
+          uf[ks][i] = ks < nks ? load_e16x8(src.lora_act, (uint32_t)m * (uint32_t)a.r + (uint32_t)j, m < a.M,
+                                            a.r - j, vec)
+                               : make_uint4(0, 0, 0, 0);
+        }
+      step_barrier();  // adapter operand staged; steps 0 and 1 decoded
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks >= nks) break;  // uniform; the loop stays unrolled (static register indices)
+        uint4 bf[4];
+        read_b<NN>(s_ad, ks, lane, bf);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = E::mfma32(E::vec(uf[ks][i]), E::vec(bf[j]), acc[i][j]);
+      }
+      if (drop_first) {
+        const uint8_t* keep = reinterpret_cast<const uint8_t*>(wbuf(2)) + slice * (64 * BN);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int rl = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), cl = 32 * j + (lane & 31);
+              if (!keep[rl * 128 + cl]) acc[i][j][v] = 0.f;
+            }
+        step_barrier();  // mask read: producers may decode into W buffers 2-3
+      }
+    } else {
+      step_barrier();  // steps 0 and 1 decoded
+    }
+
+    uint4 bc[4], bn[4];
+    // One step of MFMAs from A registers and the W buffer of `step`; the B
+    // operands of the next sub-step are read while these MFMAs run, and each
+    // sub-step's A fragments are replaced by those of step + DA once used.
+    // `last`: the final step of a phase, whose successor's W buffer is only
+    // ready after the barrier (read there).
+    auto cstep = [&](int step, AFrags& af, bool last) {
+      const uint16_t* sw = wbuf(step);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks < 3) read_b<NN>(sw, ks + 1, lane, bn);
+        else if (!last) read_b<NN>(wbuf(step + 1), 0, lane, bn);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = E::mfma32(E::vec(af.f[ks][i]), E::vec(bc[j]), acc[i][j]);
+        load_a(step + DA, ks, af.f[ks]);
+        // interleave: one MFMA, then one (NT) or two (NN) operand reads, ...
+        // the two fragment loads after the fifth and sixth MFMA
+        constexpr int kDs = NN ? 2 : 1;
+        const bool reads = ks < 3 || !last;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+          if (reads) __builtin_amdgcn_sched_group_barrier(0x100, kDs, 0);  // DS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bc[j] = bn[j];
+      }
+    };
+    read_b<NN>(wbuf(0), 0, lane, bc);
+    for (int step = 0; step < nst; step += 2 * kPhase) {
+      cstep(step, ar[0], false);
+      cstep(step + 1, ar[DA - 1], true);
       step_barrier();
-      mma_step<NN, false, E>(acc, act_ptr(stage_of(step + 1)), w_buf1, w_buf0, none, th0, lm0, 0, lane);
+      read_b<NN>(wbuf(step + 2), 0, lane, bc);
+      cstep(step + 2, ar[0], false);
+      cstep(step + 3, ar[DA - 1], true);
       step_barrier();
+      if (step + 4 < nst) read_b<NN>(wbuf(step + 4), 0, lane, bc);
     }
   }
-
-  // ---- adapter step at the end (no dropout): W buffer 0 and activation
-  // stage nst % 3 are no longer read
-  if (a.r > 0 && !drop_first && kz == 0) adapter_step(w_buf0, act_ptr(stage_of(nst)));
 
   // ---- split reduction: this split's fp32 tile, added up by a second pass
   if (a.part) {
@@ -543,22 +556,50 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
     return;
   }
 
-  // ---- epilogue: fp32 -> bf16 (round to nearest even) ---------------------
+  // ---- epilogue: fp32 -> bf16 (round to nearest even), through LDS -------
+  // The ring is free (every wave passed the last barrier).  Each consumer
+  // stages its 64 x 128 tile in rows of its own LDS region, then reads it
+  // back 16 bytes per lane: every global store instruction writes 4 rows of
+  // 256 contiguous bytes instead of 2-byte pieces.
   if (!producer) {
+    uint16_t* so = s_w + slice * (64 * kOutPitch);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int col = c0 + 32 * j + (lane & 31);
-        if (col >= a.C) continue;
+        const int col = 32 * j + (lane & 31);
 #pragma unroll
         for (int v = 0; v < 16; v += 2) {
-          const int row = row0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int rl = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           const uint32_t pk = E::pack2(acc[i][j][v], acc[i][j][v + 1]);
-          if (row < a.M) a.out[(int64_t)row * a.ld_out + col] = (uint16_t)(pk & 0xFFFFu);
-          if (row + 1 < a.M) a.out[(int64_t)(row + 1) * a.ld_out + col] = (uint16_t)(pk >> 16);
+          so[rl * kOutPitch + col] = (uint16_t)(pk & 0xFFFFu);
+          so[(rl + 1) * kOutPitch + col] = (uint16_t)(pk >> 16);
         }
       }
+    // LDS operations of one wave complete in order: the reads see the writes
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int rl = 4 * t + (lane >> 4), cl = 8 * (lane & 15);
+      const uint4 v = *reinterpret_cast<const uint4*>(so + rl * kOutPitch + cl);
+      const int row = row0 + rl, col = c0 + cl;
+      if (row < a.M && col < a.C) *reinterpret_cast<uint4*>(a.out + (int64_t)row * a.ld_out + col) = v;
+    }
+  }
+}
+
+// Fragment-tiled copy of act[M][R] (see gemm_args.h): one thread per 16-byte
+// piece, rows past M and columns past R written as zeros.
+__global__ __launch_bounds__(256) void k_tile_act(const uint16_t* __restrict__ act, int M, int R, int kbp, bool eo,
+                                                  uint16_t* __restrict__ act_t, int64_t npieces) {
+  for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < npieces; p += (int64_t)gridDim.x * 256) {
+    // piece p: lane l = p & 63 of fragment f = p >> 6 = mb * kbp + kb
+    const int l = (int)(p & 63);
+    const int64_t f = p >> 6;
+    const int mb = (int)(f / kbp), kb = (int)(f - (int64_t)mb * kbp);
+    const int m = 32 * mb + (l & 31), k = 16 * kb + 8 * (l >> 5);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (m < M && k < R) v = *reinterpret_cast<const uint4*>(act + (int64_t)m * R + k);
+    reinterpret_cast<uint4*>(act_t)[p] = eo ? x_order_even_odd(v) : v;
   }
 }
 
@@ -644,6 +685,15 @@ hipError_t launch_splitk_reduce(const float* part, int ksplit, int M, int C, uin
   const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 2048));
   if (f16) hipLaunchKernelGGL(k_splitk_reduce<F16>, dim3(blocks), dim3(256), 0, st, part, ksplit, M, C, out, ld_out);
   else hipLaunchKernelGGL(k_splitk_reduce<Bf16>, dim3(blocks), dim3(256), 0, st, part, ksplit, M, C, out, ld_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_act(const uint16_t* act, int M, int R, bool eo, uint16_t* act_t, hipStream_t st) {
+  const int kbp = tiled_kbp(R);
+  const int64_t npieces = (int64_t)tiled_mbp(M) * kbp * 64;
+  if (npieces == 0) return hipSuccess;
+  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((npieces + 255) / 256, 4096));
+  hipLaunchKernelGGL(k_tile_act, dim3(blocks), dim3(256), 0, st, act, M, R, kbp, eo, act_t, npieces);
   return hipGetLastError();
 }
 

@@ -1,4 +1,5 @@
-// Launch arguments of the fused NF4-dequant GEMMs (see gemm.hip).
+// Launch arguments of the fused NF4-dequant GEMMs (see gemm.hip), and the
+// fragment-tiled activation layout they read.
 #pragma once
 
 #include "common.h"
@@ -6,9 +7,32 @@
 
 namespace qlora {
 
+// Fragment-tiled copy of an activation matrix act[M][R] (R: the reduction
+// length of the product that reads it).  It is stored as 1 KB fragments of
+// 32 rows x 16 reduction columns, in the A-operand layout of
+// v_mfma_f32_32x32x16: fragment (mb, kb) starts at element
+// (mb * kbp + kb) * 512 and its lane l (0..63) holds the 8 elements
+// act[32 mb + (l & 31)][16 kb + 8 (l >> 5) + e], e = 0..7.  kbp = 4 ceil(R / 64)
+// fragments per 32-row block (whole 64-deep steps), mbp = ceil(M / 32)
+// blocks; rows past M and columns past R hold zeros.  The adapter kernels
+// that read act anyway (U~ over X, V~ over dY) write it; a GEMM wave then
+// loads each operand fragment with one coalesced 1 KB load, straight into
+// registers.  The forward's copy of X permutes each lane's 8 elements to the
+// order 0, 2, 4, 6, 1, 3, 5, 7 (e above runs over that order), the order in
+// which the forward GEMM decodes W; the dX product's copy of dY keeps the
+// natural order.
+__host__ __device__ inline int tiled_kbp(int64_t R) { return (int)(4 * ((R + 63) / 64)); }
+__host__ __device__ inline int tiled_mbp(int64_t M) { return (int)((M + 31) / 32); }
+__host__ __device__ inline size_t tiled_bytes(int64_t M, int64_t R) { return (size_t)tiled_mbp(M) * (size_t)tiled_kbp(R) * 1024u; }
+
+// Element offset in the tiled copy of act[m][k .. k + 7], k a multiple of 8.
+__host__ __device__ inline uint32_t tiled_elem(int m, int k, int kbp) {
+  return (uint32_t)(((m >> 5) * kbp + (k >> 4)) * 512 + ((m & 31) + 32 * ((k >> 3) & 1)) * 8);
+}
+
 struct GemmArgs {
-  const uint16_t* act;       // X [M x R] (forward) or dY [M x R] (dX), row-major bf16
-  int64_t ld_act;            // row pitch of act in elements (= R)
+  const uint16_t* act_t;     // fragment-tiled X (forward) or dY (dX), 16-bit elements
+  int kbp;                   // fragments per 32-row block of act_t (tiled_kbp(R))
   int M;                     // rows (tokens)
   int R;                     // reduction length: k_in (forward) or n_out (dX)
   int C;                     // output columns: n_out (forward) or k_in (dX)
@@ -42,5 +66,10 @@ size_t gemm_part_bytes(int64_t M, int64_t C, int64_t R, int cus);
 // order (C % 8 == 0, rows of out 16-byte aligned).
 hipError_t launch_splitk_reduce(const float* part, int ksplit, int M, int C, uint16_t* out, int64_t ld_out, bool f16,
                                 hipStream_t st);
+
+// The fragment-tiled copy of act[M][R] (row pitch R elements, R % 8 == 0)
+// alone, for products whose adapter kernels do not run (r == 0); eo: the
+// forward's element order (see above).
+hipError_t launch_tile_act(const uint16_t* act, int M, int R, bool eo, uint16_t* act_t, hipStream_t st);
 
 }  // namespace qlora

@@ -13,6 +13,8 @@
 
 #include "common.h"
 #include "dropout.h"
+#include "gemm_args.h"
+#include "nf4_lut.h"
 
 namespace qlora {
 
@@ -74,6 +76,7 @@ struct RowdotArgs {
   uint16_t* out;       // [M x r] bf16
   float* part;         // [nsplit][M][r] fp32, or null when nsplit == 1
   DropMask drop;       // dropout of `in` (thr 0: none)
+  uint16_t* tiled;     // fragment-tiled copy of `in` to write (gemm_args.h), or null
 };
 
 // Workgroup (bx, by) = (64-row block, K split) of the rowdot grid.
@@ -105,6 +108,23 @@ __device__ __forceinline__ void rowdot_body(const RowdotArgs& ra, int bx, int by
     for (int u = 0; u < 8; ++u) {
       const int k = k0 + 32 * u + 8 * kg;
       av[u] = buf_load16(rin, k < k_hi ? row_off + 2u * (uint32_t)k : kOOB);
+    }
+    if (ra.tiled) {
+      // The undropped activations, also into the fragment-tiled copy the
+      // GEMM reads: 16 lanes of one k-group write 256 contiguous bytes.  This
+      // split writes its own columns; the last one also the zero padding up
+      // to whole 64-deep steps, and rows up to the last 32-row block.
+      const int m = m0 + row, kpad = 16 * tiled_kbp(Kd), mpad = 32 * tiled_mbp(M);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = k0 + 32 * u + 8 * kg;
+        const bool own = k < k_hi || (k_hi == Kd && k < kpad);
+        // X (the forward's activations, CONTIG) goes in the element order
+        // 0, 2, 4, 6, 1, 3, 5, 7 of each 8 columns, matching the forward
+        // GEMM's W decode; dY keeps its natural order
+        const uint4 v = CONTIG ? x_order_even_odd(av[u]) : av[u];
+        if (own && m < mpad) *reinterpret_cast<uint4*>(ra.tiled + tiled_elem(m, k, tiled_kbp(Kd))) = v;
+      }
     }
     if (ra.drop.thr) {
 #pragma unroll
@@ -408,23 +428,23 @@ __global__ __launch_bounds__(256) void k_zero_u16(uint16_t* __restrict__ p, int6
 
 template <bool CONTIG, int RT, typename E>
 void rowdot_launch(dim3 grid, hipStream_t st, const uint16_t* in, int M, int Kd, const uint16_t* wt, int r,
-                   int kchunk, float scale, uint16_t* out, float* part, DropMask drop) {
-  const RowdotArgs ra{in, M, Kd, wt, r, kchunk, (int)grid.y, scale, out, part, drop};
+                   int kchunk, float scale, uint16_t* out, float* part, DropMask drop, uint16_t* tiled) {
+  const RowdotArgs ra{in, M, Kd, wt, r, kchunk, (int)grid.y, scale, out, part, drop, tiled};
   hipLaunchKernelGGL((k_rowdot<CONTIG, RT, E>), grid, dim3(256), 0, st, ra);
 }
 
 template <bool CONTIG, typename E>
 hipError_t rowdot_dispatch(const uint16_t* in, int M, int Kd, const uint16_t* wt, int r, float scale,
-                           uint16_t* out, float* part, DropMask drop, hipStream_t st) {
+                           uint16_t* out, float* part, DropMask drop, uint16_t* tiled, hipStream_t st) {
   int nsplit, kchunk;
   rowdot_split(M, Kd, &nsplit, &kchunk);
   dim3 grid((M + 63) / 64, nsplit);
   float* p = nsplit > 1 ? part : nullptr;
   switch ((r + 15) / 16) {
-    case 1: rowdot_launch<CONTIG, 1, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
-    case 2: rowdot_launch<CONTIG, 2, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
-    case 3: rowdot_launch<CONTIG, 3, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
-    default: rowdot_launch<CONTIG, 4, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
+    case 1: rowdot_launch<CONTIG, 1, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop, tiled); break;
+    case 2: rowdot_launch<CONTIG, 2, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop, tiled); break;
+    case 3: rowdot_launch<CONTIG, 3, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop, tiled); break;
+    default: rowdot_launch<CONTIG, 4, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop, tiled); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
@@ -441,11 +461,12 @@ hipError_t rowdot_dispatch(const uint16_t* in, int M, int Kd, const uint16_t* wt
 
 }  // namespace
 
-// U~ = E(s (mask * X) A^T): in = X [M x K], A [r x K]; E = fp16 when f16, else bf16
+// U~ = E(s (mask * X) A^T): in = X [M x K], A [r x K]; E = fp16 when f16,
+// else bf16.  Xt: the fragment-tiled copy of X to write too, or null.
 hipError_t launch_lora_down(const uint16_t* X, int M, int K, const uint16_t* A, int r, float s, uint16_t* U,
-                            float* part, DropMask drop, bool f16, hipStream_t st) {
-  return f16 ? rowdot_dispatch<true, F16>(X, M, K, A, r, s, U, part, drop, st)
-             : rowdot_dispatch<true, Bf16>(X, M, K, A, r, s, U, part, drop, st);
+                            float* part, DropMask drop, bool f16, uint16_t* Xt, hipStream_t st) {
+  return f16 ? rowdot_dispatch<true, F16>(X, M, K, A, r, s, U, part, drop, Xt, st)
+             : rowdot_dispatch<true, Bf16>(X, M, K, A, r, s, U, part, drop, Xt, st);
 }
 
 int coldot_chunk_rows() { return 256; }
@@ -490,11 +511,12 @@ hipError_t launch_coldot(const uint16_t* v, int r, const uint16_t* in, int M, in
 //   1. V~ split partials (or V~ itself when unsplit) and dB row-chunk partials;
 //   2. V~ finalize (when split) and dB finalize.
 hipError_t launch_vt_and_db(const uint16_t* dY, int M, int N, const uint16_t* B, const uint16_t* U, int r,
-                            float s, uint16_t* V, float* vpart, float* cpart, float* dB, bool f16, hipStream_t st) {
+                            float s, uint16_t* V, float* vpart, float* cpart, float* dB, bool f16, uint16_t* dYt,
+                            hipStream_t st) {
   int nsplit, kchunk;
   rowdot_split(M, N, &nsplit, &kchunk);
   const int rb = (M + 63) / 64;
-  const RowdotArgs ra{dY, M, N, B, r, kchunk, nsplit, s, V, nsplit > 1 ? vpart : nullptr, DropMask{}};
+  const RowdotArgs ra{dY, M, N, B, r, kchunk, nsplit, s, V, nsplit > 1 ? vpart : nullptr, DropMask{}, dYt};
   const int mchunk = coldot_chunk_rows();
   const int ctiles = (N + 127) / 128, nmc = (M + mchunk - 1) / mchunk;
   const ColdotArgs ca{U, r, dY, M, N, mchunk, cpart, DropMask{}};

@@ -126,19 +126,25 @@ def test_backward_validation(L):
     assert call(U=FAKE_MIS, ws=FAKE, wsb=need) == ALIGN
 
 
+def _tiled(M, R):
+    """Bytes of the fragment-tiled activation copy the GEMMs read: 32-row
+    blocks x whole 64-deep steps of 16-bit elements."""
+    return -(-M // 32) * 32 * (-(-R // 64) * 64) * 2
+
+
 def test_workspace_sizes(L):
     ws = L.qlora_workspace_bytes
-    assert ws(1, 2048, 4096, 4096, 0) == 0
-    assert ws(1, 2048, 4096, 4096, 16) >= 2048 * 16 * 2
+    assert ws(1, 2048, 4096, 4096, 0) == _tiled(2048, 4096)  # the tiled X only
+    assert ws(1, 2048, 4096, 4096, 16) >= 2048 * 16 * 2 + _tiled(2048, 4096)
     b = ws(2, 2048, 11008, 4096, 16)
-    assert b >= 2 * 2048 * 16 * 2 + 8 * 16 * 11008 * 4
-    assert ws(2, 2048, 4096, 4096, 0) == 0
+    assert b >= 2 * 2048 * 16 * 2 + _tiled(2048, 11008) + 8 * 16 * 11008 * 4
+    assert ws(2, 2048, 4096, 4096, 0) == _tiled(2048, 4096)  # the tiled dY only
     assert ws(9, 1, 1, 64, 1) == 0
     # few output tiles: optional room for a reduction split, also with r = 0
     # (8 tiles of 256 x 128 over 32 steps of 64: 4 splits of fp32 130 x 1024)
-    assert ws(1, 130, 1024, 2048, 0) == 4 * 130 * 1024 * 4
-    assert ws(1, 130, 1024, 2048, 16) >= 130 * 16 * 2 + 4 * 130 * 1024 * 4
-    assert ws(2, 130, 1024, 2048, 0) == 2 * 130 * 2048 * 4  # dX: 16 tiles, 16 steps
+    assert ws(1, 130, 1024, 2048, 0) == _tiled(130, 2048) + 4 * 130 * 1024 * 4
+    assert ws(1, 130, 1024, 2048, 16) >= 130 * 16 * 2 + _tiled(130, 2048) + 4 * 130 * 1024 * 4
+    assert ws(2, 130, 1024, 2048, 0) == _tiled(130, 1024) + 2 * 130 * 2048 * 4  # dX: 16 tiles, 16 steps
     assert ws(1, 16, 1024, 2048, 0) == 0  # few-token kernel: no split
     # few-token kernel over a long reduction: 4 splits of fp32 16 x 8192
     assert ws(1, 16, 8192, 28672, 0) == 4 * 16 * 8192 * 4

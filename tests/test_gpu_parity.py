@@ -474,14 +474,22 @@ def test_backward_parity(M, N, K, r, alpha):
         assert torch.equal(dA, dA2) and torch.equal(dB, dB2)
 
 
+def _tiled_bytes(M, R):
+    """The fragment-tiled activation copy a GEMM reads (r = 0: the only
+    required workspace)."""
+    return -(-M // 32) * 32 * (-(-R // 64) * 64) * 2
+
+
 def test_split_reduction_room_is_optional():
     """Few output tiles: with room in the workspace the products split the
-    reduction; without it (r = 0 needs none) they run unsplit.  Both match
-    the oracle."""
+    reduction; with only the required part (r = 0: the tiled activations)
+    they run unsplit; with less the call is refused.  Both results match the
+    oracle."""
     _need_gpu()
     M, N, K, r, alpha = 130, 1024, 2048, 0, 0.0
-    assert qlora.workspace_bytes(qlora.QLORA_OP_FWD, M, N, K, r) > 0
-    assert qlora.workspace_bytes(qlora.QLORA_OP_BWD, M, N, K, r) > 0
+    fwd_req, bwd_req = _tiled_bytes(M, K), _tiled_bytes(M, N)
+    assert qlora.workspace_bytes(qlora.QLORA_OP_FWD, M, N, K, r) > fwd_req
+    assert qlora.workspace_bytes(qlora.QLORA_OP_BWD, M, N, K, r) > bwd_req
     d, q, wb = _case(M, N, K, r, seed=5)
     w = gpu_quantize(d["W"])
     X, _, _, dY = _dev_inputs(d, r)
@@ -491,10 +499,16 @@ def test_split_reduction_room_is_optional():
     cw = w._c()
     Yu = torch.empty_like(Ys)
     dXu = torch.empty_like(dXs)
+    wsf = torch.empty(fwd_req, dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(bwd_req, dtype=torch.uint8, device="cuda")
     assert L.qlora_linear_fwd(ctypes.byref(cw), X.data_ptr(), M, None, None, 0, 0.0, Yu.data_ptr(), None,
-                              None, 0, qlora._stream()) == 0
+                              wsf.data_ptr(), fwd_req - 256, qlora._stream()) == -4  # QLORA_ERR_WORKSPACE
+    assert L.qlora_linear_fwd(ctypes.byref(cw), X.data_ptr(), M, None, None, 0, 0.0, Yu.data_ptr(), None,
+                              wsf.data_ptr(), fwd_req, qlora._stream()) == 0
     assert L.qlora_linear_bwd(ctypes.byref(cw), X.data_ptr(), dY.data_ptr(), M, None, None, 0, 0.0, None,
-                              dXu.data_ptr(), None, None, None, 0, qlora._stream()) == 0
+                              dXu.data_ptr(), None, None, wsb.data_ptr(), bwd_req - 256, qlora._stream()) == -4
+    assert L.qlora_linear_bwd(ctypes.byref(cw), X.data_ptr(), dY.data_ptr(), M, None, None, 0, 0.0, None,
+                              dXu.data_ptr(), None, None, wsb.data_ptr(), bwd_req, qlora._stream()) == 0
     torch.cuda.synchronize()
     Yr, _ = oracle.linear_fwd(wb, d["X"], d["A"], d["B"], alpha, r)
     dXr, _, _ = oracle.linear_bwd(wb, d["X"], d["dY"], d["A"], d["B"], alpha, r)
