@@ -18,7 +18,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqlora.so")
-SOURCES = ["nf4_table.cpp", "codec.hip", "gemm.hip", "skinny.hip", "lora.hip", "merge.hip", "abi.hip"]
+SOURCES = ["nf4_table.cpp", "codec.hip", "gemm.hip", "skinny.hip", "lora.hip", "adapter.hip", "merge.hip", "abi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

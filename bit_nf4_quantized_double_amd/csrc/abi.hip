@@ -31,15 +31,8 @@ hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_dx(const GemmArgs& a, hipStream_t st);
 void time_next_gemm(hipEvent_t start, hipEvent_t stop);
 hipError_t launch_lora_down(const uint16_t* X, int M, int K, const uint16_t* A, int r, float s, uint16_t* U,
-                            float* part, DropMask drop, bool f16, uint16_t* Xt, hipStream_t st);
+                            float* part, DropMask drop, bool f16, hipStream_t st);
 size_t rowdot_part_bytes(int64_t M, int64_t Kd, int r);
-int coldot_chunk_rows();
-hipError_t launch_coldot(const uint16_t* v, int r, const uint16_t* in, int M, int C, float* part,
-                         DropMask drop, bool f16, hipStream_t st);
-hipError_t launch_finalize(const float* part, int nmc, int r, int C, float* out, bool trans, hipStream_t st);
-hipError_t launch_vt_and_db(const uint16_t* dY, int M, int N, const uint16_t* B, const uint16_t* U, int r,
-                            float s, uint16_t* V, float* vpart, float* cpart, float* dB, bool f16, uint16_t* dYt,
-                            hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_zero_u16(uint16_t* p, int64_t n, hipStream_t st);
 }  // namespace qlora
@@ -149,17 +142,17 @@ int dropout_setup(int32_t r, float alpha, double p, uint64_t seed, qlora::DropMa
 }
 
 struct BwdLayout {
-  size_t u, v, dyt, part, cpart, total;  // part: U~ / V~ split-K partials; cpart: dA / dB row-chunk partials
-  int nmc;
-  size_t req;   // bytes required (U~, V~, the tiled dY and the reduction partials)
-  size_t gemm;  // split-reduction tiles of the dX product, from `part` on
+  size_t u, v, dyt, part, total;  // part: row-pass partials of V~ (and of U~ when it is recomputed)
+  size_t req;   // bytes required (U~, V~, the tiled dY and the partials)
+  size_t gemm;  // offset of the dX product's split-reduction tiles (optional room past req)
 };
 
-// [U~][V~][fragment-tiled dY][U~ / V~ partials][dA / dB partials]; U~ and V~
-// only with an adapter (r > 0)
+// [U~][V~][fragment-tiled dY][V~ partials | U~ recompute partials][split
+// tiles of the dX product]; U~, V~ and partials only with an adapter (r > 0)
 BwdLayout bwd_layout(int64_t M, int64_t n_out, int64_t k_in, int32_t r) {
   BwdLayout L{};
   if (M <= 0) return L;
+  const int cus = qlora::device_compute_units();
   const size_t urow = r > 0 ? round_up((size_t)M * r * 2) : 0;
   L.u = 0;
   L.v = urow;
@@ -167,19 +160,18 @@ BwdLayout bwd_layout(int64_t M, int64_t n_out, int64_t k_in, int32_t r) {
   L.part = L.dyt + round_up(qlora::tiled_bytes(M, n_out));
   L.req = L.part;
   if (r > 0) {
-    const int mch = qlora::coldot_chunk_rows();
-    L.nmc = (int)((M + mch - 1) / mch);
-    const int64_t widest = n_out > k_in ? n_out : k_in;
-    // U~ and V~ split-K partials share one region (stream order); the dB and
-    // dA row-chunk partials share another (dB's are produced alongside V~'s)
-    const size_t part = std::max(qlora::rowdot_part_bytes(M, k_in, r), qlora::rowdot_part_bytes(M, n_out, r));
-    L.cpart = L.part + round_up(part);
-    L.req = L.cpart + round_up((size_t)L.nmc * r * widest * 4);
+    // a U~ recompute (no U given) is done with its partials -- those of the
+    // forward's own method at this token count -- before the row pass over
+    // dY writes the V~ partials: one region serves both
+    const size_t ure = M <= qlora::skinny_max_tokens() ? qlora::rowdot_part_bytes(M, k_in, r)
+                                                       : qlora::rowpass_part_bytes(M, k_in, r, cus);
+    const size_t part = std::max(ure, qlora::rowpass_part_bytes(M, n_out, r, cus));
+    L.req = L.part + round_up(part);
   }
-  // the dX product's split-reduction tiles reuse everything from L.part on
-  // (dead by then); they need not fit: without room the product runs unsplit
-  L.gemm = round_up(qlora::gemm_part_bytes(M, k_in, n_out, qlora::device_compute_units()));
-  L.total = std::max(L.req, L.part + L.gemm);
+  // the dX product reads the V~ partials while it runs: its split tiles go
+  // after them; they need not fit (without room the product runs unsplit)
+  L.gemm = L.req;
+  L.total = L.req + round_up(qlora::gemm_part_bytes(M, k_in, n_out, cus));
   return L;
 }
 
@@ -248,15 +240,17 @@ size_t qlora_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, int
   if (M < 0 || n_out < 0 || k_in < 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
   if (op == QLORA_OP_FWD) {
     if (M == 0) return 0;
-    // [U~][fragment-tiled X (GEMM path)][U~ partials | split-reduction tiles of the main product]
-    const bool gemm_path = M > qlora::skinny_max_tokens();
-    const size_t u = r > 0 ? round_up((size_t)M * r * 2) : 0;
-    const size_t xt = gemm_path ? round_up(qlora::tiled_bytes(M, k_in)) : 0;
-    const size_t upart = r > 0 ? round_up(qlora::rowdot_part_bytes(M, k_in, r)) : 0;
     const int cus = qlora::device_compute_units();
-    const size_t gpart = round_up(gemm_path ? qlora::gemm_part_bytes(M, n_out, k_in, cus)
-                                            : qlora::skinny_part_bytes(M, n_out, k_in, cus));
-    return u + xt + std::max(upart, gpart);
+    if (M <= qlora::skinny_max_tokens()) {
+      // few tokens: [U~][U~ partials | split partials of the main product]
+      const size_t u = r > 0 ? round_up((size_t)M * r * 2) : 0;
+      const size_t upart = r > 0 ? round_up(qlora::rowdot_part_bytes(M, k_in, r)) : 0;
+      return u + std::max(upart, round_up(qlora::skinny_part_bytes(M, n_out, k_in, cus)));
+    }
+    // [fragment-tiled X][U~ partials of the row pass][split tiles of the main product]
+    const size_t xt = round_up(qlora::tiled_bytes(M, k_in));
+    const size_t upart = r > 0 ? round_up(qlora::rowpass_part_bytes(M, k_in, r, cus)) : 0;
+    return xt + upart + round_up(qlora::gemm_part_bytes(M, n_out, k_in, cus));
   }
   if (op == QLORA_OP_BWD) return bwd_layout(M, n_out, k_in, r).total;
   return 0;
@@ -335,60 +329,73 @@ static int linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t
   if (!X || !Y) return fail(QLORA_ERR_INVALID_ARG, "X or Y is NULL");
   if (!aligned16(X) || !aligned16(Y)) return fail(QLORA_ERR_ALIGN, "X and Y must be 16-byte aligned");
   if (U_out && !aligned16(U_out)) return fail(QLORA_ERR_ALIGN, "U_out must be 16-byte aligned");
-  uint16_t* U = nullptr;
-  float* part = nullptr;
-  uint16_t* Xt = nullptr;
-  // workspace: [U~ when U_out is NULL][fragment-tiled X, on the GEMM path]
-  // [split-K partials of U~, later reused for the split-reduction tiles of
-  // the main product (optional)]
-  const bool gemm_path = M > qlora::skinny_max_tokens();
-  const size_t ubytes = r > 0 && !U_out ? round_up((size_t)M * r * 2) : 0;
-  const size_t xbytes = gemm_path ? round_up(qlora::tiled_bytes(M, w->k_in)) : 0;
-  const size_t pbytes = r > 0 ? qlora::rowdot_part_bytes(M, w->k_in, r) : 0;
-  if (ubytes + xbytes + pbytes > 0) {
-    if (!ws || ws_bytes < ubytes + xbytes + pbytes) return fail(QLORA_ERR_WORKSPACE, "forward workspace too small");
-    if (!aligned16(ws)) return fail(QLORA_ERR_ALIGN, "workspace must be 16-byte aligned");
-  }
   char* base = static_cast<char*>(ws);
-  if (r > 0) U = U_out ? U_out : reinterpret_cast<uint16_t*>(base);
-  if (xbytes) Xt = reinterpret_cast<uint16_t*>(base + ubytes);
-  if (pbytes) part = reinterpret_cast<float*>(base + ubytes + xbytes);
+  const int cus = qlora::device_compute_units();
   hipError_t e;
-  if (r > 0 && w->k_in > 0) {
-    // U~, and on the GEMM path the tiled X, in one pass over X
-    e = qlora::launch_lora_down(X, (int)M, (int)w->k_in, A, r, s, U, part, dm, f16, Xt, stream);
-    if (e != hipSuccess) return hip_fail(e, "lora_down launch");
-  } else {
-    if (r > 0 && (e = qlora::launch_zero_u16(U, M * r, stream)) != hipSuccess) return hip_fail(e, "zero U");
-    if (Xt && (e = qlora::launch_tile_act(X, (int)M, (int)w->k_in, true, Xt, stream)) != hipSuccess)
-      return hip_fail(e, "tile X launch");
-  }
   if (M <= qlora::skinny_max_tokens()) {
-    // few tokens: bound by reading the packed weight; decode straight into
-    // MFMA operands, no LDS tile
+    // Few tokens: U~ first (split partial sums over k_in, then rounded),
+    // then the few-token kernel, bound by reading the packed weight.
+    // Workspace: [U~ when U_out is NULL][U~ partials, later the split
+    // partials of the main product (optional)].
+    const size_t ubytes = r > 0 && !U_out ? round_up((size_t)M * r * 2) : 0;
+    const size_t pbytes = r > 0 ? qlora::rowdot_part_bytes(M, w->k_in, r) : 0;
+    if (ubytes + pbytes > 0) {
+      if (!ws || ws_bytes < ubytes + pbytes) return fail(QLORA_ERR_WORKSPACE, "forward workspace too small");
+      if (!aligned16(ws)) return fail(QLORA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    }
+    uint16_t* U = nullptr;
+    if (r > 0) {
+      U = U_out ? U_out : reinterpret_cast<uint16_t*>(base);
+      if (w->k_in > 0) {
+        float* part = pbytes ? reinterpret_cast<float*>(base + ubytes) : nullptr;
+        e = qlora::launch_lora_down(X, (int)M, (int)w->k_in, A, r, s, U, part, dm, f16, stream);
+        if (e != hipSuccess) return hip_fail(e, "lora_down launch");
+      } else if ((e = qlora::launch_zero_u16(U, M * r, stream)) != hipSuccess) {
+        return hip_fail(e, "zero U");
+      }
+    }
     qlora::SkinnyArgs k{};
     k.X = X; k.codes = w->codes; k.q8 = w->absmax_q8; k.s2 = w->absmax_scale;
     k.U = U; k.B = B; k.Y = Y;
     k.M = (int)M; k.N = (int)w->n_out; k.K = (int)w->k_in; k.r = r;
     k.nf4 = qlora::nf4_consts();
     k.f16 = f16;
-    // split partial sums after U~ (the U~ partials are consumed by then);
-    // without room the kernel runs unsplit
-    const size_t kbytes = qlora::skinny_part_bytes(M, w->n_out, w->k_in, qlora::device_compute_units());
+    // without room for the split partials the kernel runs unsplit
+    const size_t kbytes = qlora::skinny_part_bytes(M, w->n_out, w->k_in, cus);
     if (kbytes && ws && aligned16(ws) && ws_bytes >= ubytes + kbytes)
       k.part = reinterpret_cast<float*>(base + ubytes);
     e = qlora::launch_skinny_fwd(k, stream);
     return e == hipSuccess ? QLORA_OK : hip_fail(e, "few-token forward launch");
   }
+  // The fused GEMM.  Workspace: [fragment-tiled X][U~ partials of the row
+  // pass][split tiles of the main product (optional)].  One row pass over X
+  // writes the tiled copy and the U~ partial sums; the GEMM adds them up in
+  // its prologue (and stores U~ to U_out, when given).
+  const size_t xbytes = round_up(qlora::tiled_bytes(M, w->k_in));
+  const size_t pbytes = r > 0 ? round_up(qlora::rowpass_part_bytes(M, w->k_in, r, cus)) : 0;
+  if (xbytes + pbytes > 0) {
+    if (!ws || ws_bytes < xbytes + pbytes) return fail(QLORA_ERR_WORKSPACE, "forward workspace too small");
+    if (!aligned16(ws)) return fail(QLORA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
+  uint16_t* Xt = reinterpret_cast<uint16_t*>(base);
+  float* upart = r > 0 ? reinterpret_cast<float*>(base + xbytes) : nullptr;
+  if (r > 0) {
+    e = qlora::launch_rowpass(X, (int)M, (int)w->k_in, A, r, true, dm, upart, Xt, f16, cus, stream);
+    if (e != hipSuccess) return hip_fail(e, "row pass launch");
+  } else if ((e = qlora::launch_tile_act(X, (int)M, (int)w->k_in, true, Xt, stream)) != hipSuccess) {
+    return hip_fail(e, "tile X launch");
+  }
   qlora::GemmArgs g{};
   g.act_t = Xt; g.kbp = qlora::tiled_kbp(w->k_in); g.M = (int)M; g.R = (int)w->k_in; g.C = (int)w->n_out;
   g.codes = w->codes; g.q8 = w->absmax_q8; g.s2 = w->absmax_scale; g.K = (int)w->k_in;
-  g.lora_act = U; g.lora_w = B; g.r = r;
+  g.lora_w = B; g.r = r;
+  g.lora_part = upart; g.lora_ns = qlora::rowpass_plan(M, w->k_in, cus).S; g.lora_rp = qlora::rank_pitch(r);
+  g.lora_scale = s; g.lora_out = r > 0 ? U_out : nullptr;
   g.out = Y; g.ld_out = w->n_out;
   g.nf4 = qlora::nf4_consts();
   g.f16 = f16;
-  const size_t gbytes = qlora::gemm_part_bytes(M, w->n_out, w->k_in, qlora::device_compute_units());
-  if (gbytes && ws && ws_bytes >= ubytes + xbytes + gbytes) g.part = reinterpret_cast<float*>(base + ubytes + xbytes);
+  const size_t gbytes = qlora::gemm_part_bytes(M, w->n_out, w->k_in, cus);
+  if (gbytes && ws_bytes >= xbytes + pbytes + gbytes) g.part = reinterpret_cast<float*>(base + xbytes + pbytes);
   e = qlora::launch_gemm_fwd(g, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e, "forward GEMM launch");
 }
@@ -436,6 +443,7 @@ static int linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const u
   }
 
   char* base = static_cast<char*>(ws);
+  const int cus = qlora::device_compute_units();
   uint16_t* Ut = nullptr;
   uint16_t* Vt = nullptr;
   float* part = nullptr;
@@ -446,37 +454,47 @@ static int linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const u
     if (U) {
       Ut = const_cast<uint16_t*>(U);
     } else {
+      // recompute U~ exactly as the forward formed it at this token count
       Ut = reinterpret_cast<uint16_t*>(base + L.u);
-      if ((e = qlora::launch_lora_down(X, (int)M, (int)K, A, r, s, Ut, part, dm, f16, nullptr, stream)) != hipSuccess)
-        return hip_fail(e, "lora_down launch");
+      if (M <= qlora::skinny_max_tokens()) {
+        if ((e = qlora::launch_lora_down(X, (int)M, (int)K, A, r, s, Ut, part, dm, f16, stream)) != hipSuccess)
+          return hip_fail(e, "lora_down launch");
+      } else {
+        if ((e = qlora::launch_rowpass(X, (int)M, (int)K, A, r, true, dm, part, nullptr, f16, cus, stream)) !=
+            hipSuccess)
+          return hip_fail(e, "row pass launch");
+        if ((e = qlora::launch_rowpass_finalize(part, qlora::rowpass_plan(M, K, cus).S, (int)M, r, s, Ut, f16,
+                                                stream)) != hipSuccess)
+          return hip_fail(e, "U~ finalize launch");
+      }
     }
-    // V~ = bf16(s dY B) and dB = dY^T U~ (stored [N x r]): both read dY; the
-    // V~ pass also writes the tiled dY the dX product reads
-    float* cpart = reinterpret_cast<float*>(base + L.cpart);
-    if ((e = qlora::launch_vt_and_db(dY, (int)M, (int)N, B, Ut, r, s, Vt, part, cpart, dB, f16, dYt, stream)) !=
-        hipSuccess)
-      return hip_fail(e, "V~ / dB launch");
-    // dA = V~^T (mask * X)  ([r x K])
-    if ((e = qlora::launch_coldot(Vt, r, X, (int)M, (int)K, cpart, dm, f16, stream)) != hipSuccess)
-      return hip_fail(e, "dA partials launch");
-    if ((e = qlora::launch_finalize(cpart, L.nmc, r, (int)K, dA, false, stream)) != hipSuccess)
-      return hip_fail(e, "dA finalize launch");
+    // one row pass over dY: the tiled dY the dX product reads and the V~
+    // partial sums, added up (and V~ stored) in the dX product's prologue
+    if ((e = qlora::launch_rowpass(dY, (int)M, (int)N, B, r, false, qlora::DropMask{}, part, dYt, f16, cus,
+                                   stream)) != hipSuccess)
+      return hip_fail(e, "row pass launch");
   } else if ((e = qlora::launch_tile_act(dY, (int)M, (int)N, false, dYt, stream)) != hipSuccess) {
     return hip_fail(e, "tile dY launch");
   }
   qlora::GemmArgs g{};
   g.act_t = dYt; g.kbp = qlora::tiled_kbp(N); g.M = (int)M; g.R = (int)N; g.C = (int)K;
   g.codes = w->codes; g.q8 = w->absmax_q8; g.s2 = w->absmax_scale; g.K = (int)K;
-  g.lora_act = Vt; g.lora_w = A; g.r = r;
+  g.lora_w = A; g.r = r;
+  g.lora_part = part; g.lora_ns = qlora::rowpass_plan(M, N, cus).S; g.lora_rp = qlora::rank_pitch(r);
+  g.lora_scale = s; g.lora_out = Vt;
   g.out = dX; g.ld_out = K;
   g.nf4 = qlora::nf4_consts();
   g.drop = dm;
   g.f16 = f16;
-  // split-reduction tiles, from L.part on (U~ / V~ partials and dA / dB
-  // partials are consumed by now); without room the product runs unsplit
-  if (L.gemm && ws && ws_bytes >= L.part + L.gemm) g.part = reinterpret_cast<float*>(base + L.part);
+  // split-reduction tiles past the required part; without room the product runs unsplit
+  if (ws_bytes >= L.total && L.total > L.gemm) g.part = reinterpret_cast<float*>(base + L.gemm);
   e = qlora::launch_gemm_dx(g, stream);
-  return e == hipSuccess ? QLORA_OK : hip_fail(e, "dX GEMM launch");
+  if (e != hipSuccess) return hip_fail(e, "dX GEMM launch");
+  // dA = V~^T (mask * X) [r x K] and dB = dY^T U~ [N x r], over all tokens
+  if (r > 0 && (e = qlora::launch_colpass(X, (int)K, Vt, dY, (int)N, Ut, (int)M, r, dm, dA, dB, f16, stream)) !=
+                   hipSuccess)
+    return hip_fail(e, "dA / dB launch");
+  return QLORA_OK;
 }
 
 int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* X, int64_t M, const uint16_t* A,

@@ -298,6 +298,82 @@ struct ARing {
   static constexpr int kSteps = NN ? 1 : 2;
 };
 
+// The adapter's token-side operand from the row pass's fp32 partial sums
+// (gemm_args.h): element (m, j) = E(scale * sum over z, in order, of
+// part[z][m][j]), rows past M and ranks past r zero, for the lane's rows
+// row0 + 32 i + (lane & 31) and ranks 16 ks + 8 (lane >> 5) .. + 7.  `store`:
+// also write those elements to lora_out [M x r].
+template <typename E>
+__device__ __forceinline__ void adapter_from_partials(const GemmArgs& a, int row0, int lane, int nks, bool store,
+                                                      uint4 (&uf)[4][2]) {
+  // one buffer resource per split over this wave's 64 rows (rows past M
+  // read zeros); the loads of 4 splits are in flight together.  row0 is
+  // uniform across the wave: say so, or the resource needs a waterfall loop.
+  const int urow0 = __builtin_amdgcn_readfirstlane(row0);
+  const uint32_t rbytes = (uint32_t)a.lora_rp * 4u;
+  const uint32_t pbytes = __builtin_amdgcn_readfirstlane((uint32_t)max(0, min(64, a.M - urow0)) * rbytes);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int j = 16 * ks + 8 * (lane >> 5);
+    const bool ok = ks < nks && j < a.r;
+    float s[2][8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[i][e] = 0.f;
+    if (ks < nks) {
+      for (int z0 = 0; z0 < a.lora_ns; z0 += 4) {
+        uint4 v[4][2][2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int z = min(z0 + q, a.lora_ns - 1);
+          const __amdgpu_buffer_rsrc_t rs =
+              make_rsrc(a.lora_part + ((size_t)z * (size_t)a.M + (size_t)urow0) * (size_t)a.lora_rp,
+                        pbytes);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const uint32_t off = (uint32_t)(32 * i + (lane & 31)) * rbytes + 4u * (uint32_t)j;
+            v[q][i][0] = buf_load16(rs, ok ? off : kOOB);
+            v[q][i][1] = buf_load16(rs, ok ? off + 16u : kOOB);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (z0 + q >= a.lora_ns) break;
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              s[i][4 * h + 0] += __builtin_bit_cast(float, v[q][i][h].x);
+              s[i][4 * h + 1] += __builtin_bit_cast(float, v[q][i][h].y);
+              s[i][4 * h + 2] += __builtin_bit_cast(float, v[q][i][h].z);
+              s[i][4 * h + 3] += __builtin_bit_cast(float, v[q][i][h].w);
+            }
+        }
+      }
+    }
+    const float c = a.lora_scale;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int m = row0 + 32 * i + (lane & 31);
+      uf[ks][i] = ok ? make_uint4(E::pack2(c * s[i][0], c * s[i][1]), E::pack2(c * s[i][2], c * s[i][3]),
+                                  E::pack2(c * s[i][4], c * s[i][5]), E::pack2(c * s[i][6], c * s[i][7]))
+                     : make_uint4(0, 0, 0, 0);
+      if (store && ok && m < a.M && a.lora_out) {
+        uint16_t* o = a.lora_out + (size_t)m * (size_t)a.r + j;
+        if ((a.r & 7) == 0) {
+          *reinterpret_cast<uint4*>(o) = uf[ks][i];
+        } else {
+          const uint32_t w[4] = {uf[ks][i].x, uf[ks][i].y, uf[ks][i].z, uf[ks][i].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (j + e < a.r) o[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+  }
+}
+
 // Wave-specialised workgroup of 8 waves, two per SIMD:
 //   waves 0-3 (consumers) run the MFMAs of their 64 x 128 output slice; they
 //   load their activation fragments themselves from the tiled copy (one or
@@ -427,6 +503,25 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
     wait_vmcnt<0>();
   } else {
     constexpr int DA = ARing<NN>::kSteps;
+    // The adapter's token-side operand (U~ or V~) in MFMA A-operand layout,
+    // formed before the activation loads are issued (fewer live registers).
+    const int nks = (a.r + 15) >> 4;  // 16-rank sub-steps that hold ranks
+    uint4 uf[4][2];
+    if (adapter) {
+      if (a.lora_part) {
+        adapter_from_partials<E>(a, row0, lane, nks, tn == 0, uf);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int m = row0 + 32 * i + (lane & 31), j = 16 * ks + 8 * (lane >> 5);
+            uf[ks][i] = ks < nks ? load_e16x8(src.lora_act, (uint32_t)m * (uint32_t)a.r + (uint32_t)j, m < a.M,
+                                              a.r - j, vec)
+                                 : make_uint4(0, 0, 0, 0);
+          }
+      }
+    }
     const int mbp = tiled_mbp(a.M);
     const __amdgpu_buffer_rsrc_t ract = make_rsrc(a.act_t, (uint32_t)tiled_bytes(a.M, a.R));
     // byte offsets of this lane in the two fragment blocks of the wave's rows
@@ -448,18 +543,6 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
       for (int ks = 0; ks < 4; ++ks) load_a(d, ks, ar[d].f[ks]);
 
     if (adapter) {
-      // token-side rows (U~ or V~, [M x r]) straight into MFMA A operands
-      const int nks = (a.r + 15) >> 4;  // 16-rank sub-steps that hold ranks
-      uint4 uf[4][2];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int m = row0 + 32 * i + (lane & 31), j = 16 * ks + 8 * (lane >> 5);
-          uf[ks][i] = ks < nks ? load_e16x8(src.lora_act, (uint32_t)m * (uint32_t)a.r + (uint32_t)j, m < a.M,
-                                            a.r - j, vec)
-                               : make_uint4(0, 0, 0, 0);
-        }
       step_barrier();  // adapter operand staged; steps 0 and 1 decoded
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {

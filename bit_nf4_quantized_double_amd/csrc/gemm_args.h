@@ -40,9 +40,18 @@ struct GemmArgs {
   const uint8_t* q8;         // 8-bit block absmax codes
   const float* s2;           // fp32 step per group of 256 blocks
   int K;                     // W row length (k_in)
-  const uint16_t* lora_act;  // U~ or V~ [M x r] bf16 (unused when r == 0)
+  const uint16_t* lora_act;  // U~ or V~ [M x r] bf16 (unused when r == 0 or lora_part is set)
   const uint16_t* lora_w;    // forward: B [n_out x r]; dX: A [r x k_in]
   int r;                     // adapter rank, 0..64
+  // The adapter's token-side operand from row-pass partial sums instead of
+  // lora_act (when lora_part is set): E(lora_scale * sum over z < lora_ns,
+  // in order, of lora_part[z][m][j]), row pitch lora_rp (rank_pitch(r)),
+  // formed in the prologue of the split-0 workgroups; those of column tile
+  // 0 also store it to lora_out [M x r] when that is set.
+  const float* lora_part;
+  int lora_ns, lora_rp;
+  float lora_scale;
+  uint16_t* lora_out;
   uint16_t* out;             // Y [M x n_out] or dX [M x k_in], bf16
   int64_t ld_out;
   Nf4Consts nf4;
@@ -66,6 +75,36 @@ size_t gemm_part_bytes(int64_t M, int64_t C, int64_t R, int cus);
 // order (C % 8 == 0, rows of out 16-byte aligned).
 hipError_t launch_splitk_reduce(const float* part, int ksplit, int M, int C, uint16_t* out, int64_t ld_out, bool f16,
                                 hipStream_t st);
+
+// ---- adapter passes (adapter.hip) -----------------------------------------
+// Row pass over act [M x R]: nch 128-wide chunks of the reduction, S splits
+// of cps chunks each (S <= 8), one partial sum per split.
+struct RowpassPlan {
+  int nch, cps, S;
+};
+RowpassPlan rowpass_plan(int64_t M, int64_t R, int cus);
+int rank_pitch(int r);  // r rounded up to a multiple of 8
+size_t rowpass_part_bytes(int64_t M, int64_t R, int r, int cus);
+
+// One read of act [M x R] (R % 8 == 0) writes the fragment-tiled copy
+// (when `tiled` is set) and the fp32 partial sums part[z][m][j] =
+// sum over split z's columns k of act'[m][k] w(j, k), pitch rank_pitch(r).
+// contig: w(j, k) = A[j][k] (A [r x R]; the forward's X A^T, act' = the
+// dropout mask times X, the tiled copy in the forward's element order);
+// else w(j, k) = B[k][j] (B [R x r]; dY B, natural order, no mask).
+hipError_t launch_rowpass(const uint16_t* act, int M, int R, const uint16_t* w, int r, bool contig, DropMask drop,
+                          float* part, uint16_t* tiled, bool f16, int cus, hipStream_t st);
+
+// U = E(scale * sum over z, in order, of part[z][m][j]) [M x r]: the U~ the
+// forward GEMM forms from the same partials, bit for bit.
+hipError_t launch_rowpass_finalize(const float* part, int S, int M, int r, float scale, uint16_t* U, bool f16,
+                                   hipStream_t st);
+
+// Column pass over all M tokens, one dispatch, fixed summation order:
+// dA = V~^T (mask * X) [r x K] and dB = dY^T U~ stored [N x r], fp32.
+hipError_t launch_colpass(const uint16_t* X, int K, const uint16_t* Vt, const uint16_t* dY, int N,
+                          const uint16_t* Ut, int M, int r, DropMask drop, float* dA, float* dB, bool f16,
+                          hipStream_t st);
 
 // The fragment-tiled copy of act[M][R] (row pitch R elements, R % 8 == 0)
 // alone, for products whose adapter kernels do not run (r == 0); eo: the

@@ -1,20 +1,17 @@
-// Skinny rank-r products of the adapter path ([P1] "The mechanism in brief":
-// the adapter adds (alpha / r) B A x; backward gives gradients for A and B).
+// The adapter's down projection on its own ([P1] "The mechanism in brief":
+// the adapter adds (alpha / r) B A x), for the paths that need U~ before
+// anything else runs: the few-token forward and the backward when the
+// forward's U~ was not kept.
 //
-//   rowdot:   out[m][j] = bf16(scale * sum_k in[m][k] * w(j, k))       (M x r)
-//             U~ = bf16(s X A^T)   and   V~ = bf16(s dY B)
-//   coldot:   part[mc][j][c] = sum_{m in chunk mc} v[m][j] * in[m][c]  (fp32)
-//   finalize: out = sum over chunks, in a fixed order (deterministic)
-//             dA = V~^T X  [r x K]      dB = dY^T U~  -> stored [N x r]
+//   rowdot:   U~[m][j] = E(s sum_k (mask * X)[m][k] A[j][k])        (M x r)
 //
-// All use v_mfma_f32_16x16x32 on 16-bit elements (bf16, or fp16 for the fp16
-// instance) with the rank on the 16-wide side.
+// v_mfma_f32_16x16x32 on 16-bit elements (bf16, or fp16 for the fp16
+// instance) with the rank on the 16-wide side; split partial sums over k are
+// added in a fixed order by a second pass (deterministic).
 #include <algorithm>
 
 #include "common.h"
 #include "dropout.h"
-#include "gemm_args.h"
-#include "nf4_lut.h"
 
 namespace qlora {
 
@@ -76,7 +73,6 @@ struct RowdotArgs {
   uint16_t* out;       // [M x r] bf16
   float* part;         // [nsplit][M][r] fp32, or null when nsplit == 1
   DropMask drop;       // dropout of `in` (thr 0: none)
-  uint16_t* tiled;     // fragment-tiled copy of `in` to write (gemm_args.h), or null
 };
 
 // Workgroup (bx, by) = (64-row block, K split) of the rowdot grid.
@@ -108,23 +104,6 @@ __device__ __forceinline__ void rowdot_body(const RowdotArgs& ra, int bx, int by
     for (int u = 0; u < 8; ++u) {
       const int k = k0 + 32 * u + 8 * kg;
       av[u] = buf_load16(rin, k < k_hi ? row_off + 2u * (uint32_t)k : kOOB);
-    }
-    if (ra.tiled) {
-      // The undropped activations, also into the fragment-tiled copy the
-      // GEMM reads: 16 lanes of one k-group write 256 contiguous bytes.  This
-      // split writes its own columns; the last one also the zero padding up
-      // to whole 64-deep steps, and rows up to the last 32-row block.
-      const int m = m0 + row, kpad = 16 * tiled_kbp(Kd), mpad = 32 * tiled_mbp(M);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int k = k0 + 32 * u + 8 * kg;
-        const bool own = k < k_hi || (k_hi == Kd && k < kpad);
-        // X (the forward's activations, CONTIG) goes in the element order
-        // 0, 2, 4, 6, 1, 3, 5, 7 of each 8 columns, matching the forward
-        // GEMM's W decode; dY keeps its natural order
-        const uint4 v = CONTIG ? x_order_even_odd(av[u]) : av[u];
-        if (own && m < mpad) *reinterpret_cast<uint4*>(ra.tiled + tiled_elem(m, k, tiled_kbp(Kd))) = v;
-      }
     }
     if (ra.drop.thr) {
 #pragma unroll
@@ -264,160 +243,6 @@ __global__ __launch_bounds__(256) void k_rowdot_finalize8(const float* __restric
   }
 }
 
-// ---------------------------------------------------------------- coldot ----
-// Workgroup: 128 columns x one chunk of rows; the 4 waves take interleaved
-// 32-row steps and are summed in LDS in a fixed order.  Each lane loads an
-// 8 x 8 patch (8 rows x 16 bytes) and transposes it in registers, so column
-// c0 + 8q + jj becomes the B operand of MFMA number jj.
-struct ColdotArgs {
-  const uint16_t* v;   // [M x r] bf16 (U~ or V~)
-  int r;
-  const uint16_t* in;  // [M x C] bf16 (dY or X)
-  int M, C, mchunk;
-  float* part;         // [nmc][r][C] fp32
-  DropMask drop;       // dropout of `in` (thr 0: none)
-};
-
-// Workgroup (bx, by) = (128-column tile, row chunk) of the coldot grid.
-template <int RT, typename E>
-__device__ __forceinline__ void coldot_body(const ColdotArgs& ca, int bx, int by, f32x4 (*red)[8][64]) {
-  const uint16_t* __restrict__ v = ca.v;
-  const uint16_t* __restrict__ in = ca.in;
-  const int r = ca.r, M = ca.M, C = ca.C, mchunk = ca.mchunk;
-  float* __restrict__ part = ca.part;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c0 = bx * 128, mc = by;
-  const int mbeg = mc * mchunk, mend = min(M, mbeg + mchunk);
-  const int g = lane >> 4, q = lane & 15;
-  const bool col_ok = c0 + 8 * q < C;
-  f32x4 acc[RT][8];
-#pragma unroll
-  for (int t = 0; t < RT; ++t)
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) acc[t][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int m0 = mbeg + wave * 32; m0 < mend; m0 += 128) {
-    uint4 rows[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int m = m0 + 8 * g + i;
-      rows[i] = (m < mend && col_ok) ? *reinterpret_cast<const uint4*>(in + (int64_t)m * C + c0 + 8 * q)
-                                     : make_uint4(0, 0, 0, 0);
-    }
-    if (ca.drop.thr) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        rows[i] = drop8(rows[i], (uint64_t)(m0 + 8 * g + i) * (uint64_t)C + (uint64_t)(c0 + 8 * q), ca.drop);
-    }
-    uint4 colv[8];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t d[4];
-#pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
-        const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&rows[2 * mm]);
-        const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&rows[2 * mm + 1]);
-        d[mm] = __builtin_amdgcn_perm(r1[jj >> 1], r0[jj >> 1], sel);
-      }
-      colv[jj] = make_uint4(d[0], d[1], d[2], d[3]);
-    }
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const int j = 16 * t + q;
-      uint16_t e[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int m = m0 + 8 * g + i;
-        e[i] = (j < r && m < mend) ? v[(int64_t)m * r + j] : (uint16_t)0;
-      }
-      uint4 av = make_uint4(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
-                            e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16));
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        acc[t][jj] = E::mfma16(E::vec(av), E::vec(colv[jj]), acc[t][jj]);
-    }
-  }
-  // D[j][col]: j = 16t + 4*(lane>>4) + v, column index lane&15 -> c0 + 8*(lane&15) + jj
-#pragma unroll
-  for (int t = 0; t < RT; ++t) {
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) red[wave][jj][lane] = acc[t][jj];
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 8 * 64; idx += 256) {
-      const int jj = idx >> 6, ln = idx & 63;
-      f32x4 s = red[0][jj][ln];
-#pragma unroll
-      for (int w = 1; w < 4; ++w) s += red[w][jj][ln];
-      const int c = c0 + 8 * (ln & 15) + jj;
-#pragma unroll
-      for (int vv = 0; vv < 4; ++vv) {
-        const int j = 16 * t + 4 * (ln >> 4) + vv;
-        if (j < r && c < C) part[((int64_t)mc * r + j) * C + c] = s[vv];
-      }
-    }
-    __syncthreads();
-  }
-}
-
-template <int RT, typename E>
-__global__ __launch_bounds__(256) void k_coldot(ColdotArgs ca) {
-  __shared__ f32x4 red[4][8][64];
-  coldot_body<RT, E>(ca, blockIdx.x, blockIdx.y, red);
-}
-
-// out[j][c] (or out[c][j] when TRANS) = sum_{mc} part[mc][j][c], fixed order.
-template <bool TRANS>
-__device__ __forceinline__ void finalize_body(const float* __restrict__ part, int nmc, int r, int C,
-                                              float* __restrict__ out, int b, int nb) {
-  const int64_t total = (int64_t)r * C;
-  for (int64_t idx = (int64_t)b * 256 + threadIdx.x; idx < total; idx += (int64_t)nb * 256) {
-    const int j = (int)(idx / C), c = (int)(idx % C);
-    float s = 0.f;
-    int mc = 0;
-    for (; mc + 8 <= nmc; mc += 8) {  // 8 loads in flight, added in chunk order
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = part[((int64_t)(mc + u) * r + j) * C + c];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) s += v[u];
-    }
-    for (; mc < nmc; ++mc) s += part[((int64_t)mc * r + j) * C + c];
-    if (TRANS) out[(int64_t)c * r + j] = s; else out[idx] = s;
-  }
-}
-
-template <bool TRANS>
-__global__ __launch_bounds__(256) void k_finalize(const float* __restrict__ part, int nmc, int r, int C,
-                                                  float* __restrict__ out) {
-  finalize_body<TRANS>(part, nmc, r, C, out, blockIdx.x, gridDim.x);
-}
-
-// ---- merged launches of the backward (independent work, one dispatch) ----
-// Blocks [0, nr) run the V~ rowdot grid (nr = row blocks x splits), blocks
-// [nr, nr + nc) the dB coldot grid: both read dY, neither needs the other.
-template <int RT, typename E>
-__global__ __launch_bounds__(256) void k_vt_and_db(RowdotArgs ra, int rb, ColdotArgs ca, int ctiles) {
-  __shared__ __attribute__((aligned(16))) uint16_t sw[RowdotLds<false, RT>::kElems];
-  __shared__ f32x4 red[4][8][64];
-  const int nr = rb * ra.nsplit;
-  const int b = blockIdx.x;
-  if (b < nr) rowdot_body<false, RT, E>(ra, b % rb, b / rb, sw);
-  else coldot_body<RT, E>(ca, (b - nr) % ctiles, (b - nr) / ctiles, red);
-}
-
-// Blocks [0, n1) finalize V~ (when it was split), blocks [n1, n1 + n2)
-// finalize dB (stored [N x r]).
-template <typename E>
-__global__ __launch_bounds__(256) void k_fin_vt_and_db(const float* __restrict__ vpart, int nsplit, int64_t nv,
-                                                       float scale, uint16_t* __restrict__ vout, int n1,
-                                                       const float* __restrict__ cpart, int nmc, int r, int C,
-                                                       float* __restrict__ dB, int n2) {
-  const int b = blockIdx.x;
-  if (b < n1) rowdot_finalize_body<E>(vpart, nsplit, nv, scale, vout, b, n1);
-  else finalize_body<true>(cpart, nmc, r, C, dB, b - n1, n2);
-}
-
 __global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_t n) {
   for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
 }
@@ -428,23 +253,23 @@ __global__ __launch_bounds__(256) void k_zero_u16(uint16_t* __restrict__ p, int6
 
 template <bool CONTIG, int RT, typename E>
 void rowdot_launch(dim3 grid, hipStream_t st, const uint16_t* in, int M, int Kd, const uint16_t* wt, int r,
-                   int kchunk, float scale, uint16_t* out, float* part, DropMask drop, uint16_t* tiled) {
-  const RowdotArgs ra{in, M, Kd, wt, r, kchunk, (int)grid.y, scale, out, part, drop, tiled};
+                   int kchunk, float scale, uint16_t* out, float* part, DropMask drop) {
+  const RowdotArgs ra{in, M, Kd, wt, r, kchunk, (int)grid.y, scale, out, part, drop};
   hipLaunchKernelGGL((k_rowdot<CONTIG, RT, E>), grid, dim3(256), 0, st, ra);
 }
 
 template <bool CONTIG, typename E>
 hipError_t rowdot_dispatch(const uint16_t* in, int M, int Kd, const uint16_t* wt, int r, float scale,
-                           uint16_t* out, float* part, DropMask drop, uint16_t* tiled, hipStream_t st) {
+                           uint16_t* out, float* part, DropMask drop, hipStream_t st) {
   int nsplit, kchunk;
   rowdot_split(M, Kd, &nsplit, &kchunk);
   dim3 grid((M + 63) / 64, nsplit);
   float* p = nsplit > 1 ? part : nullptr;
   switch ((r + 15) / 16) {
-    case 1: rowdot_launch<CONTIG, 1, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop, tiled); break;
-    case 2: rowdot_launch<CONTIG, 2, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop, tiled); break;
-    case 3: rowdot_launch<CONTIG, 3, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop, tiled); break;
-    default: rowdot_launch<CONTIG, 4, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop, tiled); break;
+    case 1: rowdot_launch<CONTIG, 1, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
+    case 2: rowdot_launch<CONTIG, 2, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
+    case 3: rowdot_launch<CONTIG, 3, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
+    default: rowdot_launch<CONTIG, 4, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
@@ -462,89 +287,11 @@ hipError_t rowdot_dispatch(const uint16_t* in, int M, int Kd, const uint16_t* wt
 }  // namespace
 
 // U~ = E(s (mask * X) A^T): in = X [M x K], A [r x K]; E = fp16 when f16,
-// else bf16.  Xt: the fragment-tiled copy of X to write too, or null.
+// else bf16.  part: fp32 split partials (rowdot_part_bytes).
 hipError_t launch_lora_down(const uint16_t* X, int M, int K, const uint16_t* A, int r, float s, uint16_t* U,
-                            float* part, DropMask drop, bool f16, uint16_t* Xt, hipStream_t st) {
-  return f16 ? rowdot_dispatch<true, F16>(X, M, K, A, r, s, U, part, drop, Xt, st)
-             : rowdot_dispatch<true, Bf16>(X, M, K, A, r, s, U, part, drop, Xt, st);
-}
-
-int coldot_chunk_rows() { return 256; }
-
-namespace {
-
-template <typename E>
-void coldot_launch(dim3 grid, const ColdotArgs& ca, int rt, hipStream_t st) {
-  switch (rt) {
-    case 1: hipLaunchKernelGGL((k_coldot<1, E>), grid, dim3(256), 0, st, ca); break;
-    case 2: hipLaunchKernelGGL((k_coldot<2, E>), grid, dim3(256), 0, st, ca); break;
-    case 3: hipLaunchKernelGGL((k_coldot<3, E>), grid, dim3(256), 0, st, ca); break;
-    default: hipLaunchKernelGGL((k_coldot<4, E>), grid, dim3(256), 0, st, ca); break;
-  }
-}
-
-template <typename E>
-void vt_and_db_launch(dim3 grid, const RowdotArgs& ra, int rb, const ColdotArgs& ca, int ctiles, int rt,
-                      hipStream_t st) {
-  switch (rt) {
-    case 1: hipLaunchKernelGGL((k_vt_and_db<1, E>), grid, dim3(256), 0, st, ra, rb, ca, ctiles); break;
-    case 2: hipLaunchKernelGGL((k_vt_and_db<2, E>), grid, dim3(256), 0, st, ra, rb, ca, ctiles); break;
-    case 3: hipLaunchKernelGGL((k_vt_and_db<3, E>), grid, dim3(256), 0, st, ra, rb, ca, ctiles); break;
-    default: hipLaunchKernelGGL((k_vt_and_db<4, E>), grid, dim3(256), 0, st, ra, rb, ca, ctiles); break;
-  }
-}
-
-}  // namespace
-
-// part[mc][j][c] = sum over the mc-th chunk of rows of v[m][j] * (mask * in)[m][c]
-hipError_t launch_coldot(const uint16_t* v, int r, const uint16_t* in, int M, int C, float* part, DropMask drop,
-                         bool f16, hipStream_t st) {
-  const int mchunk = coldot_chunk_rows();
-  dim3 grid((C + 127) / 128, (M + mchunk - 1) / mchunk);
-  const ColdotArgs ca{v, r, in, M, C, mchunk, part, drop};
-  if (f16) coldot_launch<F16>(grid, ca, (r + 15) / 16, st);
-  else coldot_launch<Bf16>(grid, ca, (r + 15) / 16, st);
-  return hipGetLastError();
-}
-
-// Backward adapter reductions over dY in two dispatches:
-//   1. V~ split partials (or V~ itself when unsplit) and dB row-chunk partials;
-//   2. V~ finalize (when split) and dB finalize.
-hipError_t launch_vt_and_db(const uint16_t* dY, int M, int N, const uint16_t* B, const uint16_t* U, int r,
-                            float s, uint16_t* V, float* vpart, float* cpart, float* dB, bool f16, uint16_t* dYt,
-                            hipStream_t st) {
-  int nsplit, kchunk;
-  rowdot_split(M, N, &nsplit, &kchunk);
-  const int rb = (M + 63) / 64;
-  const RowdotArgs ra{dY, M, N, B, r, kchunk, nsplit, s, V, nsplit > 1 ? vpart : nullptr, DropMask{}, dYt};
-  const int mchunk = coldot_chunk_rows();
-  const int ctiles = (N + 127) / 128, nmc = (M + mchunk - 1) / mchunk;
-  const ColdotArgs ca{U, r, dY, M, N, mchunk, cpart, DropMask{}};
-  const dim3 grid(rb * nsplit + ctiles * nmc);
-  if (f16) vt_and_db_launch<F16>(grid, ra, rb, ca, ctiles, (r + 15) / 16, st);
-  else vt_and_db_launch<Bf16>(grid, ra, rb, ca, ctiles, (r + 15) / 16, st);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t nv = (int64_t)M * r;
-  const int n1 = nsplit > 1 ? (int)std::max<int64_t>(1, std::min<int64_t>((nv + 255) / 256, 2048)) : 0;
-  const int64_t nc = (int64_t)r * N;
-  const int n2 = (int)std::max<int64_t>(1, std::min<int64_t>((nc + 255) / 256, 4096));
-  if (f16)
-    hipLaunchKernelGGL(k_fin_vt_and_db<F16>, dim3(n1 + n2), dim3(256), 0, st, vpart, nsplit, nv, s, V, n1, cpart,
-                       nmc, r, N, dB, n2);
-  else
-    hipLaunchKernelGGL(k_fin_vt_and_db<Bf16>, dim3(n1 + n2), dim3(256), 0, st, vpart, nsplit, nv, s, V, n1, cpart,
-                       nmc, r, N, dB, n2);
-  return hipGetLastError();
-}
-
-hipError_t launch_finalize(const float* part, int nmc, int r, int C, float* out, bool trans, hipStream_t st) {
-  const int64_t total = (int64_t)r * C;
-  int blocks = (int)std::min<int64_t>((total + 255) / 256, 4096);
-  if (blocks < 1) blocks = 1;
-  if (trans) hipLaunchKernelGGL((k_finalize<true>), dim3(blocks), dim3(256), 0, st, part, nmc, r, C, out);
-  else hipLaunchKernelGGL((k_finalize<false>), dim3(blocks), dim3(256), 0, st, part, nmc, r, C, out);
-  return hipGetLastError();
+                            float* part, DropMask drop, bool f16, hipStream_t st) {
+  return f16 ? rowdot_dispatch<true, F16>(X, M, K, A, r, s, U, part, drop, st)
+             : rowdot_dispatch<true, Bf16>(X, M, K, A, r, s, U, part, drop, st);
 }
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
