@@ -111,7 +111,8 @@ __global__ __launch_bounds__(64 * RowpassWaves<RT2>::n) void k_rowpass(RowpassAr
   constexpr int kWP = CONTIG ? 128 + 8 : kRanks + 8;      // staged w: [rank][k] or [k][rank]
   constexpr int kW = CONTIG ? kRanks * kWP : 128 * kWP;
   constexpr int kWave = kAct + kW;                        // elements per wave
-  constexpr int kRed = NW * 32 * kRanks;                  // fp32 sums of the waves
+  constexpr int kRP = kRanks + 1;                         // reduction pitch (odd: no bank conflicts)
+  constexpr int kRed = NW * 32 * kRP;                     // fp32 sums of the waves
   constexpr int kLds = NW * kWave * 2 > kRed * 4 ? NW * kWave * 2 : kRed * 4;
   __shared__ __attribute__((aligned(16))) uint8_t s_raw[kLds];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -131,18 +132,16 @@ __global__ __launch_bounds__(64 * RowpassWaves<RT2>::n) void k_rowpass(RowpassAr
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
 
-  for (int c = c_lo + wave; c < c_hi; c += NW) {
+  // the chunk of w: CONTIG A[j][k0 .. k0 + 127] -> sw[j][k]; else
+  // B[k0 .. k0 + 127][j] -> sw[k][j]; ranks past r are zero
+  constexpr int kLoads = (CONTIG ? kRanks * 16 : 128 * (kRanks / 8)) / 64;
+  auto load = [&](int c, uint4 (&xv)[8], uint4 (&wv)[kLoads]) {
     const int k0 = 128 * c;
-    uint4 xv[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int m = m0 + 4 * u + lrow, k = k0 + lcol;
       xv[u] = buf_load16(rin, m < a.M && k < a.R ? ((uint32_t)m * (uint32_t)a.R + (uint32_t)k) * 2u : kOOB);
     }
-    // the chunk of w: CONTIG A[j][k0 .. k0 + 127] -> sw[j][k]; else
-    // B[k0 .. k0 + 127][j] -> sw[k][j]; ranks past r are zero
-    constexpr int kLoads = (CONTIG ? kRanks * 16 : 128 * (kRanks / 8)) / 64;
-    uint4 wv[kLoads];
 #pragma unroll
     for (int u = 0; u < kLoads; ++u) {
       const int idx = lane + 64 * u;
@@ -154,6 +153,15 @@ __global__ __launch_bounds__(64 * RowpassWaves<RT2>::n) void k_rowpass(RowpassAr
         wv[u] = ld8(rw, (uint32_t)k * (uint32_t)a.r + 8u * jc, k < a.R, a.r - 8 * jc, (a.r & 7) == 0);
       }
     }
+  };
+
+  // The wave's chunks c_lo + wave, + NW, ...: once a chunk is in LDS the
+  // next one's loads are issued into the same registers, so they are in
+  // flight while the chunk is stored and multiplied.
+  uint4 xv[8], wv[kLoads];
+  if (c_lo + wave < c_hi) load(c_lo + wave, xv, wv);
+  for (int c = c_lo + wave; c < c_hi; c += NW) {
+    const int k0 = 128 * c;
 #pragma unroll
     for (int u = 0; u < 8; ++u) *reinterpret_cast<uint4*>(sa + (4 * u + lrow) * kAP + lcol) = xv[u];
 #pragma unroll
@@ -162,6 +170,7 @@ __global__ __launch_bounds__(64 * RowpassWaves<RT2>::n) void k_rowpass(RowpassAr
       if (CONTIG) *reinterpret_cast<uint4*>(sw + (idx >> 4) * kWP + 8 * (idx & 15)) = wv[u];
       else *reinterpret_cast<uint4*>(sw + (idx / (kRanks / 8)) * kWP + 8 * (idx % (kRanks / 8))) = wv[u];
     }
+    if (c + NW < c_hi) load(c + NW, xv, wv);
     // LDS operations of one wave complete in order: the reads below see the
     // stores above, and the next chunk's stores come after these reads
     __builtin_amdgcn_wave_barrier();
@@ -207,7 +216,7 @@ __global__ __launch_bounds__(64 * RowpassWaves<RT2>::n) void k_rowpass(RowpassAr
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int rl = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), j = 32 * t + (lane & 31);
-      red[(wave * 32 + rl) * kRanks + j] = acc[t][v];
+      red[(wave * 32 + rl) * kRP + j] = acc[t][v];
     }
   __syncthreads();
   for (int idx = tid; idx < 32 * a.rp; idx += 64 * NW) {
@@ -215,7 +224,7 @@ __global__ __launch_bounds__(64 * RowpassWaves<RT2>::n) void k_rowpass(RowpassAr
     if (m0 + rl >= a.M) continue;
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) s += red[(w * 32 + rl) * kRanks + j];
+    for (int w = 0; w < NW; ++w) s += red[(w * 32 + rl) * kRP + j];
     a.part[((size_t)z * a.M + m0 + rl) * a.rp + j] = s;
   }
 }
@@ -234,13 +243,16 @@ struct ColpassJob {
 // 64-row chunks in turn; a chunk of `in` and of `v` is staged in the wave's
 // LDS region and read back transposed as the two MFMA operands (k along the
 // rows).  out^T[c][j] = sum_m in[m][c] v[m][j]; the 8 waves' sums are added
-// in wave order at the end.
+// in wave order at the end.  Once a chunk is in LDS the next one's loads are
+// issued into the same registers, so they are in flight while the chunk is
+// multiplied.
 template <int RT2, typename E>
 __global__ __launch_bounds__(512) void k_colpass(ColpassJob j0, ColpassJob j1, int M, int r) {
   constexpr int kRanks = 32 * RT2;
   constexpr int kXP = 64 + 8, kVP = kRanks + 8;                 // LDS pitches
   constexpr int kWave = 64 * kXP + 64 * kVP;                    // elements per wave
-  constexpr int kRed = 8 * 64 * kRanks;                         // fp32 sums of the 8 waves
+  constexpr int kRP = kRanks + 1;                               // reduction pitch (odd: no bank conflicts)
+  constexpr int kRed = 8 * 64 * kRP;                            // fp32 sums of the 8 waves
   constexpr int kLds = 8 * kWave * 2 > kRed * 4 ? 8 * kWave * 2 : kRed * 4;
   __shared__ __attribute__((aligned(16))) uint8_t s_raw[kLds];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -260,25 +272,32 @@ __global__ __launch_bounds__(512) void k_colpass(ColpassJob j0, ColpassJob j1, i
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[ct][t][v] = 0.f;
 
-  const int nck = (M + 63) >> 6;
-  for (int ck = wave; ck < nck; ck += 8) {
+  constexpr int kVL = kRanks / 8;  // 16-byte loads per lane of a 64-row chunk of v
+  // in[m0 .. m0 + 63][c0 .. c0 + 63] (8 lanes per 128-byte row) and
+  // v[m0 .. m0 + 63][0 .. r) (ranks past r zero)
+  auto load = [&](int ck, uint4 (&xv)[8], uint4 (&vv)[kVL]) {
     const int m0 = 64 * ck;
-    // in[m0 .. m0 + 63][c0 .. c0 + 63]: 8 lanes per 128-byte row
-    uint4 xv[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int idx = lane + 64 * u, rr = idx >> 3, cc = idx & 7;
       const int m = m0 + rr, c = c0 + 8 * cc;
       xv[u] = buf_load16(rin, m < M && c < jb.C ? ((uint32_t)m * (uint32_t)jb.C + (uint32_t)c) * 2u : kOOB);
     }
-    // v[m0 .. m0 + 63][0 .. r), ranks past r zero
-    constexpr int kVL = 64 * (kRanks / 8) / 64;
-    uint4 vv[kVL];
 #pragma unroll
     for (int u = 0; u < kVL; ++u) {
       const int idx = lane + 64 * u, rr = idx / (kRanks / 8), jc = idx % (kRanks / 8), m = m0 + rr;
       vv[u] = ld8(rv, (uint32_t)m * (uint32_t)r + 8u * jc, m < M, r - 8 * jc, (r & 7) == 0);
     }
+  };
+
+  // The wave's chunks wave, wave + 8, ...: once a chunk is in LDS the next
+  // one's loads are issued into the same registers, so they are in flight
+  // while the chunk is multiplied.
+  const int nck = (M + 63) >> 6;
+  uint4 xv[8], vv[kVL];
+  if (wave < nck) load(wave, xv, vv);
+  for (int ck = wave; ck < nck; ck += 8) {
+    const int m0 = 64 * ck;
     if (jb.drop.thr) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -296,6 +315,9 @@ __global__ __launch_bounds__(512) void k_colpass(ColpassJob j0, ColpassJob j1, i
       const int idx = lane + 64 * u;
       *reinterpret_cast<uint4*>(sv + (idx / (kRanks / 8)) * kVP + 8 * (idx % (kRanks / 8))) = vv[u];
     }
+    if (ck + 8 < nck) load(ck + 8, xv, vv);
+    // LDS operations of one wave complete in order: the reads below see the
+    // stores above, and the next chunk's stores come after these reads
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -321,7 +343,7 @@ __global__ __launch_bounds__(512) void k_colpass(ColpassJob j0, ColpassJob j1, i
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int cl = 32 * ct + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), j = 32 * t + (lane & 31);
-        red[(wave * 64 + cl) * kRanks + j] = acc[ct][t][v];
+        red[(wave * 64 + cl) * kRP + j] = acc[ct][t][v];
       }
   __syncthreads();
   for (int idx = tid; idx < 64 * r; idx += 512) {
@@ -330,7 +352,7 @@ __global__ __launch_bounds__(512) void k_colpass(ColpassJob j0, ColpassJob j1, i
     if (c0 + cl >= jb.C) continue;
     float s = 0.f;
 #pragma unroll
-    for (int w8 = 0; w8 < 8; ++w8) s += red[(w8 * 64 + cl) * kRanks + j];
+    for (int w8 = 0; w8 < 8; ++w8) s += red[(w8 * 64 + cl) * kRP + j];
     if (jb.trans) jb.out[(size_t)(c0 + cl) * r + j] = s;
     else jb.out[(size_t)j * jb.C + c0 + cl] = s;
   }
