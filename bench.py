@@ -403,6 +403,8 @@ def bench_secondary(torch, qlora, synth, dev, evs, reps=10):
                                           w0.n_out, w0.k_in) for _ in range(2)]
         out = torch.empty((lin.n_out, lin.k_in), dtype=torch.bfloat16, device=dev)
         nw = lin.n_out * lin.k_in
+        if idx == 0:
+            res["hbm_ceiling_70b_gate"] = bench_hbm_ceiling(torch, out, reps)
         for c in copies:
             qlora.dequant(c, out)
         torch.cuda.synchronize()
@@ -474,6 +476,38 @@ def bench_secondary(torch, qlora, synth, dev, evs, reps=10):
                                                "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
         del copies, w0
         torch.cuda.empty_cache()
+    # the 2-byte-per-weight output alone, written at the measured plain-write
+    # rate, bounds each of these kernels' time from below (gate and down hold
+    # the same number of weights)
+    t_floor = res["hbm_ceiling_70b_gate"]["write_us"]
+    for key in [k for k in res if k.startswith(("dequant_70b", "merge_70b", "requantize_70b"))]:
+        res[key]["frac_plain_write_ceiling"] = round(t_floor / res[key]["us"], 4)
+    return res
+
+
+def bench_hbm_ceiling(torch, out, reps):
+    """Plain-write and plain-copy rates of this GPU on a 16-bit buffer of the
+    70B gate's size (the dequantized weight, 2 bytes per weight), with torch's
+    own fill and copy kernels: what any kernel that writes these bytes can
+    approach.  The copy source is a second buffer of the same size."""
+    src = torch.empty_like(out)
+    src.fill_(0.5)
+    nbytes = out.numel() * out.element_size()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {"bytes": nbytes}
+    for name, fn, moved in (("write", lambda: out.fill_(1.0), nbytes), ("copy", lambda: out.copy_(src), 2 * nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps * 3):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        us = 1e3 * a.elapsed_time(b) / (reps * 3)
+        res[f"{name}_us"] = round(us, 2)
+        res[f"{name}_GB/s"] = round(moved / (us * 1e-6) / 1e9, 1)
+        res[f"{name}_frac_hbm"] = round(moved / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+    del src
     return res
 
 
