@@ -87,53 +87,85 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
   // instruction touches fall in 16 different LDS banks (rows a multiple of
   // 128 bytes apart hit 2 banks: about 30 conflict cycles per read).
   const int nbr = a.K >> 6;
+  // Blocks of each row the workgroup reads: all of them, or with the
+  // reduction split only those of its own chunks, [blk0, blk0 + nbl).
+  const int blk0 = 2 * cbase;
+  const int nbl = max(1, min(2 * a.kchunks, nbr - blk0));
   const uint32_t R = (uint32_t)a.tiles * 16u;
-  const uint32_t qp = (nbr & 3) ? (uint32_t)nbr : (uint32_t)nbr + 4u;  // LDS row pitch in bytes
-  const uint32_t qbase = (uint32_t)blockIdx.x * R * (uint32_t)nbr;    // first block
-  const uint32_t qbytes = R * (uint32_t)nbr;                         // multiple of 16
-  const uint32_t g_first = qbase >> 8;
+  const uint32_t qp = (nbl & 3) ? (uint32_t)nbl : (uint32_t)nbl + 4u;  // LDS row pitch in bytes
+  const uint32_t rowbase = (uint32_t)blockIdx.x * R;                  // first W row
+  const uint32_t qbase = rowbase * (uint32_t)nbr;                     // its first block
+  const uint32_t g_first = (qbase + (uint32_t)blk0) >> 8;
   const uint8_t* const s_q8 = reinterpret_cast<const uint8_t*>(s_dyn);
   const float* const s_s2 = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(s_dyn) + R * qp);
   if (SL) {
     uint8_t* q8w = reinterpret_cast<uint8_t*>(s_dyn);
     float* s2w = reinterpret_cast<float*>(q8w + R * qp);
-    const uint32_t ngs = ((qbase + qbytes - 1) >> 8) - g_first + 1;
-    uint4 qv[kSkMaxStageLoads];  // all staged loads in flight at once
-#pragma unroll
-    for (int u = 0; u < kSkMaxStageLoads; ++u) {
-      const uint32_t i = (uint32_t)tid + (uint32_t)u * kSkThreads;
-      qv[u] = buf_load16(src.q8, i < qbytes / 16 ? qbase + 16 * i : kOOB);
-    }
+    const uint32_t ngs = ((qbase + (R - 1) * (uint32_t)nbr + (uint32_t)(blk0 + nbl) - 1) >> 8) - g_first + 1;
     float sv = 0.f;
     if ((uint32_t)tid < ngs) sv = __builtin_bit_cast(float, buf_load4(src.s2, (g_first + tid) * 4));
+    if (nbl == nbr) {
+      // whole rows: one contiguous run of R * nbr bytes (a multiple of 16)
+      const uint32_t qbytes = R * (uint32_t)nbr;
+      uint4 qv[kSkMaxStageLoads];  // all staged loads in flight at once
 #pragma unroll
-    for (int u = 0; u < kSkMaxStageLoads; ++u) {
-      const uint32_t i = (uint32_t)tid + (uint32_t)u * kSkThreads;
-      if (i < qbytes / 16) {
-        if (qp == (uint32_t)nbr) {
-          *reinterpret_cast<uint4*>(q8w + 16 * i) = qv[u];
-        } else {
-          // dwords 4 i .. 4 i + 3 of the rows: row r = 16 i / nbr, byte b (a multiple of 4)
-          uint32_t r = (16 * i) / (uint32_t)nbr, b = 16 * i - r * (uint32_t)nbr;
-          const uint32_t dw[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+      for (int u = 0; u < kSkMaxStageLoads; ++u) {
+        const uint32_t i = (uint32_t)tid + (uint32_t)u * kSkThreads;
+        qv[u] = buf_load16(src.q8, i < qbytes / 16 ? qbase + 16 * i : kOOB);
+      }
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            *reinterpret_cast<uint32_t*>(q8w + r * qp + b) = dw[d];
-            b += 4;
-            if (b == (uint32_t)nbr) { b = 0; ++r; }
+      for (int u = 0; u < kSkMaxStageLoads; ++u) {
+        const uint32_t i = (uint32_t)tid + (uint32_t)u * kSkThreads;
+        if (i < qbytes / 16) {
+          if (qp == (uint32_t)nbr) {
+            *reinterpret_cast<uint4*>(q8w + 16 * i) = qv[u];
+          } else {
+            // dwords 4 i .. 4 i + 3 of the rows: row r = 16 i / nbr, byte b (a multiple of 4)
+            uint32_t r = (16 * i) / (uint32_t)nbr, b = 16 * i - r * (uint32_t)nbr;
+            const uint32_t dw[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              *reinterpret_cast<uint32_t*>(q8w + r * qp + b) = dw[d];
+              b += 4;
+              if (b == (uint32_t)nbr) { b = 0; ++r; }
+            }
           }
         }
+      }
+    } else if (((nbr | blk0 | nbl) & 3) == 0) {
+      // a split: nbl bytes of each row, as dwords (every piece 4-byte aligned)
+      // (batches of kSkMaxStageLoads dwords per thread, all in flight at once)
+      const uint32_t pr = (uint32_t)nbl / 4, n = R * pr;
+      for (uint32_t i0 = 0; i0 < n; i0 += kSkMaxStageLoads * kSkThreads) {
+        uint32_t qv[kSkMaxStageLoads];
+#pragma unroll
+        for (int u = 0; u < kSkMaxStageLoads; ++u) {
+          const uint32_t i = i0 + (uint32_t)tid + (uint32_t)u * kSkThreads, r = i / pr, d = i - r * pr;
+          qv[u] = buf_load4(src.q8, i < n ? (rowbase + r) * (uint32_t)nbr + (uint32_t)blk0 + 4 * d : kOOB);
+        }
+#pragma unroll
+        for (int u = 0; u < kSkMaxStageLoads; ++u) {
+          const uint32_t i = i0 + (uint32_t)tid + (uint32_t)u * kSkThreads, r = i / pr, d = i - r * pr;
+          if (i < n) *reinterpret_cast<uint32_t*>(q8w + r * qp + 4 * d) = qv[u];
+        }
+      }
+    } else {
+      // a split with unaligned pieces: byte by byte
+      for (uint32_t i = (uint32_t)tid; i < R * (uint32_t)nbl; i += kSkThreads) {
+        const uint32_t r = i / (uint32_t)nbl, b = i - r * (uint32_t)nbl;
+        q8w[r * qp + b] = (uint8_t)buf_load1(src.q8, (rowbase + r) * (uint32_t)nbr + (uint32_t)blk0 + b);
       }
     }
     if ((uint32_t)tid < ngs) s2w[tid] = sv;
     __syncthreads();
   }
-  // block scale a' = fp32(q8 * s2) of tile t, chunk c for this lane
+  // block scale a' = fp32(q8 * s2) of tile t, chunk c for this lane; chunks
+  // past the split (padding: X == 0 there) take any staged finite scale
   auto lds_scale = [&](int t, int c) {
-    const int blk = min(2 * c + (g >> 1), nbr - 1);  // padding chunks: any finite scale
+    const int bl = min(min(2 * c + (g >> 1), nbr - 1) - blk0, nbl - 1);  // staged block index
     const uint32_t rw = (uint32_t)((wa * TPW + t) * 16 + row);
-    const uint32_t bl = rw * (uint32_t)nbr + (uint32_t)blk;  // block index within the workgroup's rows
-    return (float)s_q8[rw * qp + (uint32_t)blk] * s_s2[((qbase + bl) >> 8) - g_first];
+    const uint32_t gb = qbase + rw * (uint32_t)nbr + (uint32_t)(blk0 + bl);  // global block index
+    return (float)s_q8[rw * qp + (uint32_t)bl] * s_s2[(gb >> 8) - g_first];
   };
   const uint32_t e0 = (uint32_t)n0 * (uint32_t)a.K + 32u * (uint32_t)g;  // weight index at chunk 0
 
@@ -389,11 +421,19 @@ hipError_t launch_skinny_fwd(SkinnyArgs a, hipStream_t st) {
   a.nci = nci;
   const dim3 grid((ntiles + a.tiles - 1) / a.tiles, ks);
   const size_t red = (size_t)a.tiles * nwk * 64 * sizeof(float4);
-  // staged scales: q8 of 16 * tiles rows plus the s2 groups they span
-  const size_t qbytes = (size_t)a.tiles * 16 * (size_t)(a.K / 64);
-  const size_t qpad = ((a.K / 64) & 3) ? 0 : (size_t)a.tiles * 16 * 4;  // row padding of the LDS copy
-  const size_t sbytes = qbytes + qpad + 4 * (qbytes / 256 + 2);
-  const bool sl = a.K >= 64 && sbytes <= 60 * 1024;  // stays within the default 64 KB of dynamic LDS
+  // staged scales: q8 of 16 * tiles rows (the blocks of one split's chunks
+  // when the reduction is split; the first split has the most), plus the
+  // s2 groups the rows span
+  const size_t nbr = (size_t)(a.K / 64);
+  const size_t nbl = std::max<size_t>(1, std::min<size_t>(2 * (size_t)a.kchunks, nbr));
+  const size_t rows = (size_t)a.tiles * 16;
+  const size_t qbytes = rows * nbl;
+  const size_t qpad = (nbl & 3) ? 0 : rows * 4;  // row padding of the LDS copy
+  const size_t ngs = rows * nbr / 256 + 2;       // s2 groups, one staging thread each
+  const size_t sbytes = qbytes + qpad + 4 * ngs;
+  // within the default 64 KB of dynamic LDS (so the whole-row copy takes at
+  // most kSkMaxStageLoads 16-byte pieces per thread), one thread per s2 group
+  const bool sl = a.K >= 64 && sbytes <= 60 * 1024 && ngs <= (size_t)kSkThreads;
   const size_t lds = std::max(red, sl ? sbytes : (size_t)0);
   switch (tpw * 16 + rd) {
     case 1 * 16 + 1: return sk_launch<1, 1>(a, grid, lds, sl, st);
