@@ -371,6 +371,10 @@ SHAPES = [
     (64, 264, 4096, 8, 16.0),     # forward split 8 ways over a partial column tile
     (16, 2048, 1024, 16, 32.0),   # few-token forward; dX (GEMM) split 4 ways at 16 tokens
     (1, 1024, 2048, 8, 16.0),     # one token: dX split 2 ways over a single row
+    (40, 512, 8192, 16, 32.0),    # row passes at their most splits: 8 partial sums in the GEMM prologue
+    (70, 328, 6400, 24, 48.0),    # 6 row-pass splits, the last one chunk short; 24 ranks
+    (20, 64, 64, 16, 32.0),       # GEMM path over a single 64-deep step (half a 128-wide chunk)
+    (40, 8192, 512, 16, 32.0),    # the row pass over dY at 8 splits: V~ from 8 partials in the dX prologue
 ]
 
 
