@@ -643,8 +643,11 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
   // The ring is free (every wave passed the last barrier).  Each consumer
   // stages its 64 x 128 tile in rows of its own LDS region, then reads it
   // back 16 bytes per lane: every global store instruction writes 4 rows of
-  // 256 contiguous bytes instead of 2-byte pieces.
+  // 256 contiguous bytes instead of 2-byte pieces.  The stores are
+  // non-temporal (the output is not read again here): about 1 us less per
+  // launch than plain stores on the 7B shapes.
   if (!producer) {
+    typedef __attribute__((ext_vector_type(4))) unsigned v4u;
     uint16_t* so = s_w + slice * (64 * kOutPitch);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -665,7 +668,8 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
       const int rl = 4 * t + (lane >> 4), cl = 8 * (lane & 15);
       const uint4 v = *reinterpret_cast<const uint4*>(so + rl * kOutPitch + cl);
       const int row = row0 + rl, col = c0 + cl;
-      if (row < a.M && col < a.C) *reinterpret_cast<uint4*>(a.out + (int64_t)row * a.ld_out + col) = v;
+      if (row < a.M && col < a.C)
+        __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(a.out + (int64_t)row * a.ld_out + col));
     }
   }
 }
