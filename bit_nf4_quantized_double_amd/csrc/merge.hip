@@ -16,8 +16,10 @@
 // with the operands arranged so the accumulator lands where the output goes:
 // the MFMA's M index runs over columns, permuted so that lane l ends up
 // holding t[n][64 g + 0 .. 63] of row n = l & 15, g = l >> 4 -- exactly one
-// 64-weight block.  The lane decodes that block's 32 bytes of codes, adds
-// s * t and puts the 128 bytes of merged weight in a wave-private LDS tile,
+// 64-weight block.  The lane decodes that block's 32 bytes of codes (with
+// the block's 16 decoded values as a byte-plane table in registers, looked
+// up with v_perm_b32: no LDS reads), adds s * t and puts the 128 bytes of
+// merged weight in a wave-private LDS tile,
 // which the wave reads back row by row so every store instruction writes two
 // contiguous 512-byte rows (16-byte pieces of 64 separate rows per store ran
 // at half the speed).  The M-operand comes from the LDS copy of A through
@@ -26,6 +28,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "nf4_lut.h"
 
 namespace qlora {
 namespace {
@@ -58,6 +61,25 @@ __device__ __forceinline__ uint4 load8(const uint16_t* p, int valid, bool ok, bo
                     h[6] | (uint32_t)h[7] << 16);
 }
 
+// The lane's block table, all 16 entries bf16(level[c] * a), as the two
+// byte-plane halves decode8_lut reads ("a" = levels 0..7, "b" = 8..15): a
+// lane here decodes a whole block, so it builds the whole table itself.
+__device__ __forceinline__ Lut block_lut(const Nf4Consts& c, float a) {
+  uint32_t p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = pack_bf16x2(c.level[2 * i] * a, c.level[2 * i + 1] * a);
+  Lut L;
+  L.alo0 = __builtin_amdgcn_perm(p[1], p[0], 0x06040200u);
+  L.ahi0 = __builtin_amdgcn_perm(p[1], p[0], 0x07050301u);
+  L.alo1 = __builtin_amdgcn_perm(p[3], p[2], 0x06040200u);
+  L.ahi1 = __builtin_amdgcn_perm(p[3], p[2], 0x07050301u);
+  L.blo0 = __builtin_amdgcn_perm(p[5], p[4], 0x06040200u);
+  L.bhi0 = __builtin_amdgcn_perm(p[5], p[4], 0x07050301u);
+  L.blo1 = __builtin_amdgcn_perm(p[7], p[6], 0x06040200u);
+  L.bhi1 = __builtin_amdgcn_perm(p[7], p[6], 0x07050301u);
+  return L;
+}
+
 template <int RP>
 __global__ __launch_bounds__(256) void k_merge(const uint4* __restrict__ codes, const uint8_t* __restrict__ q8,
                                                const float* __restrict__ s2, int N, int K,
@@ -65,11 +87,9 @@ __global__ __launch_bounds__(256) void k_merge(const uint4* __restrict__ codes, 
                                                int r, float s, uint16_t* __restrict__ out, Nf4Consts c) {
   __shared__ __attribute__((aligned(16))) uint16_t sa[RP * kAPitch];
   __shared__ __attribute__((aligned(16))) uint16_t so[4 * kWaveRows * kOPitch];
-  __shared__ float lv[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k0 = blockIdx.x * kTileK, n0 = blockIdx.y * kRowsPerWg;
   const bool vec = (r & 7) == 0;
-  if (tid < 16) lv[tid] = c.level[tid];
 
   // A[:, k0 : k0 + 256] -> LDS (rows j >= r and columns >= K are zero).
   // Column k0 + 64 p + 4 m + e (p < 4, m < 16, e < 4) is stored at
@@ -145,9 +165,11 @@ __global__ __launch_bounds__(256) void k_merge(const uint4* __restrict__ codes, 
     // staging tile (row, columns 64 g .. + 63)
     uint16_t* sw = so + wave * (kWaveRows * kOPitch);
     const uint32_t cwd[8] = {cc0.x, cc0.y, cc0.z, cc0.w, cc1.x, cc1.y, cc1.z, cc1.w};
+    const Lut L = block_lut(c, scc);
+    const LaneMask lm = lane_mask(false);
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
-      const uint4 wb = decode8(cwd[d], scc, lv);  // weights 8 d .. 8 d + 7 = tiles 2 d, 2 d + 1
+      const uint4 wb = decode8_lut(L, cwd[d], lm);  // weights 8 d .. 8 d + 7 = tiles 2 d, 2 d + 1
       const uint32_t wv[4] = {wb.x, wb.y, wb.z, wb.w};
       uint32_t o[4];
 #pragma unroll
