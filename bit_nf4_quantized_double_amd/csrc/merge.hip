@@ -10,10 +10,12 @@
 // result rounded once to bf16 (round to nearest even).
 //
 // Workgroup: 4 waves over a 256-column slice of the weight; the slice of A
-// (RP x 256, zero-padded to RP = 32 or 64 ranks) is staged once in LDS and
-// each wave then walks 16-row blocks on its own, with no workgroup barrier.
-// The rank-r product of a 16 x 256 block runs on v_mfma_f32_16x16x32_bf16
-// with the operands arranged so the accumulator lands where the output goes:
+// (RP x 256, zero-padded to RP = 16, 32 or 64 ranks) is staged once in LDS
+// and each wave then walks 16-row blocks on its own, with no workgroup
+// barrier.  The rank-r product of a 16 x 256 block runs on
+// v_mfma_f32_16x16x32_bf16 (v_mfma_f32_16x16x16_bf16 for up to 16 ranks,
+// so that rank 16 neither reads nor multiplies 16 ranks of zeros) with the
+// operands arranged so the accumulator lands where the output goes:
 // the MFMA's M index runs over columns, permuted so that lane l ends up
 // holding t[n][64 g + 0 .. 63] of row n = l & 15, g = l >> 4 -- exactly one
 // 64-weight block.  The lane decodes that block's 32 bytes of codes (with
@@ -113,9 +115,14 @@ __global__ __launch_bounds__(256) void k_merge(const uint4* __restrict__ codes, 
   // operands of one 16-row block held in registers: this lane's 64 codes
   // and block scale, and its B fragments (B[n][32 u + 8 g .. + 7]).  The
   // next block's are requested before the current one is computed.
+  // RP = 16: v_mfma_f32_16x16x16_bf16, 4 ranks per lane group (lane group
+  // g: ranks 4 g .. 4 g + 3); else the 32-deep MFMA, 8 ranks per group.
+  constexpr int KD = RP == 16 ? 16 : 32;  // MFMA depth
+  constexpr int NU = RP / KD;             // MFMAs per output tile
+  constexpr int RG = KD / 4;              // ranks per lane group
   uint4 cw[2];
   float sc;
-  uint4 bf[RP / 32];
+  uint4 bf[NU];
   auto fetch = [&](int nb) {
     const int n = nb + row;
     const bool ok = n < N && kok;
@@ -124,9 +131,19 @@ __global__ __launch_bounds__(256) void k_merge(const uint4* __restrict__ codes, 
     cw[1] = ok ? codes[(e >> 5) + 1] : make_uint4(0, 0, 0, 0);
     sc = ok ? block_scale(q8, s2, e >> 6) : 0.f;
 #pragma unroll
-    for (int u = 0; u < RP / 32; ++u) {
-      const int j = 32 * u + 8 * g;
-      bf[u] = load8(B + (int64_t)n * r + j, r - j, n < N, vec);
+    for (int u = 0; u < NU; ++u) {
+      const int j = KD * u + RG * g;
+      if (RG == 8) {
+        bf[u] = load8(B + (int64_t)n * r + j, r - j, n < N, vec);
+      } else if ((r & 3) == 0) {  // 4 ranks of a row, 8-byte aligned
+        const uint2 v = (n < N && j < r) ? *reinterpret_cast<const uint2*>(B + (int64_t)n * r + j) : make_uint2(0, 0);
+        bf[u] = make_uint4(v.x, v.y, 0u, 0u);
+      } else {
+        uint16_t h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = (n < N && j + i < r) ? B[(int64_t)n * r + j + i] : (uint16_t)0;
+        bf[u] = make_uint4(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16, 0u, 0u);
+      }
     }
   };
   const int nw0 = n0 + kWaveRows * wave;
@@ -137,9 +154,9 @@ __global__ __launch_bounds__(256) void k_merge(const uint4* __restrict__ codes, 
     if (nb >= N) break;  // uniform over the wave
     const uint4 cc0 = cw[0], cc1 = cw[1];
     const float scc = sc;
-    uint4 bcur[RP / 32];
+    uint4 bcur[NU];
 #pragma unroll
-    for (int u = 0; u < RP / 32; ++u) bcur[u] = bf[u];
+    for (int u = 0; u < NU; ++u) bcur[u] = bf[u];
     if (sb + 1 < kSubBlocks) fetch(nb + 4 * kWaveRows);
 
     // acc[m][v] = t[nb + row][k0 + 64 g + 4 m + v] = sum_j A[j][k] B[n][j]
@@ -147,18 +164,23 @@ __global__ __launch_bounds__(256) void k_merge(const uint4* __restrict__ codes, 
 #pragma unroll
     for (int m = 0; m < 16; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < RP / 32; ++u) {
-      const int jb = 32 * u + 8 * g + q;
-      const bf16x8 bn = __builtin_bit_cast(bf16x8, bcur[u]);
+    for (int u = 0; u < NU; ++u) {
+      const int jb = KD * u + RG * g + q;
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
         // lane p + 4 q addresses row jb, stored columns 16 m + 4 p .. + 3; it
         // receives stored column 16 m + (lane & 15), rows jb - q .. + 3 (and + 4 .. + 7)
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sa + jb * kAPitch + 16 * m + 4 * p));
-        const i16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sa + (jb + 4) * kAPitch + 16 * m + 4 * p));
-        const i16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bn, acc[m], 0, 0, 0);
+        if (RG == 8) {
+          const i16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sa + (jb + 4) * kAPitch + 16 * m + 4 * p));
+          const i16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                           __builtin_bit_cast(bf16x8, bcur[u]), acc[m], 0, 0, 0);
+        } else {
+          const i16x4 bn = __builtin_bit_cast(i16x4, make_uint2(bcur[u].x, bcur[u].y));
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, bn, acc[m], 0, 0, 0);
+        }
       }
     }
     // decode the block and form Wm = bf16(Wbf + s * t) into this wave's
@@ -203,7 +225,9 @@ hipError_t launch_merge(const uint8_t* codes, const uint8_t* q8, const float* s2
                         const uint16_t* B, int r, float s, uint16_t* out, hipStream_t st) {
   const dim3 grid((K + kTileK - 1) / kTileK, (N + kRowsPerWg - 1) / kRowsPerWg);
   const uint4* cw = reinterpret_cast<const uint4*>(codes);
-  if (r <= 32)
+  if (r <= 16)
+    hipLaunchKernelGGL(k_merge<16>, grid, dim3(256), 0, st, cw, q8, s2, N, K, A, B, r, s, out, nf4_consts());
+  else if (r <= 32)
     hipLaunchKernelGGL(k_merge<32>, grid, dim3(256), 0, st, cw, q8, s2, N, K, A, B, r, s, out, nf4_consts());
   else
     hipLaunchKernelGGL(k_merge<64>, grid, dim3(256), 0, st, cw, q8, s2, N, K, A, B, r, s, out, nf4_consts());
