@@ -30,6 +30,9 @@ hipError_t launch_merge(const uint8_t* codes, const uint8_t* q8, const float* s2
 hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_dx(const GemmArgs& a, hipStream_t st);
 void time_next_gemm(hipEvent_t start, hipEvent_t stop);
+hipError_t launch_lora_down_partials(const uint16_t* X, int M, int K, const uint16_t* A, int r, float* part,
+                                     DropMask drop, bool f16, hipStream_t st);
+int rowdot_nsplit(int64_t M, int64_t Kd, int r);
 hipError_t launch_lora_down(const uint16_t* X, int M, int K, const uint16_t* A, int r, float s, uint16_t* U,
                             float* part, DropMask drop, bool f16, hipStream_t st);
 size_t rowdot_part_bytes(int64_t M, int64_t Kd, int r);
@@ -242,10 +245,10 @@ size_t qlora_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, int
     if (M == 0) return 0;
     const int cus = qlora::device_compute_units();
     if (M <= qlora::skinny_max_tokens()) {
-      // few tokens: [U~][U~ partials | split partials of the main product]
+      // few tokens: [U~][U~ partials][split partials of the main product]
       const size_t u = r > 0 ? round_up((size_t)M * r * 2) : 0;
       const size_t upart = r > 0 ? round_up(qlora::rowdot_part_bytes(M, k_in, r)) : 0;
-      return u + std::max(upart, round_up(qlora::skinny_part_bytes(M, n_out, k_in, cus)));
+      return u + upart + round_up(qlora::skinny_part_bytes(M, n_out, k_in, cus));
     }
     // [fragment-tiled X][U~ partials of the row pass][split tiles of the main product]
     const size_t xt = round_up(qlora::tiled_bytes(M, k_in));
@@ -338,32 +341,40 @@ static int linear_fwd_impl(const qlora_nf4_weight* w, const uint16_t* X, int64_t
     // Workspace: [U~ when U_out is NULL][U~ partials, later the split
     // partials of the main product (optional)].
     const size_t ubytes = r > 0 && !U_out ? round_up((size_t)M * r * 2) : 0;
-    const size_t pbytes = r > 0 ? qlora::rowdot_part_bytes(M, w->k_in, r) : 0;
+    const size_t pbytes = r > 0 ? round_up(qlora::rowdot_part_bytes(M, w->k_in, r)) : 0;
     if (ubytes + pbytes > 0) {
       if (!ws || ws_bytes < ubytes + pbytes) return fail(QLORA_ERR_WORKSPACE, "forward workspace too small");
       if (!aligned16(ws)) return fail(QLORA_ERR_ALIGN, "workspace must be 16-byte aligned");
     }
+    qlora::SkinnyArgs k{};
     uint16_t* U = nullptr;
     if (r > 0) {
       U = U_out ? U_out : reinterpret_cast<uint16_t*>(base);
       if (w->k_in > 0) {
-        float* part = pbytes ? reinterpret_cast<float*>(base + ubytes) : nullptr;
-        e = qlora::launch_lora_down(X, (int)M, (int)w->k_in, A, r, s, U, part, dm, f16, stream);
+        // the down projection's split partials; the few-token kernel adds
+        // them (and stores U~ to U_out)
+        float* part = reinterpret_cast<float*>(base + ubytes);
+        e = qlora::launch_lora_down_partials(X, (int)M, (int)w->k_in, A, r, part, dm, f16, stream);
         if (e != hipSuccess) return hip_fail(e, "lora_down launch");
+        k.upart = part;
+        k.uns = qlora::rowdot_nsplit(M, w->k_in, r);
+        k.uscale = s;
+        k.Uout = U_out;
       } else if ((e = qlora::launch_zero_u16(U, M * r, stream)) != hipSuccess) {
         return hip_fail(e, "zero U");
       }
     }
-    qlora::SkinnyArgs k{};
     k.X = X; k.codes = w->codes; k.q8 = w->absmax_q8; k.s2 = w->absmax_scale;
     k.U = U; k.B = B; k.Y = Y;
     k.M = (int)M; k.N = (int)w->n_out; k.K = (int)w->k_in; k.r = r;
     k.nf4 = qlora::nf4_consts();
     k.f16 = f16;
-    // without room for the split partials the kernel runs unsplit
+    // the split partials of the main product go after the U~ partials (the
+    // kernel reads those while it writes these); without room the kernel
+    // runs unsplit
     const size_t kbytes = qlora::skinny_part_bytes(M, w->n_out, w->k_in, cus);
-    if (kbytes && ws && aligned16(ws) && ws_bytes >= ubytes + kbytes)
-      k.part = reinterpret_cast<float*>(base + ubytes);
+    if (kbytes && ws && aligned16(ws) && ws_bytes >= ubytes + pbytes + kbytes)
+      k.part = reinterpret_cast<float*>(base + ubytes + pbytes);
     e = qlora::launch_skinny_fwd(k, stream);
     return e == hipSuccess ? QLORA_OK : hip_fail(e, "few-token forward launch");
   }

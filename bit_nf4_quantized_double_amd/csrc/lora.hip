@@ -7,7 +7,8 @@
 //
 // v_mfma_f32_16x16x32 on 16-bit elements (bf16, or fp16 for the fp16
 // instance) with the rank on the 16-wide side; split partial sums over k are
-// added in a fixed order by a second pass (deterministic).
+// added in a fixed order (deterministic) by a second pass, or by the
+// few-token kernel, which stages them in LDS and adds them the same way.
 #include <algorithm>
 
 #include "common.h"
@@ -16,22 +17,30 @@
 namespace qlora {
 
 // K split of the rowdot kernel: enough (row block, split) workgroups to fill
-// the GPU (>= 512), splits of whole 256-wide sub-chunks.
-void rowdot_split(int M, int Kd, int* nsplit, int* kchunk) {
+// the GPU (>= 512), splits of whole 256-wide sub-chunks -- but no more
+// partial sums than fit in 32 KB at a rank pitch of 8 (the few-token kernel
+// stages them in LDS and adds them itself).
+void rowdot_split(int M, int Kd, int r, int* nsplit, int* kchunk) {
   const int rb = (M + 63) / 64;
   const int nsub = std::max(1, (Kd + 255) / 256);
-  int ns = std::min(nsub, std::max(1, (512 + rb - 1) / rb));
+  const int cap = std::max(1, (32 << 10) / (std::max(M, 1) * std::max((r + 7) & ~7, 8) * 4));
+  int ns = std::min({nsub, std::max(1, (512 + rb - 1) / rb), cap});
   const int per = (nsub + ns - 1) / ns;
   ns = (nsub + per - 1) / per;
   *nsplit = ns;
   *kchunk = per * 256;
 }
 
-// fp32 partial bytes the rowdot kernel needs for these sizes (0 if unsplit).
-size_t rowdot_part_bytes(int64_t M, int64_t Kd, int r) {
+int rowdot_nsplit(int64_t M, int64_t Kd, int r) {
   int ns, kc;
-  rowdot_split((int)M, (int)Kd, &ns, &kc);
-  return ns > 1 ? (size_t)ns * (size_t)M * (size_t)r * 4u : 0;
+  rowdot_split((int)M, (int)Kd, r, &ns, &kc);
+  return ns;
+}
+
+// fp32 partial bytes of the rowdot kernel for these sizes (one [M x r] sum
+// per split, also when there is one split).
+size_t rowdot_part_bytes(int64_t M, int64_t Kd, int r) {
+  return (size_t)rowdot_nsplit(M, Kd, r) * (size_t)M * (size_t)r * 4u;
 }
 
 namespace {
@@ -187,13 +196,15 @@ __global__ __launch_bounds__(256) void k_rowdot(RowdotArgs ra) {
   rowdot_body<CONTIG, RT, E>(ra, blockIdx.x, blockIdx.y, sw);
 }
 
-// out[m][j] = bf16(scale * sum_{split} part[split][m][j]), fixed order.
+// out[m][j] = bf16(scale * sum_{split} part[split][m][j]): split 0's value,
+// then the others added in split order (the few-token kernel adds its staged
+// copy of the partials the same way).
 template <typename E>
 __device__ __forceinline__ void rowdot_finalize_body(const float* __restrict__ part, int nsplit, int64_t n,
                                                      float scale, uint16_t* __restrict__ out, int b, int nb) {
   for (int64_t i = (int64_t)b * 256 + threadIdx.x; i < n; i += (int64_t)nb * 256) {
-    float s = 0.f;
-    int k = 0;
+    float s = part[i];
+    int k = 1;
     for (; k + 8 <= nsplit; k += 8) {  // 8 loads in flight, added in split order
       float v[8];
 #pragma unroll
@@ -213,36 +224,6 @@ __global__ __launch_bounds__(256) void k_rowdot_finalize(const float* __restrict
   rowdot_finalize_body<E>(part, nsplit, n, scale, out, blockIdx.x, gridDim.x);
 }
 
-// The same sum for few outputs and many splits: 8 lanes per output, lane t
-// adding splits t, t + 8, t + 16, ... in order, then the 8 sums combined in a
-// fixed butterfly; lane t == 0 stores.  A handful of memory latencies
-// instead of nsplit / 8 of them.
-template <typename E>
-__global__ __launch_bounds__(256) void k_rowdot_finalize8(const float* __restrict__ part, int nsplit, int64_t n,
-                                                          float scale, uint16_t* __restrict__ out) {
-  const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t i = gi >> 3;
-  const int t = (int)(gi & 7);
-  const bool ok = i < n;
-  float s = 0.f;
-  int k = t;
-  for (; k + 56 < nsplit; k += 64) {  // 8 loads in flight
-    float v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = ok ? part[(int64_t)(k + 8 * j) * n + i] : 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) s += v[j];
-  }
-  for (; k < nsplit; k += 8) s += ok ? part[(int64_t)k * n + i] : 0.f;
-  s += __shfl_xor(s, 1);
-  s += __shfl_xor(s, 2);
-  s += __shfl_xor(s, 4);
-  if (ok && t == 0) {
-    const uint32_t pk = E::pack2(scale * s, 0.f);
-    out[i] = (uint16_t)(pk & 0xFFFFu);
-  }
-}
-
 __global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_t n) {
   for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
 }
@@ -258,13 +239,15 @@ void rowdot_launch(dim3 grid, hipStream_t st, const uint16_t* in, int M, int Kd,
   hipLaunchKernelGGL((k_rowdot<CONTIG, RT, E>), grid, dim3(256), 0, st, ra);
 }
 
+// keep_part: write the fp32 partial sums (also for one split) and stop
+// there; otherwise round them into out (a finalize pass when split).
 template <bool CONTIG, typename E>
 hipError_t rowdot_dispatch(const uint16_t* in, int M, int Kd, const uint16_t* wt, int r, float scale,
-                           uint16_t* out, float* part, DropMask drop, hipStream_t st) {
+                           uint16_t* out, float* part, DropMask drop, bool keep_part, hipStream_t st) {
   int nsplit, kchunk;
-  rowdot_split(M, Kd, &nsplit, &kchunk);
+  rowdot_split(M, Kd, r, &nsplit, &kchunk);
   dim3 grid((M + 63) / 64, nsplit);
-  float* p = nsplit > 1 ? part : nullptr;
+  float* p = nsplit > 1 || keep_part ? part : nullptr;
   switch ((r + 15) / 16) {
     case 1: rowdot_launch<CONTIG, 1, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
     case 2: rowdot_launch<CONTIG, 2, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
@@ -272,13 +255,8 @@ hipError_t rowdot_dispatch(const uint16_t* in, int M, int Kd, const uint16_t* wt
     default: rowdot_launch<CONTIG, 4, E>(grid, st, in, M, Kd, wt, r, kchunk, scale, out, p, drop); break;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nsplit == 1) return e;
+  if (e != hipSuccess || keep_part || nsplit == 1) return e;
   const int64_t n = (int64_t)M * r;
-  if (n <= 4096 && nsplit >= 16) {
-    hipLaunchKernelGGL(k_rowdot_finalize8<E>, dim3((int)((8 * n + 255) / 256)), dim3(256), 0, st, part, nsplit, n,
-                       scale, out);
-    return hipGetLastError();
-  }
   const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 2048));
   hipLaunchKernelGGL(k_rowdot_finalize<E>, dim3(blocks), dim3(256), 0, st, part, nsplit, n, scale, out);
   return hipGetLastError();
@@ -286,12 +264,31 @@ hipError_t rowdot_dispatch(const uint16_t* in, int M, int Kd, const uint16_t* wt
 
 }  // namespace
 
+// U~ = E(s sum over splits of part) for rowdot's nsplit partials [nsplit][M][r].
+hipError_t launch_rowdot_finalize(const float* part, int nsplit, int M, int r, float s, uint16_t* U, bool f16,
+                                  hipStream_t st) {
+  const int64_t n = (int64_t)M * r;
+  if (n <= 0) return hipSuccess;
+  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 2048));
+  if (f16) hipLaunchKernelGGL(k_rowdot_finalize<F16>, dim3(blocks), dim3(256), 0, st, part, nsplit, n, s, U);
+  else hipLaunchKernelGGL(k_rowdot_finalize<Bf16>, dim3(blocks), dim3(256), 0, st, part, nsplit, n, s, U);
+  return hipGetLastError();
+}
+
+// The split partial sums of (mask * X) A^T alone, [rowdot_nsplit][M][r] fp32,
+// for a consumer that adds them itself.
+hipError_t launch_lora_down_partials(const uint16_t* X, int M, int K, const uint16_t* A, int r, float* part,
+                                     DropMask drop, bool f16, hipStream_t st) {
+  return f16 ? rowdot_dispatch<true, F16>(X, M, K, A, r, 1.f, nullptr, part, drop, true, st)
+             : rowdot_dispatch<true, Bf16>(X, M, K, A, r, 1.f, nullptr, part, drop, true, st);
+}
+
 // U~ = E(s (mask * X) A^T): in = X [M x K], A [r x K]; E = fp16 when f16,
 // else bf16.  part: fp32 split partials (rowdot_part_bytes).
 hipError_t launch_lora_down(const uint16_t* X, int M, int K, const uint16_t* A, int r, float s, uint16_t* U,
                             float* part, DropMask drop, bool f16, hipStream_t st) {
-  return f16 ? rowdot_dispatch<true, F16>(X, M, K, A, r, s, U, part, drop, st)
-             : rowdot_dispatch<true, Bf16>(X, M, K, A, r, s, U, part, drop, st);
+  return f16 ? rowdot_dispatch<true, F16>(X, M, K, A, r, s, U, part, drop, false, st)
+             : rowdot_dispatch<true, Bf16>(X, M, K, A, r, s, U, part, drop, false, st);
 }
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {

@@ -36,12 +36,16 @@ namespace qlora {
 void take_gemm_events(hipEvent_t& start, hipEvent_t& stop);  // gemm.hip
 hipError_t launch_splitk_reduce(const float* part, int ksplit, int M, int C, uint16_t* out, int64_t ld_out, bool f16,
                                 hipStream_t st);  // gemm.hip
+hipError_t launch_rowdot_finalize(const float* part, int nsplit, int M, int r, float s, uint16_t* U, bool f16,
+                                  hipStream_t st);  // lora.hip
 
 namespace {
 
 constexpr int kSkWaves = 8;
 constexpr int kSkThreads = 64 * kSkWaves;
 constexpr int kSkMaxStageLoads = 8;  // 16-byte staged-scale loads per thread: sbytes <= 60 KB
+constexpr int kSkUpLoads = 4;        // 16-byte staged U~-partial loads per thread: <= 32 KB
+constexpr int kSkUpBytes = kSkUpLoads * 16 * kSkThreads;
 
 struct SkSeg {
   uint4 code;  // 32 codes
@@ -98,6 +102,49 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
   const uint32_t g_first = (qbase + (uint32_t)blk0) >> 8;
   const uint8_t* const s_q8 = reinterpret_cast<const uint8_t*>(s_dyn);
   const float* const s_s2 = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(s_dyn) + R * qp);
+
+  // U~ partials [uns][M][rp] (rp = r rounded up to 8, ranks past r zero) ->
+  // LDS, for the workgroups that add the adapter term; requested here,
+  // stored with the staged scales
+  const bool ustage = a.upart != nullptr && a.r > 0 && kz == 0;
+  const int urp = (a.r + 7) & ~7;
+  float* const s_up = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(s_dyn) + a.uoff);
+  const uint32_t un = ustage ? (uint32_t)(a.uns * a.M * urp) : 0u;  // floats staged, <= kSkUpBytes / 4
+  const bool uvec = (a.r & 7) == 0;  // then the LDS copy is the global array
+  uint4 upv[kSkUpLoads];
+  float ups[4 * kSkUpLoads];
+  if (ustage) {
+    if (uvec) {
+#pragma unroll
+      for (int u = 0; u < kSkUpLoads; ++u) {
+        const uint32_t i = (uint32_t)tid + (uint32_t)u * kSkThreads;
+        upv[u] = i < un / 4 ? *reinterpret_cast<const uint4*>(a.upart + 4 * i) : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4 * kSkUpLoads; ++u) {
+        const uint32_t i = (uint32_t)tid + (uint32_t)u * kSkThreads;
+        const uint32_t zm = i / (uint32_t)urp, j = i - zm * (uint32_t)urp;
+        ups[u] = i < un && j < (uint32_t)a.r ? a.upart[zm * (uint32_t)a.r + j] : 0.f;
+      }
+    }
+  }
+  auto store_up = [&]() {
+    if (!ustage) return;
+    if (uvec) {
+#pragma unroll
+      for (int u = 0; u < kSkUpLoads; ++u) {
+        const uint32_t i = (uint32_t)tid + (uint32_t)u * kSkThreads;
+        if (i < un / 4) *reinterpret_cast<uint4*>(s_up + 4 * i) = upv[u];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4 * kSkUpLoads; ++u) {
+        const uint32_t i = (uint32_t)tid + (uint32_t)u * kSkThreads;
+        if (i < un) s_up[i] = ups[u];
+      }
+    }
+  };
   if (SL) {
     uint8_t* q8w = reinterpret_cast<uint8_t*>(s_dyn);
     float* s2w = reinterpret_cast<float*>(q8w + R * qp);
@@ -157,6 +204,10 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
       }
     }
     if ((uint32_t)tid < ngs) s2w[tid] = sv;
+    store_up();
+    __syncthreads();
+  } else if (ustage) {
+    store_up();
     __syncthreads();
   }
   // block scale a' = fp32(q8 * s2) of tile t, chunk c for this lane; chunks
@@ -277,7 +328,31 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
     for (int j0 = 0; j0 < a.r; j0 += 32) {
       const int j = j0 + 8 * g;
       uint4 uf = make_uint4(0, 0, 0, 0);
-      if (row < a.M && j < a.r) {
+      if (row < a.M && j < a.r && ustage) {
+        // U~[row][j .. j + 7] = E(uscale * (p0 + p1 + ...)) from the staged
+        // partials, split 0 first then the others in order (as the finalize
+        // pass of the down projection adds them)
+        f32x4 lo = *reinterpret_cast<const f32x4*>(s_up + row * urp + j);
+        f32x4 hi = *reinterpret_cast<const f32x4*>(s_up + row * urp + j + 4);
+        for (int z = 1; z < a.uns; ++z) {
+          lo += *reinterpret_cast<const f32x4*>(s_up + (z * a.M + row) * urp + j);
+          hi += *reinterpret_cast<const f32x4*>(s_up + (z * a.M + row) * urp + j + 4);
+        }
+        const float c = a.uscale;
+        uf = make_uint4(E::pack2(c * lo[0], c * lo[1]), E::pack2(c * lo[2], c * lo[3]), E::pack2(c * hi[0], c * hi[1]),
+                        E::pack2(c * hi[2], c * hi[3]));
+        if (a.Uout && blockIdx.x == 0 && wa == 0) {
+          uint16_t* o = a.Uout + (int64_t)row * a.r + j;
+          if (vec) {
+            *reinterpret_cast<uint4*>(o) = uf;
+          } else {
+            const uint32_t w[4] = {uf.x, uf.y, uf.z, uf.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (j + e < a.r) o[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      } else if (row < a.M && j < a.r) {
         const uint16_t* p = a.U + (int64_t)row * a.r + j;
         if (vec) {
           uf = *reinterpret_cast<const uint4*>(p);
@@ -434,7 +509,25 @@ hipError_t launch_skinny_fwd(SkinnyArgs a, hipStream_t st) {
   // within the default 64 KB of dynamic LDS (so the whole-row copy takes at
   // most kSkMaxStageLoads 16-byte pieces per thread), one thread per s2 group
   const bool sl = a.K >= 64 && sbytes <= 60 * 1024 && ngs <= (size_t)kSkThreads;
-  const size_t lds = std::max(red, sl ? sbytes : (size_t)0);
+  size_t lds = std::max(red, sl ? sbytes : (size_t)0);
+  if (a.upart) {
+    // the U~ partials go after the staged scales; when they do not fit, a
+    // finalize pass rounds them into U first
+    const size_t ubytes = (size_t)a.uns * (size_t)a.M * (size_t)((a.r + 7) & ~7) * 4u;
+    const size_t uoff = sl ? (sbytes + 15) & ~(size_t)15 : 0;
+    if (a.r <= 0 || ubytes > (size_t)kSkUpBytes || uoff + ubytes > 64 * 1024) {
+      if (a.r > 0) {
+        if (!a.U) return hipErrorInvalidValue;
+        // U is then the caller's U~ buffer (U_out or workspace), writable
+        hipError_t e = launch_rowdot_finalize(a.upart, a.uns, a.M, a.r, a.uscale, const_cast<uint16_t*>(a.U), a.f16, st);
+        if (e != hipSuccess) return e;
+      }
+      a.upart = nullptr;
+    } else {
+      a.uoff = (int)uoff;
+      lds = std::max(lds, uoff + ubytes);
+    }
+  }
   switch (tpw * 16 + rd) {
     case 1 * 16 + 1: return sk_launch<1, 1>(a, grid, lds, sl, st);
     case 1 * 16 + 2: return sk_launch<1, 2>(a, grid, lds, sl, st);

@@ -10,7 +10,16 @@ struct SkinnyArgs {
   const uint8_t* codes;
   const uint8_t* q8;
   const float* s2;
-  const uint16_t* U;  // [M x r] bf16 scaled adapter activation, or null (r == 0)
+  const uint16_t* U;  // [M x r] bf16 scaled adapter activation, or null (r == 0 or upart set)
+  // U~ from the down projection's fp32 split partial sums instead of U (when
+  // set): U~ = E(uscale * (upart[0] + upart[1] + ... + upart[uns - 1])),
+  // each [M x r]; the partials are staged in LDS at the kernel's start.  The
+  // workgroup of tile group 0 stores U~ to Uout when that is set.
+  const float* upart;
+  int uns;
+  float uscale;
+  uint16_t* Uout;
+  int uoff;           // LDS byte offset of the staged partials; set by the launcher
   const uint16_t* B;  // [N x r] bf16, or null (r == 0)
   uint16_t* Y;        // [M x N] bf16, written
   int M, N, K, r;
@@ -33,6 +42,8 @@ struct SkinnySplit {
 SkinnySplit skinny_split(int64_t M, int64_t N, int64_t K, int cus);
 // fp32 bytes the split's partial sums take (0 if unsplit)
 size_t skinny_part_bytes(int64_t M, int64_t N, int64_t K, int cus);
+// With upart set and the partials too large to stage, the launcher first
+// rounds them into U (which must then be set) with a finalize pass.
 hipError_t launch_skinny_fwd(SkinnyArgs a, hipStream_t st);
 
 }  // namespace qlora
