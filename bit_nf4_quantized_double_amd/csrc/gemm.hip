@@ -23,8 +23,10 @@
 //   NT (forward): W tile = 128 rows n x 64 k, stored [n][k], read with
 //                 ds_read_b128.
 //   NN (dX):      W tile = 64 rows n x 128 columns c, stored [n][c] as
-//                 decoded; the B operand needs 8 consecutive n per lane and
-//                 gets them with gfx950's transposing ds_read_b64_tr_b16.
+//                 decoded (each group of 8 columns in the order 0, 2, 4, 6,
+//                 1, 3, 5, 7, which the epilogue undoes); the B operand
+//                 needs 8 consecutive n per lane and gets them with gfx950's
+//                 transposing ds_read_b64_tr_b16.
 // Rows of 64 bf16 (128 B) keep their 16-byte chunks XOR-swizzled by swz(row)
 // so row-consecutive operand reads are bank-conflict-free.
 //
@@ -160,8 +162,7 @@ __device__ __forceinline__ CodeSeg load_codes(const GemmArgs& a, const Srcs& src
 // covers, and the lookup masks.
 struct DecodeConsts {
   float th[8];
-  LaneMask lm;   // NN lookup (byte-spread order)
-  EoConsts eo;   // NT lookup (element order)
+  EoConsts eo;
 };
 
 template <bool NN>
@@ -171,17 +172,16 @@ __device__ __forceinline__ DecodeConsts decode_consts(const Nf4Consts& nf4, int 
   seg_of<NN>(tid, row, half);
   const bool odd = NN ? (half & 1) : half;  // the lane building levels 8..15
   lane_levels(nf4, odd, dc.th);
-  dc.lm = lane_mask(odd);
-  dc.eo = eo_consts();
+  dc.eo = eo_consts(NN && odd);  // NN (kXor1 tables): that lane's own half is "a"
   return dc;
 }
 
-// Decode 32 weights and store them in the W tile.  NT: the element-order
-// lookup (16 permutes + 7 operations per 8 codes) leaves each group of 8
-// reduction columns in the order 0, 2, 4, 6, 1, 3, 5, 7 -- the tiled X copy
-// the forward reads carries the same order, so the products pair up.  NN:
-// the byte-spread lookup keeps the natural column order (the output
-// columns).
+// Decode 32 weights and store them in the W tile with the element-order
+// lookup (16 permutes + 7 operations per 8 codes), which leaves each group
+// of 8 columns in the order 0, 2, 4, 6, 1, 3, 5, 7.  NT: those are reduction
+// columns, and the tiled X copy the forward reads carries the same order, so
+// the products pair up.  NN: they are output columns; the epilogue (and the
+// adapter operand, and the dropout mask) use the same order (eo_col).
 template <bool NN, typename E>
 __device__ __forceinline__ void decode_store(uint16_t* s, const CodeSeg& cs, const DecodeConsts& dc, int tid) {
   int row, half;
@@ -190,10 +190,10 @@ __device__ __forceinline__ void decode_store(uint16_t* s, const CodeSeg& cs, con
   if (NN) {
     const Lut L = build_lut<LutPartner::kXor1, E>(dc.th, scale);
     const int c = half * 32;
-    *reinterpret_cast<uint4*>(s + nn_off(row, c + 0)) = decode8_lut(L, cs.code.x, dc.lm);
-    *reinterpret_cast<uint4*>(s + nn_off(row, c + 8)) = decode8_lut(L, cs.code.y, dc.lm);
-    *reinterpret_cast<uint4*>(s + nn_off(row, c + 16)) = decode8_lut(L, cs.code.z, dc.lm);
-    *reinterpret_cast<uint4*>(s + nn_off(row, c + 24)) = decode8_lut(L, cs.code.w, dc.lm);
+    *reinterpret_cast<uint4*>(s + nn_off(row, c + 0)) = decode8_lut_hl(L, cs.code.x, dc.eo);
+    *reinterpret_cast<uint4*>(s + nn_off(row, c + 8)) = decode8_lut_hl(L, cs.code.y, dc.eo);
+    *reinterpret_cast<uint4*>(s + nn_off(row, c + 16)) = decode8_lut_hl(L, cs.code.z, dc.eo);
+    *reinterpret_cast<uint4*>(s + nn_off(row, c + 24)) = decode8_lut_hl(L, cs.code.w, dc.eo);
   } else {
     const Lut L = build_lut<LutPartner::kRows16, E>(dc.th, scale);
     const int c = half * 4;
@@ -203,6 +203,10 @@ __device__ __forceinline__ void decode_store(uint16_t* s, const CodeSeg& cs, con
     *reinterpret_cast<uint4*>(s + kt_off(row, c + 3)) = decode8_lut_hl(L, cs.code.w, dc.eo);
   }
 }
+
+// Output column held at NN tile column p (group of 8 in the decode's element
+// order 0, 2, 4, 6, 1, 3, 5, 7).
+__device__ __forceinline__ int eo_col(int p) { return (p & ~7) | ((p & 3) << 1) | ((p >> 2) & 1); }
 
 // B operand for MFMA sub-step ks, columns col0..col0+31.
 template <bool NN>
@@ -463,7 +467,7 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
       for (int u = 0; u < 4; ++u) {
         const int idx = ptid + u * kThreads;
         if (!NN) *reinterpret_cast<uint4*>(s_ad + kt_off(idx >> 3, idx & 7)) = wv[u];
-        else *reinterpret_cast<uint4*>(s_ad + nn_off(idx >> 4, 8 * (idx & 15))) = wv[u];
+        else *reinterpret_cast<uint4*>(s_ad + nn_off(idx >> 4, 8 * (idx & 15))) = x_order_even_odd(wv[u]);
       }
     }
     if (drop_first) {
@@ -563,7 +567,7 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
               const int rl = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), cl = 32 * j + (lane & 31);
-              if (!keep[rl * 128 + cl]) acc[i][j][v] = 0.f;
+              if (!keep[rl * 128 + eo_col(cl)]) acc[i][j][v] = 0.f;
             }
         step_barrier();  // mask read: producers may decode into W buffers 2-3
       }
@@ -627,7 +631,8 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int col = c0 + 32 * j + (lane & 31);
+          const int cl = 32 * j + (lane & 31);
+          const int col = c0 + (NN ? eo_col(cl) : cl);
           if (col >= a.C) continue;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
@@ -653,7 +658,7 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int col = 32 * j + (lane & 31);
+        const int col = NN ? eo_col(32 * j + (lane & 31)) : 32 * j + (lane & 31);
 #pragma unroll
         for (int v = 0; v < 16; v += 2) {
           const int rl = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);

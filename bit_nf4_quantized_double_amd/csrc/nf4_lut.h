@@ -121,15 +121,19 @@ __device__ __forceinline__ uint4 decode8_lut(const Lut& L, uint32_t d, const Lan
 // operand must carry the same order (x_order_even_odd).
 
 // Constants of the element-order lookup, held in VGPRs so that each
-// (x & m) | c folds into one v_and_or_b32 (one scalar operand at most).
+// (x & m) ^ c folds into one VALU operation (one scalar operand at most).
+// `base` selects table "a" for codes 0..7: 0x03020100 with kRows16 tables
+// (and with kXor1 tables on the lane that built levels 0..7); the kXor1 lane
+// that built levels 8..15 holds them in "a" and takes base 0x07060504, which
+// swaps the pick.
 struct EoConsts {
   uint32_t m7;    // 0x07070707
   uint32_t m4;    // 0x04040404
-  uint32_t base;  // 0x03020100
+  uint32_t base;  // 0x03020100, or 0x07060504 (see above)
 };
 
-__device__ __forceinline__ EoConsts eo_consts() {
-  EoConsts k{0x07070707u, 0x04040404u, 0x03020100u};
+__device__ __forceinline__ EoConsts eo_consts(bool swap_ab = false) {
+  EoConsts k{0x07070707u, 0x04040404u, swap_ab ? 0x07060504u : 0x03020100u};
   asm volatile("" : "+v"(k.m7), "+v"(k.m4), "+v"(k.base));
   return k;
 }
@@ -148,13 +152,14 @@ __device__ __forceinline__ void lookup4_eo(const Lut& L, uint32_t idx, uint32_t 
 
 // 8 codes (one dword, element 0 in the low nibble) -> 8 16-bit values in the
 // element order 0, 2, 4, 6, 1, 3, 5, 7, from kRows16 tables built with
-// lane_levels: a code c is looked up at entry c & 7 of both tables and bit 3
-// of c picks the result.  7 operations per 8 codes besides the 16 permutes.
+// lane_levels (or kXor1 tables, see EoConsts): a code c is looked up at
+// entry c & 7 of both tables and bit 3 of c picks the result.  7 operations
+// per 8 codes besides the 16 permutes.
 __device__ __forceinline__ uint4 decode8_lut_hl(const Lut& L, uint32_t d, const EoConsts& k) {
   const uint32_t ie = d & k.m7;                    // low nibbles: c & 7
   const uint32_t io = (d >> 4) & k.m7;             // high nibbles: c & 7
-  const uint32_t se = ((d >> 1) & k.m4) | k.base;  // bit 3 of the low nibble -> bit 2
-  const uint32_t so = ((d >> 5) & k.m4) | k.base;  // bit 3 of the high nibble -> bit 2
+  const uint32_t se = ((d >> 1) & k.m4) ^ k.base;  // bit 3 of the low nibble -> bit 2
+  const uint32_t so = ((d >> 5) & k.m4) ^ k.base;  // bit 3 of the high nibble -> bit 2
   uint4 o;
   lookup4_eo(L, ie, se, o.x, o.y);
   lookup4_eo(L, io, so, o.z, o.w);
