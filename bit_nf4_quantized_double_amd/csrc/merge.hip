@@ -20,8 +20,9 @@
 // holding t[n][64 g + 0 .. 63] of row n = l & 15, g = l >> 4 -- exactly one
 // 64-weight block.  The lane decodes that block's 32 bytes of codes (with
 // the block's 16 decoded values as a byte-plane table in registers, looked
-// up with v_perm_b32: no LDS reads), adds s * t and puts the 128 bytes of
-// merged weight in a wave-private LDS tile,
+// up with v_perm_b32: no LDS reads; the element-order lookup, whose order
+// the pairing with t follows), adds s * t and puts the 128 bytes of merged
+// weight in a wave-private LDS tile,
 // which the wave reads back row by row so every store instruction writes two
 // contiguous 512-byte rows (16-byte pieces of 64 separate rows per store ran
 // at half the speed).  The M-operand comes from the LDS copy of A through
@@ -64,8 +65,8 @@ __device__ __forceinline__ uint4 load8(const uint16_t* p, int valid, bool ok, bo
 }
 
 // The lane's block table, all 16 entries bf16(level[c] * a), as the two
-// byte-plane halves decode8_lut reads ("a" = levels 0..7, "b" = 8..15): a
-// lane here decodes a whole block, so it builds the whole table itself.
+// byte-plane halves decode8_lut_hl reads ("a" = levels 0..7, "b" = 8..15):
+// a lane here decodes a whole block, so it builds the whole table itself.
 __device__ __forceinline__ Lut block_lut(const Nf4Consts& c, float a) {
   uint32_t p[8];
 #pragma unroll
@@ -188,18 +189,23 @@ __global__ __launch_bounds__(256) void k_merge(const uint4* __restrict__ codes, 
     uint16_t* sw = so + wave * (kWaveRows * kOPitch);
     const uint32_t cwd[8] = {cc0.x, cc0.y, cc0.z, cc0.w, cc1.x, cc1.y, cc1.z, cc1.w};
     const Lut L = block_lut(c, scc);
-    const LaneMask lm = lane_mask(false);
+    const EoConsts ek = eo_consts();
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
-      const uint4 wb = decode8_lut(L, cwd[d], lm);  // weights 8 d .. 8 d + 7 = tiles 2 d, 2 d + 1
-      const uint32_t wv[4] = {wb.x, wb.y, wb.z, wb.w};
+      // weights 8 d .. 8 d + 7 (tiles 2 d, 2 d + 1), decoded in the element
+      // order 0, 2, 4, 6, 1, 3, 5, 7: wb = {w0 w2, w4 w6, w1 w3, w5 w7}
+      const uint4 wb = decode8_lut_hl(L, cwd[d], ek);
+      float w[8];
+      w[0] = bf16_to_f32((uint16_t)(wb.x & 0xFFFFu)); w[2] = bf16_to_f32((uint16_t)(wb.x >> 16));
+      w[4] = bf16_to_f32((uint16_t)(wb.y & 0xFFFFu)); w[6] = bf16_to_f32((uint16_t)(wb.y >> 16));
+      w[1] = bf16_to_f32((uint16_t)(wb.z & 0xFFFFu)); w[3] = bf16_to_f32((uint16_t)(wb.z >> 16));
+      w[5] = bf16_to_f32((uint16_t)(wb.w & 0xFFFFu)); w[7] = bf16_to_f32((uint16_t)(wb.w >> 16));
       uint32_t o[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const f32x4& t = acc[2 * d + (i >> 1)];
-        const float w0 = bf16_to_f32((uint16_t)(wv[i] & 0xFFFFu)), w1 = bf16_to_f32((uint16_t)(wv[i] >> 16));
         // w + s * t with one rounding (fused multiply-add), then bf16 RNE
-        o[i] = pack_bf16x2(__builtin_fmaf(s, t[2 * (i & 1)], w0), __builtin_fmaf(s, t[2 * (i & 1) + 1], w1));
+        o[i] = pack_bf16x2(__builtin_fmaf(s, t[2 * (i & 1)], w[2 * i]), __builtin_fmaf(s, t[2 * (i & 1) + 1], w[2 * i + 1]));
       }
       *reinterpret_cast<uint4*>(sw + row * kOPitch + kl + 8 * d) = make_uint4(o[0], o[1], o[2], o[3]);
     }
