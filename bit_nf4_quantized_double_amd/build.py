@@ -18,6 +18,9 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqlora.so")
+# The same sources with every raw global access range checked (skipped and
+# counted when outside its buffer; qlora_debug_oob_count reads the count).
+LIB_CHECKED = os.path.join(PKG, "libqlora_checked.so")
 SOURCES = ["nf4_table.cpp", "codec.hip", "gemm.hip", "skinny.hip", "lora.hip", "adapter.hip", "merge.hip", "abi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -36,8 +39,10 @@ FLAGS = [
 CONTRACT = {"codec.hip": "-ffp-contract=off", "merge.hip": "-ffp-contract=off"}
 
 
-def _compile(src: str, obj: str) -> None:
+def _compile(src: str, obj: str, checked: bool = False) -> None:
     cmd = [HIPCC, *FLAGS, CONTRACT.get(src, "-ffp-contract=fast")]
+    if checked:
+        cmd.append("-DQLORA_BOUNDS_CHECK")
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -50,20 +55,26 @@ def _compile(src: str, obj: str) -> None:
 
 
 def build(verbose: bool = True) -> str:
+    """Build libqlora.so and its bounds-checked twin libqlora_checked.so."""
     if not shutil.which(HIPCC) and not os.path.exists(HIPCC):
         raise RuntimeError("hipcc not found; cannot build libqlora.so")
     with tempfile.TemporaryDirectory(prefix="qlora_build_") as tmp:
-        objs = [os.path.join(tmp, s.rsplit(".", 1)[0] + ".o") for s in SOURCES]
-        with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-            list(ex.map(_compile, SOURCES, objs))
-        out_tmp = LIB + ".tmp"
-        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp, *objs]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-        os.replace(out_tmp, LIB)
-    if verbose:
-        print(f"built {LIB}")
+        jobs = []
+        for checked, lib in ((False, LIB), (True, LIB_CHECKED)):
+            tag = "c_" if checked else ""
+            objs = [os.path.join(tmp, tag + s.rsplit(".", 1)[0] + ".o") for s in SOURCES]
+            jobs.append((lib, objs, [(s, o, checked) for s, o in zip(SOURCES, objs)]))
+        with ThreadPoolExecutor(max_workers=8) as ex:
+            list(ex.map(lambda t: _compile(*t), [t for _, _, ts in jobs for t in ts]))
+        for lib, objs, _ in jobs:
+            out_tmp = lib + ".tmp"
+            cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp, *objs]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+            os.replace(out_tmp, lib)
+            if verbose:
+                print(f"built {lib}")
     return LIB
 
 

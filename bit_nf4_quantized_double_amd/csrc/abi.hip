@@ -33,6 +33,13 @@ void time_next_gemm(hipEvent_t start, hipEvent_t stop);
 hipError_t launch_lora_down_partials(const uint16_t* X, int M, int K, const uint16_t* A, int r, float* part,
                                      DropMask drop, bool f16, hipStream_t st);
 int rowdot_nsplit(int64_t M, int64_t Kd, int r);
+// the per-source-file out-of-bounds counters of the bounds-checked build
+uint64_t oob_count_codec(bool reset);
+uint64_t oob_count_gemm(bool reset);
+uint64_t oob_count_skinny(bool reset);
+uint64_t oob_count_lora(bool reset);
+uint64_t oob_count_adapter(bool reset);
+uint64_t oob_count_merge(bool reset);
 hipError_t launch_lora_down(const uint16_t* X, int M, int K, const uint16_t* A, int r, float s, uint16_t* U,
                             float* part, DropMask drop, bool f16, hipStream_t st);
 size_t rowdot_part_bytes(int64_t M, int64_t Kd, int r);
@@ -208,6 +215,21 @@ const char* qlora_status_string(int status) {
 const char* qlora_last_error(void) { return g_last_error.c_str(); }
 
 void qlora_time_next_gemm(hipEvent_t start, hipEvent_t stop) { qlora::time_next_gemm(start, stop); }
+
+int qlora_debug_oob_count(uint64_t* count, int reset) {
+  if (!count) return fail(QLORA_ERR_INVALID_ARG, "count is NULL");
+  if (!qlora::kBoundsChecked) return fail(QLORA_ERR_INVALID_ARG, "not the bounds-checked build");
+  const bool rs = reset != 0;
+  const uint64_t c[] = {qlora::oob_count_codec(rs), qlora::oob_count_gemm(rs), qlora::oob_count_skinny(rs),
+                        qlora::oob_count_lora(rs), qlora::oob_count_adapter(rs), qlora::oob_count_merge(rs)};
+  uint64_t total = 0;
+  for (uint64_t v : c) {
+    if (v == ~(uint64_t)0) return fail(QLORA_ERR_HIP, "reading the out-of-bounds counters failed");
+    total += v;
+  }
+  *count = total;
+  return QLORA_OK;
+}
 
 void qlora_nf4_table(float out[16]) {
   if (!out) return;

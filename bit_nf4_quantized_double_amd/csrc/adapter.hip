@@ -183,7 +183,8 @@ __global__ __launch_bounds__(64 * RowpassWaves<RT2>::n) void k_rowpass(RowpassAr
 #pragma unroll
       for (int f = 0; f < 8; ++f) {
         const int kb = 8 * c + f;
-        if (kb < a.kbp)
+        if (kb < a.kbp && in_bounds(((int64_t)mb * a.kbp + kb) * 512 + 8 * lane, 8,
+                                    (int64_t)tiled_mbp(a.M) * a.kbp * 512))
           *reinterpret_cast<uint4*>(a.tiled + ((size_t)mb * a.kbp + kb) * 512 + 8 * lane) =
               a.eo ? x_order_even_odd(xf[f]) : xf[f];
       }
@@ -225,7 +226,8 @@ __global__ __launch_bounds__(64 * RowpassWaves<RT2>::n) void k_rowpass(RowpassAr
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) s += red[(w * 32 + rl) * kRP + j];
-    a.part[((size_t)z * a.M + m0 + rl) * a.rp + j] = s;
+    if (in_bounds(((int64_t)z * a.M + m0 + rl) * a.rp + j, 1, (int64_t)a.S * a.M * a.rp))
+      a.part[((size_t)z * a.M + m0 + rl) * a.rp + j] = s;
   }
 }
 
@@ -353,8 +355,8 @@ __global__ __launch_bounds__(512) void k_colpass(ColpassJob j0, ColpassJob j1, i
     float s = 0.f;
 #pragma unroll
     for (int w8 = 0; w8 < 8; ++w8) s += red[(w8 * 64 + cl) * kRP + j];
-    if (jb.trans) jb.out[(size_t)(c0 + cl) * r + j] = s;
-    else jb.out[(size_t)j * jb.C + c0 + cl] = s;
+    const int64_t oi = jb.trans ? (int64_t)(c0 + cl) * r + j : (int64_t)j * jb.C + c0 + cl;
+    if (in_bounds(oi, 1, (int64_t)jb.C * r)) jb.out[oi] = s;
   }
 }
 
@@ -367,6 +369,7 @@ __global__ __launch_bounds__(256) void k_rowpass_finalize(const float* __restric
   const int64_t n = (int64_t)M * r;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     const int m = (int)(i / r), j = (int)(i - (int64_t)m * r);
+    if (!in_bounds(((int64_t)(S - 1) * M + m) * rp + j, 1, (int64_t)S * M * rp)) continue;
     float s = 0.f;
     for (int z = 0; z < S; ++z) s += part[((int64_t)z * M + m) * rp + j];
     out[i] = (uint16_t)(E::pack2(scale * s, 0.f) & 0xFFFFu);
@@ -426,5 +429,7 @@ hipError_t launch_colpass(const uint16_t* X, int K, const uint16_t* Vt, const ui
   }
   return hipGetLastError();
 }
+
+QLORA_OOB_READER(oob_count_adapter)
 
 }  // namespace qlora

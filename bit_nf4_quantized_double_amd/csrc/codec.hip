@@ -78,7 +78,9 @@ __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ W, uint3
 #pragma unroll
     for (int j = 0; j < kChunks; ++j) {
       const int c = tid + 256 * j;
-      v[j] = (uint32_t)(c / kChunks) < nblk ? src[c] : make_uint4(0, 0, 0, 0);
+      v[j] = (uint32_t)(c / kChunks) < nblk && in_bounds((int64_t)b0 * kChunks + c, 1, (int64_t)nb * kChunks)
+                 ? src[c]
+                 : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < kChunks; ++j) {
@@ -158,12 +160,14 @@ __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ W, uint3
       }
     }
     uint4* out = reinterpret_cast<uint4*>(codes + (size_t)b * (kBlock / 2));
-    out[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    out[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    if (in_bounds(2 * (int64_t)b, 2, 2 * (int64_t)nb)) {
+      out[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+      out[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    }
   }
 
   if (!DQ) {
-    if (valid) absmax[b] = am;
+    if (valid && in_bounds(b, 1, nb)) absmax[b] = am;
     return;
   }
   // group max -> s2 = max / 255, q8 = round-half-even(absmax / s2)
@@ -180,9 +184,9 @@ __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ W, uint3
       const float t = rintf(am / step);  // round half to even
       q = (uint32_t)fminf(fmaxf(t, 0.f), 255.f);
     }
-    q8[b] = (uint8_t)q;
+    if (in_bounds(b, 1, nb)) q8[b] = (uint8_t)q;
   }
-  if (tid == 0) s2[g] = step;
+  if (tid == 0 && in_bounds(g, 1, ((int64_t)nb + kGroup - 1) / kGroup)) s2[g] = step;
 }
 
 template <bool DQ, typename E>
@@ -198,9 +202,13 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ co
   // ~4 % faster on the 70B shapes than plain stores.
   typedef __attribute__((ext_vector_type(4))) unsigned v4u;
   const uint32_t stride = gridDim.x * blockDim.x;
+  const int64_t nblk = ndw / 8, ngrp = (nblk + kGroup - 1) / kGroup;
   for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < ndw; i += stride) {
-    const uint4 o = decode8<E>(codes[i], DQ ? block_scale(q8, s2, i >> 3) : absmax[i >> 3], lv);
-    __builtin_nontemporal_store(v4u{o.x, o.y, o.z, o.w}, reinterpret_cast<v4u*>(out + i));
+    const uint32_t b = i >> 3;
+    const bool ok = in_bounds(i, 1, ndw) && in_bounds(b, 1, nblk) && (!DQ || in_bounds(b >> 8, 1, ngrp));
+    const float sc = !ok ? 0.f : DQ ? block_scale(q8, s2, b) : absmax[b];
+    const uint4 o = decode8<E>(ok ? codes[i] : 0u, sc, lv);
+    if (ok) __builtin_nontemporal_store(v4u{o.x, o.y, o.z, o.w}, reinterpret_cast<v4u*>(out + i));
   }
 }
 
@@ -249,6 +257,8 @@ hipError_t launch_dequant_fmt(const uint8_t* codes, const uint8_t* q8, const flo
   }
   return hipGetLastError();
 }
+
+QLORA_OOB_READER(oob_count_codec)
 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* q8, const float* s2, int64_t nweights,
                           uint16_t* out, bool f16, hipStream_t st) {

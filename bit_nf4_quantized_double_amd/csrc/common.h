@@ -140,6 +140,45 @@ __device__ __forceinline__ uint32_t buf_load1(__amdgpu_buffer_rsrc_t r, uint32_t
   return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
 
+// ---- bounds-checked build ---------------------------------------------------
+// Every raw global store, and every raw global load of caller-sized data
+// (buffer loads are range checked by the hardware), is guarded by
+// in_bounds(i, w, n): elements [i, i + w) of a buffer the caller sized to n
+// elements (w == 0: no access, always in bounds).  In the normal build the guard is constant true and compiles
+// away.  Built with -DQLORA_BOUNDS_CHECK (libqlora_checked.so), an access
+// outside the buffer is skipped (a load reads zeros) and counted in a device
+// counter of the translation unit, which qlora_debug_oob_count reads: a wrong
+// index shows up as a count, not as a memory fault.
+#ifdef QLORA_BOUNDS_CHECK
+constexpr bool kBoundsChecked = true;
+namespace {
+__device__ unsigned int g_oob_count;
+}  // namespace
+__device__ __forceinline__ bool in_bounds(int64_t i, int64_t w, int64_t n) {
+  if (w == 0 || (i >= 0 && w > 0 && i + w <= n)) return true;
+  __hip_atomic_fetch_add(&g_oob_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return false;
+}
+// host: this translation unit's count, cleared when `reset`
+#define QLORA_OOB_READER(fn)                                                          \
+  uint64_t fn(bool reset) {                                                           \
+    unsigned int v = 0;                                                               \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_oob_count), sizeof(v), 0, hipMemcpyDeviceToHost) != hipSuccess) \
+      return ~(uint64_t)0;                                                            \
+    if (reset) {                                                                      \
+      const unsigned int z = 0;                                                       \
+      if (hipMemcpyToSymbol(HIP_SYMBOL(g_oob_count), &z, sizeof(z), 0, hipMemcpyHostToDevice) != hipSuccess) \
+        return ~(uint64_t)0;                                                          \
+    }                                                                                 \
+    return v;                                                                         \
+  }
+#else
+constexpr bool kBoundsChecked = false;
+__device__ __forceinline__ constexpr bool in_bounds(int64_t, int64_t, int64_t) { return true; }
+#define QLORA_OOB_READER(fn) \
+  uint64_t fn(bool) { return 0; }
+#endif
+
 // 16-byte chunk swizzle inside a 64-element (128-byte) bf16 LDS row: keeps
 // ds_read_b128 / ds_write_b128 conflict-free for row-consecutive and for
 // 8-row-strided access patterns.

@@ -365,13 +365,14 @@ __device__ __forceinline__ void adapter_from_partials(const GemmArgs& a, int row
                      : make_uint4(0, 0, 0, 0);
       if (store && ok && m < a.M && a.lora_out) {
         uint16_t* o = a.lora_out + (size_t)m * (size_t)a.r + j;
+        const int64_t oi = (int64_t)m * a.r + j, on = (int64_t)a.M * a.r;
         if ((a.r & 7) == 0) {
-          *reinterpret_cast<uint4*>(o) = uf[ks][i];
+          if (in_bounds(oi, 8, on)) *reinterpret_cast<uint4*>(o) = uf[ks][i];
         } else {
           const uint32_t w[4] = {uf[ks][i].x, uf[ks][i].y, uf[ks][i].z, uf[ks][i].w};
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            if (j + e < a.r) o[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+            if (j + e < a.r && in_bounds(oi + e, 1, on)) o[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
         }
       }
     }
@@ -637,7 +638,8 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int row = row0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (row < a.M) a.part[((int64_t)kz * a.M + row) * a.C + col] = acc[i][j][v];
+            const int64_t pi = ((int64_t)kz * a.M + row) * a.C + col;
+            if (row < a.M && in_bounds(pi, 1, (int64_t)a.ksplit * a.M * a.C)) a.part[pi] = acc[i][j][v];
           }
         }
     }
@@ -673,7 +675,7 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
       const int rl = 4 * t + (lane >> 4), cl = 8 * (lane & 15);
       const uint4 v = *reinterpret_cast<const uint4*>(so + rl * kOutPitch + cl);
       const int row = row0 + rl, col = c0 + cl;
-      if (row < a.M && col < a.C)
+      if (row < a.M && col < a.C && in_bounds((int64_t)row * a.ld_out + col, 8, (int64_t)a.M * a.ld_out))
         __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(a.out + (int64_t)row * a.ld_out + col));
     }
   }
@@ -690,8 +692,9 @@ __global__ __launch_bounds__(256) void k_tile_act(const uint16_t* __restrict__ a
     const int mb = (int)(f / kbp), kb = (int)(f - (int64_t)mb * kbp);
     const int m = 32 * mb + (l & 31), k = 16 * kb + 8 * (l >> 5);
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (m < M && k < R) v = *reinterpret_cast<const uint4*>(act + (int64_t)m * R + k);
-    reinterpret_cast<uint4*>(act_t)[p] = eo ? x_order_even_odd(v) : v;
+    if (m < M && k < R && in_bounds((int64_t)m * R + k, 8, (int64_t)M * R))
+      v = *reinterpret_cast<const uint4*>(act + (int64_t)m * R + k);
+    if (in_bounds(p, 1, npieces)) reinterpret_cast<uint4*>(act_t)[p] = eo ? x_order_even_odd(v) : v;
   }
 }
 
@@ -705,6 +708,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
   const int64_t zs = (int64_t)M * C;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     const int m = (int)(i / c8), c = (int)(i - (int64_t)m * c8) * 8;
+    if (!in_bounds((int64_t)(ksplit - 1) * zs + (int64_t)m * C + c, 8, (int64_t)ksplit * zs)) continue;
     const float4* p = reinterpret_cast<const float4*>(part + (int64_t)m * C + c);
     float4 lo = p[0], hi = p[1];
     for (int z = 1; z < ksplit; ++z) {
@@ -713,8 +717,9 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
       lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
       hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
     }
-    *reinterpret_cast<uint4*>(out + (int64_t)m * ld_out + c) =
-        make_uint4(E::pack2(lo.x, lo.y), E::pack2(lo.z, lo.w), E::pack2(hi.x, hi.y), E::pack2(hi.z, hi.w));
+    if (in_bounds((int64_t)m * ld_out + c, 8, (int64_t)M * ld_out))
+      *reinterpret_cast<uint4*>(out + (int64_t)m * ld_out + c) =
+          make_uint4(E::pack2(lo.x, lo.y), E::pack2(lo.z, lo.w), E::pack2(hi.x, hi.y), E::pack2(hi.z, hi.w));
   }
 }
 
@@ -740,6 +745,8 @@ hipError_t launch(GemmArgs a, hipStream_t st) {
 }
 
 }  // namespace
+
+QLORA_OOB_READER(oob_count_gemm)
 
 void take_gemm_events(hipEvent_t& start, hipEvent_t& stop) {
   start = t_ev_start;

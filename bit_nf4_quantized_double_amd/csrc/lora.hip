@@ -125,10 +125,11 @@ __global__ __launch_bounds__(256) void k_rowdot(RowdotArgs ra) {
 #pragma unroll
     for (int w = 1; w < 4; ++w) s += red[(w * 16 + m) * kRP + j];
     if (ra.part) {
-      ra.part[((int64_t)split * M + m) * r + j] = s;
+      if (in_bounds(((int64_t)split * M + m) * r + j, 1, (int64_t)ra.nsplit * M * r))
+        ra.part[((int64_t)split * M + m) * r + j] = s;
     } else {
       const uint32_t pk = E::pack2(ra.scale * s, 0.f);
-      ra.out[(int64_t)m * r + j] = (uint16_t)(pk & 0xFFFFu);
+      if (in_bounds((int64_t)m * r + j, 1, (int64_t)M * r)) ra.out[(int64_t)m * r + j] = (uint16_t)(pk & 0xFFFFu);
     }
   }
 }
@@ -140,6 +141,7 @@ template <typename E>
 __device__ __forceinline__ void rowdot_finalize_body(const float* __restrict__ part, int nsplit, int64_t n,
                                                      float scale, uint16_t* __restrict__ out, int b, int nb) {
   for (int64_t i = (int64_t)b * 256 + threadIdx.x; i < n; i += (int64_t)nb * 256) {
+    if (!in_bounds((int64_t)(nsplit - 1) * n + i, 1, (int64_t)nsplit * n)) continue;
     float s = part[i];
     int k = 1;
     for (; k + 8 <= nsplit; k += 8) {  // 8 loads in flight, added in split order
@@ -162,11 +164,13 @@ __global__ __launch_bounds__(256) void k_rowdot_finalize(const float* __restrict
 }
 
 __global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_t n) {
-  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    if (in_bounds(i, 1, n)) p[i] = 0.f;
 }
 
 __global__ __launch_bounds__(256) void k_zero_u16(uint16_t* __restrict__ p, int64_t n) {
-  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    if (in_bounds(i, 1, n)) p[i] = 0;
 }
 
 template <int RT, typename E>
@@ -201,6 +205,8 @@ hipError_t rowdot_dispatch(const uint16_t* in, int M, int Kd, const uint16_t* wt
 }
 
 }  // namespace
+
+QLORA_OOB_READER(oob_count_lora)
 
 // U~ = E(s sum over splits of part) for rowdot's nsplit partials [nsplit][M][r].
 hipError_t launch_rowdot_finalize(const float* part, int nsplit, int M, int r, float s, uint16_t* U, bool f16,

@@ -100,7 +100,8 @@ __global__ __launch_bounds__(256) void k_merge(const uint4* __restrict__ codes, 
   for (int idx = tid; idx < RP * (kTileK / 8); idx += 256) {
     const int j = idx / (kTileK / 8), kl = 8 * (idx % (kTileK / 8)), k = k0 + kl;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (j < r && k < K) v = *reinterpret_cast<const uint4*>(A + (int64_t)j * K + k);
+    if (j < r && k < K && in_bounds((int64_t)j * K + k, 8, (int64_t)r * K))
+      v = *reinterpret_cast<const uint4*>(A + (int64_t)j * K + k);
     const int p = kl >> 6, m = (kl & 63) >> 2;  // m even: the 8 columns are tiles m, m + 1
     uint16_t* d = sa + j * kAPitch + 16 * m + 4 * p;
     *reinterpret_cast<uint2*>(d) = make_uint2(v.x, v.y);
@@ -126,23 +127,27 @@ __global__ __launch_bounds__(256) void k_merge(const uint4* __restrict__ codes, 
   uint4 bf[NU];
   auto fetch = [&](int nb) {
     const int n = nb + row;
-    const bool ok = n < N && kok;
     const uint32_t e = (uint32_t)n * (uint32_t)K + (uint32_t)(k0 + kl);  // first weight of the block
+    const int64_t nw = (int64_t)N * K, nblk = nw / 64;
+    const bool ok = n < N && kok && in_bounds(e >> 5, 2, nw / 32) && in_bounds(e >> 6, 1, nblk) &&
+                    in_bounds(e >> 14, 1, (nblk + 255) / 256);
     cw[0] = ok ? codes[e >> 5] : make_uint4(0, 0, 0, 0);
     cw[1] = ok ? codes[(e >> 5) + 1] : make_uint4(0, 0, 0, 0);
     sc = ok ? block_scale(q8, s2, e >> 6) : 0.f;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int j = KD * u + RG * g;
+      const int64_t bi = (int64_t)n * r + j, bn = (int64_t)N * r;
       if (RG == 8) {
-        bf[u] = load8(B + (int64_t)n * r + j, r - j, n < N, vec);
+        bf[u] = load8(B + bi, r - j, n < N && in_bounds(bi, min(8, max(r - j, 0)), bn), vec);
       } else if ((r & 3) == 0) {  // 4 ranks of a row, 8-byte aligned
-        const uint2 v = (n < N && j < r) ? *reinterpret_cast<const uint2*>(B + (int64_t)n * r + j) : make_uint2(0, 0);
+        const uint2 v = (n < N && j < r && in_bounds(bi, 4, bn)) ? *reinterpret_cast<const uint2*>(B + bi)
+                                                                 : make_uint2(0, 0);
         bf[u] = make_uint4(v.x, v.y, 0u, 0u);
       } else {
         uint16_t h[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = (n < N && j + i < r) ? B[(int64_t)n * r + j + i] : (uint16_t)0;
+        for (int i = 0; i < 4; ++i) h[i] = (n < N && j + i < r && in_bounds(bi + i, 1, bn)) ? B[bi + i] : (uint16_t)0;
         bf[u] = make_uint4(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16, 0u, 0u);
       }
     }
@@ -217,7 +222,7 @@ __global__ __launch_bounds__(256) void k_merge(const uint4* __restrict__ codes, 
       const int rr = 2 * i + (lane >> 5), cl = 8 * (lane & 31);
       const uint4 v = *reinterpret_cast<const uint4*>(sw + rr * kOPitch + cl);
       typedef __attribute__((ext_vector_type(4))) unsigned v4u;
-      if (nb + rr < N && k0 + cl < K)
+      if (nb + rr < N && k0 + cl < K && in_bounds((int64_t)(nb + rr) * K + k0 + cl, 8, (int64_t)N * K))
         __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w},
                                     reinterpret_cast<v4u*>(out + (size_t)(nb + rr) * K + k0 + cl));
     }
@@ -226,6 +231,8 @@ __global__ __launch_bounds__(256) void k_merge(const uint4* __restrict__ codes, 
 }
 
 }  // namespace
+
+QLORA_OOB_READER(oob_count_merge)
 
 hipError_t launch_merge(const uint8_t* codes, const uint8_t* q8, const float* s2, int N, int K, const uint16_t* A,
                         const uint16_t* B, int r, float s, uint16_t* out, hipStream_t st) {

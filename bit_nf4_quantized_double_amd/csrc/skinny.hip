@@ -118,14 +118,18 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
 #pragma unroll
       for (int u = 0; u < kSkUpLoads; ++u) {
         const uint32_t i = (uint32_t)tid + (uint32_t)u * kSkThreads;
-        upv[u] = i < un / 4 ? *reinterpret_cast<const uint4*>(a.upart + 4 * i) : make_uint4(0, 0, 0, 0);
+        upv[u] = i < un / 4 && in_bounds(4 * (int64_t)i, 4, (int64_t)a.uns * a.M * a.r)
+                     ? *reinterpret_cast<const uint4*>(a.upart + 4 * i)
+                     : make_uint4(0, 0, 0, 0);
       }
     } else {
 #pragma unroll
       for (int u = 0; u < 4 * kSkUpLoads; ++u) {
         const uint32_t i = (uint32_t)tid + (uint32_t)u * kSkThreads;
         const uint32_t zm = i / (uint32_t)urp, j = i - zm * (uint32_t)urp;
-        ups[u] = i < un && j < (uint32_t)a.r ? a.upart[zm * (uint32_t)a.r + j] : 0.f;
+        ups[u] = i < un && j < (uint32_t)a.r && in_bounds((int64_t)zm * a.r + j, 1, (int64_t)a.uns * a.M * a.r)
+                     ? a.upart[zm * (uint32_t)a.r + j]
+                     : 0.f;
       }
     }
   }
@@ -343,23 +347,25 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
                         E::pack2(c * hi[2], c * hi[3]));
         if (a.Uout && blockIdx.x == 0 && wa == 0) {
           uint16_t* o = a.Uout + (int64_t)row * a.r + j;
+          const int64_t oi = (int64_t)row * a.r + j, on = (int64_t)a.M * a.r;
           if (vec) {
-            *reinterpret_cast<uint4*>(o) = uf;
+            if (in_bounds(oi, 8, on)) *reinterpret_cast<uint4*>(o) = uf;
           } else {
             const uint32_t w[4] = {uf.x, uf.y, uf.z, uf.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              if (j + e < a.r) o[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+              if (j + e < a.r && in_bounds(oi + e, 1, on)) o[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
           }
         }
       } else if (row < a.M && j < a.r) {
         const uint16_t* p = a.U + (int64_t)row * a.r + j;
+        const int64_t ui = (int64_t)row * a.r + j, un_ = (int64_t)a.M * a.r;
         if (vec) {
-          uf = *reinterpret_cast<const uint4*>(p);
+          if (in_bounds(ui, 8, un_)) uf = *reinterpret_cast<const uint4*>(p);
         } else {
           uint16_t v[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = j + e < a.r ? p[e] : (uint16_t)0;
+          for (int e = 0; e < 8; ++e) v[e] = j + e < a.r && in_bounds(ui + e, 1, un_) ? p[e] : (uint16_t)0;
           uf = make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16,
                           v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
         }
@@ -370,12 +376,13 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
         uint4 bf = make_uint4(0, 0, 0, 0);
         if (n < a.N && j < a.r) {
           const uint16_t* p = a.B + (int64_t)n * a.r + j;
+          const int64_t bi = (int64_t)n * a.r + j, bn_ = (int64_t)a.N * a.r;
           if (vec) {
-            bf = *reinterpret_cast<const uint4*>(p);
+            if (in_bounds(bi, 8, bn_)) bf = *reinterpret_cast<const uint4*>(p);
           } else {
             uint16_t v[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = j + e < a.r ? p[e] : (uint16_t)0;
+            for (int e = 0; e < 8; ++e) v[e] = j + e < a.r && in_bounds(bi + e, 1, bn_) ? p[e] : (uint16_t)0;
             bf = make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16,
                             v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
           }
@@ -405,12 +412,13 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
     const int m = l & 15;
     const int n = (blockIdx.x * a.tiles + tt) * 16 + 4 * (l >> 4);
     if (m < a.M && n < a.N && a.part) {  // this split's fp32 partial sums
-      *reinterpret_cast<float4*>(a.part + ((int64_t)kz * a.M + m) * a.N + n) = s;
+      if (in_bounds(((int64_t)kz * a.M + m) * a.N + n, 4, (int64_t)gridDim.y * a.M * a.N))
+        *reinterpret_cast<float4*>(a.part + ((int64_t)kz * a.M + m) * a.N + n) = s;
     } else if (m < a.M && n < a.N) {  // n_out % 8 == 0: the 4 rows are all in range
       uint2 o;
       o.x = E::pack2(s.x, s.y);
       o.y = E::pack2(s.z, s.w);
-      *reinterpret_cast<uint2*>(a.Y + (int64_t)m * a.N + n) = o;
+      if (in_bounds((int64_t)m * a.N + n, 4, (int64_t)a.M * a.N)) *reinterpret_cast<uint2*>(a.Y + (int64_t)m * a.N + n) = o;
     }
   }
 }
@@ -435,6 +443,8 @@ hipError_t sk_launch(const SkinnyArgs& a, dim3 grid, size_t lds, bool sl, hipStr
 }
 
 }  // namespace
+
+QLORA_OOB_READER(oob_count_skinny)
 
 // Largest M the few-token kernel handles.
 int skinny_max_tokens() { return 16; }

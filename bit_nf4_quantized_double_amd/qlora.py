@@ -10,6 +10,7 @@ bf16 tensors are passed as their raw bits (the ABI takes uint16_t).
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from dataclasses import dataclass
@@ -18,6 +19,9 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqlora.so")
+# the same library with every raw global access range checked (see
+# qlora_debug_oob_count in include/qlora.h)
+LIB_CHECKED_PATH = os.path.join(_HERE, "libqlora_checked.so")
 
 QLORA_OK = 0
 QLORA_OP_FWD = 1
@@ -36,16 +40,44 @@ class _CWeight(ctypes.Structure):
 
 
 _lib = None
+_loaded = {}
 
 
 def lib() -> ctypes.CDLL:
     """Load libqlora.so (once).  Raises if it has not been built."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is not built: run `python -m bit_nf4_quantized_double_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+    if _lib is None:
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+@contextlib.contextmanager
+def library(path: str):
+    """Route every call made inside the block through the library at `path`
+    (e.g. LIB_CHECKED_PATH); the previous one is restored afterwards."""
+    global _lib
+    prev = _lib
+    _lib = _load(path)
+    try:
+        yield _lib
+    finally:
+        _lib = prev
+
+
+def debug_oob_count(reset: bool = True) -> int:
+    """Out-of-range accesses the bounds-checked build skipped since the last
+    reset (qlora_debug_oob_count; raises in the normal build)."""
+    n = ctypes.c_uint64(0)
+    _check(lib().qlora_debug_oob_count(ctypes.byref(n), 1 if reset else 0), "qlora_debug_oob_count")
+    return int(n.value)
+
+
+def _load(path: str) -> ctypes.CDLL:
+    if path in _loaded:
+        return _loaded[path]
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m bit_nf4_quantized_double_amd.build`")
+    L = ctypes.CDLL(path)
     W = ctypes.POINTER(_CWeight)
     sig = {
         "qlora_quantize_nf4_dq": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
@@ -85,12 +117,13 @@ def lib() -> ctypes.CDLL:
         "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "qlora_last_error": (ctypes.c_char_p, []),
         "qlora_time_next_gemm": (None, [_vp, _vp]),
+        "qlora_debug_oob_count": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint64), ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = L
+    _loaded[path] = L
     return L
 
 

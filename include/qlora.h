@@ -326,6 +326,18 @@ int qlora_plan(int op, int64_t M, int64_t n_out, int64_t k_in, int compute_units
  * the setting is thread-local, so concurrent threads do not interfere. */
 void qlora_time_next_gemm(hipEvent_t start, hipEvent_t stop);
 
+/* Diagnostic of the bounds-checked build (libqlora_checked.so, compiled with
+ * QLORA_BOUNDS_CHECK; same entry points, same arithmetic).  There every raw
+ * global store, and every raw global load of caller-sized data, first checks
+ * its element index against the size of the buffer it addresses (as the
+ * layouts above define it); an access outside is skipped (a load reads
+ * zeros) and counted on the device.  Writes the number of such accesses
+ * since the last reset to *count (synchronising the device) and clears it
+ * when `reset` is nonzero.  Returns QLORA_OK; QLORA_ERR_INVALID_ARG for
+ * count == NULL or in the normal build, which has no checks; QLORA_ERR_HIP
+ * if the counters cannot be read. */
+int qlora_debug_oob_count(uint64_t *count, int reset);
+
 /* Host function: copies the 16 fp32 NF4 levels the kernels use into out[16]
  * (ascending; 7 negative, an exact 0, 8 positive, extremes -1 and +1: 16
  * levels at normal quantiles, [P1] "The mechanism in brief"). */

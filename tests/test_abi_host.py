@@ -46,6 +46,20 @@ def test_header_symbols_exported(L):
         assert hasattr(L, n), n
 
 
+def test_checked_build_exports_the_same_symbols(L):
+    """The bounds-checked twin library is built beside the normal one and has
+    the same entry points; the normal build reports that it has no counter
+    (without touching the device)."""
+    assert os.path.exists(qlora.LIB_CHECKED_PATH)
+    C = ctypes.CDLL(qlora.LIB_CHECKED_PATH)
+    for n in _declared_functions():
+        assert hasattr(C, n), n
+    n = ctypes.c_uint64(7)
+    assert L.qlora_debug_oob_count(ctypes.byref(n), 0) == INVALID
+    assert L.qlora_debug_oob_count(None, 0) == INVALID
+    assert n.value == 7
+
+
 def test_library_table_matches_oracle_bitwise(L):
     t = np.array(qlora.nf4_table(), dtype=np.float32)
     assert np.array_equal(t.view(np.uint32), oracle.nf4_table().view(np.uint32))
