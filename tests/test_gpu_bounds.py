@@ -160,3 +160,27 @@ def test_noalloc_forward_in_bounds(M, N, K, r):
     _same(ref[0], got[0], "Y")
     _same(ref[1], got[1], "U~")
     assert oob == 0
+
+
+def test_fewtoken_u_finalize_fallback_matches_staged():
+    """When the down projection's partials do not fit in LDS beside the
+    staged block scales (4 tokens, 5120 x 64512, rank 64: 32 KB of scales and
+    32 KB of partials), the few-token launcher rounds them with a finalize
+    pass first.  U~ depends only on X, A and the split of k_in, so a narrow
+    weight (1024 outputs: the kernel adds the staged partials itself) must
+    give the same U~ bit for bit; and the wide case runs in bounds."""
+    _need_gpu()
+    M, K, r, alpha = 4, 64512, 64, 128.0
+    X = _rand((M, K), 21)
+    A = _rand((r, K), 22, K ** -0.5)
+    outs = {}
+    for N in (1024, 5120):
+        w = qlora.quantize(_rand((N, K), 23 + N, 0.02, torch.float32))
+        B = _rand((N, r), 24, 0.01)
+        ref, got, oob = _both(lambda: qlora.linear_fwd(w, X, A, B, r, alpha))
+        _same(ref[0], got[0], f"Y ({N} outputs)")
+        _same(ref[1], got[1], f"U~ ({N} outputs)")
+        assert oob == 0
+        outs[N] = ref[1]
+        del w
+    _same(outs[1024], outs[5120], "U~ through the finalize pass against U~ formed in the kernel")
