@@ -169,6 +169,12 @@ def test_workspace_sizes(L):
     # few-token kernel over a long reduction: 4 splits of fp32 16 x 8192
     assert ws(1, 16, 8192, 28672, 0) == 4 * 16 * 8192 * 4
     assert ws(1, 4, 8192, 28672, 0) == 0  # under 8 tokens: unsplit
+    # few tokens with an adapter: U~, then the down projection's partials
+    # (112 sub-chunks of 256 in 28 splits of 4: at most 32 KB of partials),
+    # then the main product's split partials -- disjoint, since the few-token
+    # kernel reads the first while it writes the second
+    assert ws(1, 16, 8192, 28672, 16) == 16 * 16 * 2 + 28 * 16 * 16 * 4 + 4 * 16 * 8192 * 4
+    assert ws(1, 1, 8192, 28672, 16) == 256 + 28 * 1 * 16 * 4  # (U~ rounded up to 256 bytes; no split)
     assert ws(1, 16, 64, 64, 65) == 0
 
 
