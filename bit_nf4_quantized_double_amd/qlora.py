@@ -18,10 +18,11 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqlora.so")
 # the same library with every raw global access range checked (see
 # qlora_debug_oob_count in include/qlora.h)
 LIB_CHECKED_PATH = os.path.join(_HERE, "libqlora_checked.so")
+# QLORA_LIBRARY=checked runs everything through the bounds-checked build
+LIB_PATH = LIB_CHECKED_PATH if os.environ.get("QLORA_LIBRARY") == "checked" else os.path.join(_HERE, "libqlora.so")
 
 QLORA_OK = 0
 QLORA_OP_FWD = 1

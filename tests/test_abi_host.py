@@ -54,9 +54,11 @@ def test_checked_build_exports_the_same_symbols(L):
     C = ctypes.CDLL(qlora.LIB_CHECKED_PATH)
     for n in _declared_functions():
         assert hasattr(C, n), n
+    N = ctypes.CDLL(os.path.join(os.path.dirname(qlora.LIB_CHECKED_PATH), "libqlora.so"))
     n = ctypes.c_uint64(7)
-    assert L.qlora_debug_oob_count(ctypes.byref(n), 0) == INVALID
-    assert L.qlora_debug_oob_count(None, 0) == INVALID
+    N.qlora_debug_oob_count.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    assert N.qlora_debug_oob_count(ctypes.byref(n), 0) == INVALID
+    assert N.qlora_debug_oob_count(None, 0) == INVALID
     assert n.value == 7
 
 
