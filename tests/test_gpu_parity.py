@@ -872,6 +872,39 @@ def test_few_token_70b_sampled_columns(index, M):
     check_close(f64(Y)[:, cols], Yr, "Y sampled columns")
 
 
+def test_few_token_u_finalize_fallback_against_oracle():
+    """4 tokens on a 5120 x 64512 weight at rank 64: the down projection's
+    partials (32 KB) do not fit in LDS beside the staged block scales
+    (32 KB), so the launcher rounds them with a finalize pass before the
+    few-token kernel.  U~ in full and 64 sampled output columns of Y against
+    the oracle."""
+    _need_gpu()
+    M, N, K, r, alpha = 4, 5120, 64512, 64, 128.0
+    d = synth.linear_inputs(N, K, M, r, np.random.default_rng(64512), with_grad=False)
+    w = gpu_quantize(d["W"])
+    X, A, B = dev_bf16(d["X"]), dev_bf16(d["A"]), dev_bf16(d["B"])
+    Y, U = qlora.linear_fwd(w, X, A, B, r, alpha)
+    torch.cuda.synchronize()
+    del w
+    cols = np.sort(np.random.default_rng(5).choice(N, 64, replace=False))
+    flat = d["W"].ravel()
+    bpr = K // 64
+    Wrows = []
+    for n in cols:
+        b0 = n * bpr
+        groups = sorted(set(range(b0 // 256, (b0 + bpr - 1) // 256 + 1)))
+        part = oracle.quantize_groups(flat, groups)
+        codes = np.concatenate([part[g]["codes"] for g in groups])
+        q8 = np.concatenate([part[g]["absmax_q8"] for g in groups])
+        s2 = np.concatenate([part[g]["absmax_scale"] for g in groups])
+        gb0 = groups[0] * 256
+        _, wbr = oracle.dequant(codes, q8, s2, 1, codes.size * 2, first_block=gb0)
+        Wrows.append(wbr.ravel()[(b0 - gb0) * 64:(b0 - gb0 + bpr) * 64])
+    Yr, Ur = oracle.linear_fwd(np.stack(Wrows), d["X"], d["A"], d["B"][cols], alpha, r)
+    check_close(f64(Y)[:, cols], Yr, "Y sampled columns")
+    check_close(f64(U), oracle.lora_scale(alpha, r) * Ur, "U~")
+
+
 # ------------------------------------------------------ merge, re-quantize ----
 
 MERGE_SHAPES = [
