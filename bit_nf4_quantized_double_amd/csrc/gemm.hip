@@ -508,8 +508,28 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
     wait_vmcnt<0>();
   } else {
     constexpr int DA = ARing<NN>::kSteps;
+    const int mbp = tiled_mbp(a.M);
+    const __amdgpu_buffer_rsrc_t ract = make_rsrc(a.act_t, (uint32_t)tiled_bytes(a.M, a.R));
+    // byte offsets of this lane in the two fragment blocks of the wave's rows
+    const int mb0 = row0 >> 5;
+    uint32_t abase[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      abase[i] = mb0 + i < mbp ? (uint32_t)(mb0 + i) * (uint32_t)a.kbp * 1024u + 16u * (uint32_t)lane : kOOB;
+    auto load_a = [&](int step, int ks, uint4 (&dst)[2]) {
+      const bool ok = step < nloc;
+      const uint32_t kb = 4u * (uint32_t)(s0 + step) + (uint32_t)ks;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) dst[i] = buf_load16(ract, ok && abase[i] != kOOB ? abase[i] + kb * 1024u : kOOB);
+    };
+    AFrags ar[DA];  // A fragments of steps s .. s + DA - 1 (step s in ar[s % DA])
+    // step 0's fragments first, so that their loads and the adapter
+    // operand's are in flight together
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) load_a(0, ks, ar[0].f[ks]);
     // The adapter's token-side operand (U~ or V~) in MFMA A-operand layout,
-    // formed before the activation loads are issued (fewer live registers).
+    // formed before the later steps' activation loads are issued (fewer live
+    // registers).
     const int nks = (a.r + 15) >> 4;  // 16-rank sub-steps that hold ranks
     uint4 uf[4][2];
     if (adapter) {
@@ -527,23 +547,8 @@ __global__ __launch_bounds__(2 * kThreads) void k_gemm_nf4(GemmArgs a) {
           }
       }
     }
-    const int mbp = tiled_mbp(a.M);
-    const __amdgpu_buffer_rsrc_t ract = make_rsrc(a.act_t, (uint32_t)tiled_bytes(a.M, a.R));
-    // byte offsets of this lane in the two fragment blocks of the wave's rows
-    const int mb0 = row0 >> 5;
-    uint32_t abase[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      abase[i] = mb0 + i < mbp ? (uint32_t)(mb0 + i) * (uint32_t)a.kbp * 1024u + 16u * (uint32_t)lane : kOOB;
-    auto load_a = [&](int step, int ks, uint4 (&dst)[2]) {
-      const bool ok = step < nloc;
-      const uint32_t kb = 4u * (uint32_t)(s0 + step) + (uint32_t)ks;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) dst[i] = buf_load16(ract, ok && abase[i] != kOOB ? abase[i] + kb * 1024u : kOOB);
-    };
-    AFrags ar[DA];  // A fragments of steps s .. s + DA - 1 (step s in ar[s % DA])
-#pragma unroll
-    for (int d = 0; d < DA; ++d)
+    for (int d = 1; d < DA; ++d)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) load_a(d, ks, ar[d].f[ks]);
 
