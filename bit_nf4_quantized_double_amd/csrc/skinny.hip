@@ -12,7 +12,8 @@
 // 16 tokens on the other.
 //
 // Workgroup: 8 waves (two per SIMD, so up to 256 VGPRs per lane for deep
-// prefetch), `tiles` 16-row W tiles (a tile = 16 output features),
+// prefetch), or 16 (four per SIMD) when each wave holds 2 tiles of an unsplit
+// reduction at fewer than 8 tokens; `tiles` 16-row W tiles (a tile = 16 output features),
 // the whole reduction length.  Wave (a, b): tiles a*TPW .. a*TPW + TPW - 1
 // of the group, 128-wide reduction chunks b, b + nwk, b + 2 nwk, ...
 // Lane l: W row (l & 15) of a tile, reduction columns 32 (l >> 4) .. + 31 of
@@ -20,7 +21,8 @@
 // holds the other half and shares the block's lookup table.  The X fragment
 // of a chunk is loaded once and reused by all TPW tiles of the wave.  At the
 // end, the nwk partial tiles of each output tile are added in LDS in a fixed
-// order (deterministic); the b == 0 wave adds the adapter term first.
+// order (deterministic; with 16 waves after a pairwise fold); the b == 0 wave
+// adds the adapter term first.
 //
 // The reduction index is permuted consistently in both operands (lane group
 // g, dword i of a chunk <-> columns kc + 32 g + 8 i .. + 7, and inside each
@@ -41,11 +43,22 @@ hipError_t launch_rowdot_finalize(const float* part, int nsplit, int M, int r, f
 
 namespace {
 
-constexpr int kSkWaves = 8;
-constexpr int kSkThreads = 64 * kSkWaves;
-constexpr int kSkMaxStageLoads = 8;  // 16-byte staged-scale loads per thread: sbytes <= 60 KB
-constexpr int kSkUpLoads = 4;        // 16-byte staged U~-partial loads per thread: <= 32 KB
-constexpr int kSkUpBytes = kSkUpLoads * 16 * kSkThreads;
+// A workgroup has NW = 8 waves (two per SIMD, up to 256 VGPRs each), or 16
+// (four per SIMD, up to 128 VGPRs: at most 2 W tiles per wave) where a wave
+// has few tiles and a long reduction -- there more waves hide more load and
+// MFMA latency than the larger tile groups save.
+constexpr int kSkUpBytes = 32 * 1024;  // staged U~ partials
+template <int NW>
+struct SkGeom {
+  static_assert(NW == 8 || NW == 16, "8 or 16 waves per workgroup");
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int kStageLoads = 4096 / kThreads;  // 16-byte staged-scale loads per thread: sbytes <= 60 KB
+  static constexpr int kUpLoads = kSkUpBytes / 16 / kThreads;  // 16-byte staged U~-partial loads per thread
+  // The nwk partial tiles of an output tile meet in LDS after one pairwise
+  // fold (wave b + nwk / 2 into wave b) with 16 waves, so the reduction
+  // buffer stays at tiles * 8 / nwt KB <= 64 KB.
+  static constexpr int kFold = NW > 8 ? 1 : 0;
+};
 
 struct SkSeg {
   uint4 code;  // 32 codes
@@ -60,8 +73,12 @@ struct SkSrcs {
 // SL: the workgroup's block scales (absmax codes of its rows, and the
 // second-level scales they use) are staged in LDS once, with coalesced loads,
 // instead of two scattered small loads per 32 weights.
-template <int TPW, int RD, bool SL, typename E>
-__global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
+template <int TPW, int RD, bool SL, typename E, int NW>
+__global__ __launch_bounds__(64 * NW) void k_skinny_fwd(SkinnyArgs a) {
+  using G = SkGeom<NW>;
+  constexpr int kSkThreads = G::kThreads;
+  constexpr int kSkMaxStageLoads = G::kStageLoads;
+  constexpr int kSkUpLoads = G::kUpLoads;
   extern __shared__ __attribute__((aligned(16))) float4 s_dyn[];
   float4* const s_red = s_dyn;  // [tiles][nwk][64], used after the main loop
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -393,19 +410,37 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
   }
 
   // partial tiles -> LDS [tile][b][lane] (over the staged scales: wait for
-  // every wave to leave the main loop), then a fixed-order sum over b
+  // every wave to leave the main loop), then a fixed-order sum over b.
+  // With the fold, waves b >= nred first hand their tiles to wave b - nred,
+  // which adds them to its own: slot b then holds acc_b + acc_(b + nred).
+  constexpr int kFold = G::kFold;
+  const int red_log2 = a.nwk_log2 - kFold, nred = 1 << red_log2;
   __syncthreads();
+  if (!kFold || wb >= nred) {
+    const int slot = kFold ? wb - nred : wb;
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int tt = wa * TPW + t;
-    s_red[((tt << a.nwk_log2) + wb) * 64 + lane] = float4{acc[t][0], acc[t][1], acc[t][2], acc[t][3]};
+    for (int t = 0; t < TPW; ++t) {
+      const int tt = wa * TPW + t;
+      s_red[((tt << red_log2) + slot) * 64 + lane] = float4{acc[t][0], acc[t][1], acc[t][2], acc[t][3]};
+    }
+  }
+  if (kFold) {
+    __syncthreads();
+    if (wb < nred) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        float4* slot = s_red + (((wa * TPW + t) << red_log2) + wb) * 64 + lane;
+        const float4 v = *slot;
+        *slot = float4{acc[t][0] + v.x, acc[t][1] + v.y, acc[t][2] + v.z, acc[t][3] + v.w};
+      }
+    }
   }
   __syncthreads();
   for (int idx = tid; idx < a.tiles * 64; idx += kSkThreads) {
     const int tt = idx >> 6, l = idx & 63;
-    float4 s = s_red[(tt << a.nwk_log2) * 64 + l];
-    for (int b = 1; b < nwk; ++b) {
-      const float4 v = s_red[((tt << a.nwk_log2) + b) * 64 + l];
+    float4 s = s_red[(tt << red_log2) * 64 + l];
+    for (int b = 1; b < nred; ++b) {
+      const float4 v = s_red[((tt << red_log2) + b) * 64 + l];
       s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
     }
     // fragment element v of lane l: W row 4 (l >> 4) + v of the tile, token l & 15
@@ -423,18 +458,19 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_fwd(SkinnyArgs a) {
   }
 }
 
-template <int TPW, int RD>
+template <int TPW, int RD, int NW = 8>
 hipError_t sk_launch(const SkinnyArgs& a, dim3 grid, size_t lds, bool sl, hipStream_t st) {
+  constexpr int kSkThreads = SkGeom<NW>::kThreads;
   hipEvent_t ev0, ev1;
   take_gemm_events(ev0, ev1);
   hipError_t e;
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
   if (a.f16) {
-    if (sl) hipLaunchKernelGGL((k_skinny_fwd<TPW, RD, true, F16>), dim3(grid), dim3(kSkThreads), lds, st, a);
-    else hipLaunchKernelGGL((k_skinny_fwd<TPW, RD, false, F16>), dim3(grid), dim3(kSkThreads), lds, st, a);
+    if (sl) hipLaunchKernelGGL((k_skinny_fwd<TPW, RD, true, F16, NW>), dim3(grid), dim3(kSkThreads), lds, st, a);
+    else hipLaunchKernelGGL((k_skinny_fwd<TPW, RD, false, F16, NW>), dim3(grid), dim3(kSkThreads), lds, st, a);
   } else {
-    if (sl) hipLaunchKernelGGL((k_skinny_fwd<TPW, RD, true, Bf16>), dim3(grid), dim3(kSkThreads), lds, st, a);
-    else hipLaunchKernelGGL((k_skinny_fwd<TPW, RD, false, Bf16>), dim3(grid), dim3(kSkThreads), lds, st, a);
+    if (sl) hipLaunchKernelGGL((k_skinny_fwd<TPW, RD, true, Bf16, NW>), dim3(grid), dim3(kSkThreads), lds, st, a);
+    else hipLaunchKernelGGL((k_skinny_fwd<TPW, RD, false, Bf16, NW>), dim3(grid), dim3(kSkThreads), lds, st, a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.part && (e = launch_splitk_reduce(a.part, (int)grid.y, a.M, a.N, a.Y, a.N, a.f16, st)) != hipSuccess) return e;
@@ -491,13 +527,19 @@ hipError_t launch_skinny_fwd(SkinnyArgs a, hipStream_t st) {
   const int tpg = ks > 1 ? 8 : std::max(1, (ntiles + num_cu - 1) / num_cu);
   int tpw = std::min(tpg, 8);
   int nwt = 1;
-  while (nwt * tpw < tpg && nwt < kSkWaves) nwt *= 2;
+  while (nwt * tpw < tpg && nwt < 8) nwt *= 2;
   tpw = std::min(8, (tpg + nwt - 1) / nwt);
+  // 16 waves when a wave holds 2 tiles of an unsplit reduction and X is
+  // short (fewer than 8 tokens): measured 3-4 % faster on a 8192 x 28672
+  // weight at 1 and 4 tokens; with 1 tile per wave, or 16 tokens, no gain
+  const bool w16 = ks == 1 && tpw == 2 && a.M < 8;
+  const int nw = w16 ? 16 : 8;
   int nwk_log2 = 0;
-  while ((nwt << (nwk_log2 + 1)) <= kSkWaves) ++nwk_log2;
+  while ((nwt << (nwk_log2 + 1)) <= nw) ++nwk_log2;
   const int nwk = 1 << nwk_log2;
   int nci = (a.kchunks + nwk - 1) / nwk;
-  int rd = tpw >= 5 ? 1 : (tpw >= 3 ? 2 : (tpw == 2 ? 4 : 8));
+  // prefetch depth; with 16 waves (128 VGPRs) 2 chunks
+  int rd = tpw >= 5 ? 1 : (tpw >= 3 ? 2 : (tpw == 2 ? (w16 ? 2 : 4) : 8));
   while (rd > 2 && nci % rd) rd /= 2;
   const int unroll = std::max(rd, 2);
   nci = (nci + unroll - 1) / unroll * unroll;  // padding chunks read nothing and add zeros
@@ -505,7 +547,7 @@ hipError_t launch_skinny_fwd(SkinnyArgs a, hipStream_t st) {
   a.nwk_log2 = nwk_log2;
   a.nci = nci;
   const dim3 grid((ntiles + a.tiles - 1) / a.tiles, ks);
-  const size_t red = (size_t)a.tiles * nwk * 64 * sizeof(float4);
+  const size_t red = (size_t)a.tiles * (nwk >> (w16 ? SkGeom<16>::kFold : 0)) * 64 * sizeof(float4);
   // staged scales: q8 of 16 * tiles rows (the blocks of one split's chunks
   // when the reduction is split; the first split has the most), plus the
   // s2 groups the rows span
@@ -518,7 +560,7 @@ hipError_t launch_skinny_fwd(SkinnyArgs a, hipStream_t st) {
   const size_t sbytes = qbytes + qpad + 4 * ngs;
   // within the default 64 KB of dynamic LDS (so the whole-row copy takes at
   // most kSkMaxStageLoads 16-byte pieces per thread), one thread per s2 group
-  const bool sl = a.K >= 64 && sbytes <= 60 * 1024 && ngs <= (size_t)kSkThreads;
+  const bool sl = a.K >= 64 && sbytes <= 60 * 1024 && ngs <= (size_t)(64 * nw);
   size_t lds = std::max(red, sl ? sbytes : (size_t)0);
   if (a.upart) {
     // the U~ partials go after the staged scales; when they do not fit, a
@@ -536,6 +578,12 @@ hipError_t launch_skinny_fwd(SkinnyArgs a, hipStream_t st) {
     } else {
       a.uoff = (int)uoff;
       lds = std::max(lds, uoff + ubytes);
+    }
+  }
+  if (w16) {
+    switch (tpw * 16 + rd) {
+      case 2 * 16 + 2: return sk_launch<2, 2, 16>(a, grid, lds, sl, st);
+      default: return hipErrorInvalidValue;
     }
   }
   switch (tpw * 16 + rd) {

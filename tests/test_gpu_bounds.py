@@ -113,6 +113,7 @@ LINEAR_CASES = [
     (3, 136, 192, 5, torch.bfloat16, 0.0, False),      # few-token, ragged, U~ recomputed
     (7, 520, 768, 3, torch.float16, 0.0, True),
     (8, 1024, 4096, 16, torch.bfloat16, 0.0, False),   # few-token with a reduction split
+    (5, 4104, 1088, 17, torch.float16, 0.0, False),    # few-token with 16 waves, ragged, U~ recomputed
     (16, 1024, 8192, 40, torch.bfloat16, 0.05, True),  # more than 32 ranks, dropout
     (16, 8, 64, 0, torch.bfloat16, 0.0, True),         # no adapter, one tile
     (17, 136, 192, 5, torch.bfloat16, 0.0, False),     # GEMM path, ragged, U~ recomputed

@@ -253,6 +253,7 @@ F16_SHAPES = [
     (16, 4104, 320, 64, 128.0),   # few-token kernel, partial tile
     (130, 1024, 2048, 16, 32.0),  # split reduction in both products
     (16, 8192, 8192, 16, 32.0),   # few-token split across workgroups; dX split 4 ways
+    (3, 4104, 1088, 16, 32.0),    # few-token kernel with 16 waves
 ]
 
 
@@ -434,6 +435,7 @@ FEW_SHAPES = [
     (9, 1032, 960, 1, 2.0),
     (16, 8192, 8192, 16, 32.0),   # reduction split 4 ways across workgroups (8 tiles each)
     (9, 8192, 8256, 17, 34.0),    # split 17 + 17 + 17 + 14 chunks, half a chunk at the end
+    (6, 5000, 1088, 17, 34.0),    # 16 waves, 2 tiles each; most waves hold only padding chunks
 ]
 
 
