@@ -153,6 +153,7 @@ int dropout_setup(int32_t r, float alpha, double p, uint64_t seed, qlora::DropMa
 
 struct BwdLayout {
   size_t u, v, dyt, part, total;  // part: row-pass partials of V~ (and of U~ when it is recomputed)
+  size_t mask;  // keep-mask bits of X (M x k_in / 8 bytes) for the column pass under dropout
   size_t req;   // bytes required (U~, V~, the tiled dY and the partials)
   size_t gemm;  // offset of the dX product's split-reduction tiles (optional room past req)
 };
@@ -176,7 +177,8 @@ BwdLayout bwd_layout(int64_t M, int64_t n_out, int64_t k_in, int32_t r) {
     const size_t ure = M <= qlora::skinny_max_tokens() ? qlora::rowdot_part_bytes(M, k_in, r)
                                                        : qlora::rowpass_part_bytes(M, k_in, r, cus);
     const size_t part = std::max(ure, qlora::rowpass_part_bytes(M, n_out, r, cus));
-    L.req = L.part + round_up(part);
+    L.mask = L.part + round_up(part);
+    L.req = L.mask + round_up((size_t)M * (size_t)(k_in / 32) * 4u);
   }
   // the dX product reads the V~ partials while it runs: its split tiles go
   // after them; they need not fit (without room the product runs unsplit)
@@ -480,10 +482,12 @@ static int linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const u
   uint16_t* Ut = nullptr;
   uint16_t* Vt = nullptr;
   float* part = nullptr;
+  uint32_t* mbits = nullptr;
   uint16_t* dYt = reinterpret_cast<uint16_t*>(base + L.dyt);
   if (r > 0) {
     Vt = reinterpret_cast<uint16_t*>(base + L.v);
     part = reinterpret_cast<float*>(base + L.part);
+    if (dm.thr) mbits = reinterpret_cast<uint32_t*>(base + L.mask);
     if (U) {
       Ut = const_cast<uint16_t*>(U);
     } else {
@@ -503,8 +507,10 @@ static int linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const u
     }
     // one row pass over dY: the tiled dY the dX product reads and the V~
     // partial sums, added up (and V~ stored) in the dX product's prologue
+    // (under dropout it also writes the keep mask of X as bits for the
+    // column pass, which then need not regenerate it)
     if ((e = qlora::launch_rowpass(dY, (int)M, (int)N, B, r, false, qlora::DropMask{}, part, dYt, f16, cus,
-                                   stream)) != hipSuccess)
+                                   stream, mbits, (int)K, dm)) != hipSuccess)
       return hip_fail(e, "row pass launch");
   } else if ((e = qlora::launch_tile_act(dY, (int)M, (int)N, false, dYt, stream)) != hipSuccess) {
     return hip_fail(e, "tile dY launch");
@@ -524,8 +530,8 @@ static int linear_bwd_impl(const qlora_nf4_weight* w, const uint16_t* X, const u
   e = qlora::launch_gemm_dx(g, stream);
   if (e != hipSuccess) return hip_fail(e, "dX GEMM launch");
   // dA = V~^T (mask * X) [r x K] and dB = dY^T U~ [N x r], over all tokens
-  if (r > 0 && (e = qlora::launch_colpass(X, (int)K, Vt, dY, (int)N, Ut, (int)M, r, dm, dA, dB, f16, stream)) !=
-                   hipSuccess)
+  if (r > 0 && (e = qlora::launch_colpass(X, (int)K, Vt, dY, (int)N, Ut, (int)M, r, dm, dA, dB, f16, stream,
+                                          mbits)) != hipSuccess)
     return hip_fail(e, "dA / dB launch");
   return QLORA_OK;
 }

@@ -63,6 +63,13 @@ struct RowpassArgs {
   int kbp;
   bool eo;             // the copy in the forward's element order
   DropMask drop;       // dropout of `in` in the product (CONTIG only; thr 0: none)
+  // Keep-mask bits of the [M x mK] adapter input (mdrop, the backward's
+  // dropout) written by the pass over dY for the column pass: word w of row
+  // m holds elements 32 w .. 32 w + 31 (bit b = element 32 w + b).  This
+  // workgroup writes its rows' words [z wps, (z + 1) wps); null: none.
+  uint32_t* mbits;
+  int mwords;          // mK / 32
+  DropMask mdrop;
 };
 
 // 8 consecutive 16-bit elements at element e of a buffer, the first `valid`
@@ -102,7 +109,7 @@ struct RowpassWaves {
 // stores those to the tiled copy (1 KB contiguous each), stages the chunk of
 // w in LDS and runs 8 MFMAs per 32 ranks.  The waves' sums are added in wave
 // order at the end.
-template <bool CONTIG, int RT2, typename E>
+template <bool CONTIG, int RT2, typename E, bool MK = false>
 __global__ __launch_bounds__(64 * RowpassWaves<RT2>::n) void k_rowpass(RowpassArgs a) {
   constexpr int NW = RowpassWaves<RT2>::n;
   constexpr int kRanks = 32 * RT2;
@@ -160,6 +167,25 @@ __global__ __launch_bounds__(64 * RowpassWaves<RT2>::n) void k_rowpass(RowpassAr
   // flight while the chunk is stored and multiplied.
   uint4 xv[8], wv[kLoads];
   if (c_lo + wave < c_hi) load(c_lo + wave, xv, wv);
+  if (MK) {
+    // the keep-mask words, while the first chunk's loads are in flight: 32
+    // bits from 8 generator blocks per word (dropout.h)
+    const int wps = (a.mwords + a.S - 1) / a.S, w0 = z * wps, nw = max(0, min(wps, a.mwords - w0));
+    for (int it = tid; it < 32 * nw; it += 64 * NW) {
+      const int rl = it / nw, w = w0 + (it - rl * nw), m = m0 + rl;
+      if (m >= a.M) continue;
+      const uint64_t q0 = ((uint64_t)m * (uint64_t)a.mwords * 32u + 32u * (uint64_t)w) >> 2;
+      uint32_t bits = 0;
+#pragma unroll 2
+      for (int i = 0; i < 8; ++i) {
+        const uint64_t q = q0 + (uint64_t)i;
+        const uint4 u = philox4x32_10(make_uint4((uint32_t)q, (uint32_t)(q >> 32), 0u, 0u), a.mdrop.k0, a.mdrop.k1);
+        bits |= ((u.x >= a.mdrop.thr ? 1u : 0u) | (u.y >= a.mdrop.thr ? 2u : 0u) | (u.z >= a.mdrop.thr ? 4u : 0u) |
+                 (u.w >= a.mdrop.thr ? 8u : 0u)) << (4 * i);
+      }
+      if (in_bounds((int64_t)m * a.mwords + w, 1, (int64_t)a.M * a.mwords)) a.mbits[(size_t)m * a.mwords + w] = bits;
+    }
+  }
   for (int c = c_lo + wave; c < c_hi; c += NW) {
     const int k0 = 128 * c;
 #pragma unroll
@@ -239,6 +265,7 @@ struct ColpassJob {
   bool trans;
   DropMask drop;       // dropout of `in` (dA only)
   int nblk;            // 64-column blocks
+  const uint32_t* mbits;  // the keep mask of `in` as bits (see RowpassArgs), or null: from drop
 };
 
 // Workgroup = one 64-column block of one job, all M rows: 8 waves take
@@ -248,7 +275,7 @@ struct ColpassJob {
 // in wave order at the end.  Once a chunk is in LDS the next one's loads are
 // issued into the same registers, so they are in flight while the chunk is
 // multiplied.
-template <int RT2, typename E>
+template <int RT2, typename E, bool MB = false>
 __global__ __launch_bounds__(512) void k_colpass(ColpassJob j0, ColpassJob j1, int M, int r) {
   constexpr int kRanks = 32 * RT2;
   constexpr int kXP = 64 + 8, kVP = kRanks + 8;                 // LDS pitches
@@ -277,13 +304,17 @@ __global__ __launch_bounds__(512) void k_colpass(ColpassJob j0, ColpassJob j1, i
   constexpr int kVL = kRanks / 8;  // 16-byte loads per lane of a 64-row chunk of v
   // in[m0 .. m0 + 63][c0 .. c0 + 63] (8 lanes per 128-byte row) and
   // v[m0 .. m0 + 63][0 .. r) (ranks past r zero)
-  auto load = [&](int ck, uint4 (&xv)[8], uint4 (&vv)[kVL]) {
+  // MB: the dA job's mask from the row pass's bits (a separate instantiation)
+  const bool mb = MB && jb.drop.thr != 0 && jb.mbits != nullptr;
+  const __amdgpu_buffer_rsrc_t rmb = make_rsrc(jb.mbits, mb ? (uint32_t)((uint64_t)M * (jb.C >> 5) * 4) : 0u);
+  auto load = [&](int ck, uint4 (&xv)[8], uint4 (&vv)[kVL], uint32_t (&mv)[8]) {
     const int m0 = 64 * ck;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int idx = lane + 64 * u, rr = idx >> 3, cc = idx & 7;
       const int m = m0 + rr, c = c0 + 8 * cc;
       xv[u] = buf_load16(rin, m < M && c < jb.C ? ((uint32_t)m * (uint32_t)jb.C + (uint32_t)c) * 2u : kOOB);
+      if (mb) mv[u] = buf_load4(rmb, m < M && c < jb.C ? ((uint32_t)m * (uint32_t)(jb.C >> 5) + (uint32_t)(c >> 5)) * 4u : kOOB);
     }
 #pragma unroll
     for (int u = 0; u < kVL; ++u) {
@@ -297,10 +328,22 @@ __global__ __launch_bounds__(512) void k_colpass(ColpassJob j0, ColpassJob j1, i
   // while the chunk is multiplied.
   const int nck = (M + 63) >> 6;
   uint4 xv[8], vv[kVL];
-  if (wave < nck) load(wave, xv, vv);
+  uint32_t mv[8];
+  if (wave < nck) load(wave, xv, vv, mv);
   for (int ck = wave; ck < nck; ck += 8) {
     const int m0 = 64 * ck;
-    if (jb.drop.thr) {
+    if (mb) {
+      // 8 bits of the row's mask word per 8 elements (c is a multiple of 8)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int cc = (lane + 64 * u) & 7;
+        const uint32_t k8 = mv[u] >> ((8 * cc + c0) & 31);
+        auto keep2 = [&](uint32_t w, int b) {
+          return ((k8 >> b) & 1u ? (w & 0x0000FFFFu) : 0u) | ((k8 >> (b + 1)) & 1u ? (w & 0xFFFF0000u) : 0u);
+        };
+        xv[u] = make_uint4(keep2(xv[u].x, 0), keep2(xv[u].y, 2), keep2(xv[u].z, 4), keep2(xv[u].w, 6));
+      }
+    } else if (jb.drop.thr) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int idx = lane + 64 * u, rr = idx >> 3, cc = idx & 7;
@@ -317,7 +360,7 @@ __global__ __launch_bounds__(512) void k_colpass(ColpassJob j0, ColpassJob j1, i
       const int idx = lane + 64 * u;
       *reinterpret_cast<uint4*>(sv + (idx / (kRanks / 8)) * kVP + 8 * (idx % (kRanks / 8))) = vv[u];
     }
-    if (ck + 8 < nck) load(ck + 8, xv, vv);
+    if (ck + 8 < nck) load(ck + 8, xv, vv, mv);
     // LDS operations of one wave complete in order: the reads below see the
     // stores above, and the next chunk's stores come after these reads
     __builtin_amdgcn_wave_barrier();
@@ -378,6 +421,12 @@ __global__ __launch_bounds__(256) void k_rowpass_finalize(const float* __restric
 
 template <bool CONTIG, typename E>
 hipError_t rowpass_dispatch(const RowpassArgs& ra, dim3 grid, hipStream_t st) {
+  // the keep-mask bits only from the pass over dY (a separate instantiation)
+  if (!CONTIG && ra.mbits) {
+    if (ra.r <= 32) hipLaunchKernelGGL((k_rowpass<false, 1, E, true>), grid, dim3(64 * RowpassWaves<1>::n), 0, st, ra);
+    else hipLaunchKernelGGL((k_rowpass<false, 2, E, true>), grid, dim3(64 * RowpassWaves<2>::n), 0, st, ra);
+    return hipGetLastError();
+  }
   if (ra.r <= 32) hipLaunchKernelGGL((k_rowpass<CONTIG, 1, E>), grid, dim3(64 * RowpassWaves<1>::n), 0, st, ra);
   else hipLaunchKernelGGL((k_rowpass<CONTIG, 2, E>), grid, dim3(64 * RowpassWaves<2>::n), 0, st, ra);
   return hipGetLastError();
@@ -390,10 +439,12 @@ hipError_t rowpass_dispatch(const RowpassArgs& ra, dim3 grid, hipStream_t st) {
 // copy in the forward's element order); else w = B [R x r] (dY B, natural
 // order).  part: fp32 [S][M][rank_pitch(r)], S = rowpass_plan(M, R, cus).S.
 hipError_t launch_rowpass(const uint16_t* act, int M, int R, const uint16_t* w, int r, bool contig, DropMask drop,
-                          float* part, uint16_t* tiled, bool f16, int cus, hipStream_t st) {
+                          float* part, uint16_t* tiled, bool f16, int cus, hipStream_t st, uint32_t* mbits,
+                          int mK, DropMask mdrop) {
   if (M <= 0 || r <= 0) return hipSuccess;
   const RowpassPlan p = rowpass_plan(M, R, cus);
-  RowpassArgs ra{act, M, R, w, r, p.S, p.cps, part, rank_pitch(r), tiled, tiled_kbp(R), contig, drop};
+  RowpassArgs ra{act, M, R, w, r, p.S, p.cps, part, rank_pitch(r), tiled, tiled_kbp(R), contig, drop,
+                 mdrop.thr ? mbits : nullptr, mK / 32, mdrop};
   const dim3 grid(tiled_mbp(M), p.S);
   if (contig) return f16 ? rowpass_dispatch<true, F16>(ra, grid, st) : rowpass_dispatch<true, Bf16>(ra, grid, st);
   ra.drop = DropMask{};
@@ -415,12 +466,20 @@ hipError_t launch_rowpass_finalize(const float* part, int S, int M, int r, float
 // tokens, one dispatch.
 hipError_t launch_colpass(const uint16_t* X, int K, const uint16_t* Vt, const uint16_t* dY, int N,
                           const uint16_t* Ut, int M, int r, DropMask drop, float* dA, float* dB, bool f16,
-                          hipStream_t st) {
-  const ColpassJob ja{X, K, Vt, dA, false, drop, (K + 63) / 64};
-  const ColpassJob jb{dY, N, Ut, dB, true, DropMask{}, (N + 63) / 64};
+                          hipStream_t st, const uint32_t* mbits) {
+  const ColpassJob ja{X, K, Vt, dA, false, drop, (K + 63) / 64, drop.thr ? mbits : nullptr};
+  const ColpassJob jb{dY, N, Ut, dB, true, DropMask{}, (N + 63) / 64, nullptr};
   const dim3 grid(ja.nblk + jb.nblk);
   if (grid.x == 0) return hipSuccess;
-  if (r <= 32) {
+  if (ja.mbits) {
+    if (r <= 32) {
+      if (f16) hipLaunchKernelGGL((k_colpass<1, F16, true>), grid, dim3(512), 0, st, ja, jb, M, r);
+      else hipLaunchKernelGGL((k_colpass<1, Bf16, true>), grid, dim3(512), 0, st, ja, jb, M, r);
+    } else {
+      if (f16) hipLaunchKernelGGL((k_colpass<2, F16, true>), grid, dim3(512), 0, st, ja, jb, M, r);
+      else hipLaunchKernelGGL((k_colpass<2, Bf16, true>), grid, dim3(512), 0, st, ja, jb, M, r);
+    }
+  } else if (r <= 32) {
     if (f16) hipLaunchKernelGGL((k_colpass<1, F16>), grid, dim3(512), 0, st, ja, jb, M, r);
     else hipLaunchKernelGGL((k_colpass<1, Bf16>), grid, dim3(512), 0, st, ja, jb, M, r);
   } else {

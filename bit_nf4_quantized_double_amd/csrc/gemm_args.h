@@ -92,8 +92,12 @@ size_t rowpass_part_bytes(int64_t M, int64_t R, int r, int cus);
 // contig: w(j, k) = A[j][k] (A [r x R]; the forward's X A^T, act' = the
 // dropout mask times X, the tiled copy in the forward's element order);
 // else w(j, k) = B[k][j] (B [R x r]; dY B, natural order, no mask).
+// mbits (with mdrop.thr != 0): the pass also writes the keep mask mdrop of
+// an [M x mK] adapter input as bits, word w of row m = elements 32 w ..
+// 32 w + 31 (mK % 32 == 0; M * mK / 8 bytes), for the column pass.
 hipError_t launch_rowpass(const uint16_t* act, int M, int R, const uint16_t* w, int r, bool contig, DropMask drop,
-                          float* part, uint16_t* tiled, bool f16, int cus, hipStream_t st);
+                          float* part, uint16_t* tiled, bool f16, int cus, hipStream_t st, uint32_t* mbits = nullptr,
+                          int mK = 0, DropMask mdrop = DropMask{});
 
 // U = E(scale * sum over z, in order, of part[z][m][j]) [M x r]: the U~ the
 // forward GEMM forms from the same partials, bit for bit.
@@ -101,10 +105,11 @@ hipError_t launch_rowpass_finalize(const float* part, int S, int M, int r, float
                                    hipStream_t st);
 
 // Column pass over all M tokens, one dispatch, fixed summation order:
-// dA = V~^T (mask * X) [r x K] and dB = dY^T U~ stored [N x r], fp32.
+// dA = V~^T (mask * X) [r x K] and dB = dY^T U~ stored [N x r], fp32.  The
+// mask comes from mbits (the row pass's bits) when set, else from drop.
 hipError_t launch_colpass(const uint16_t* X, int K, const uint16_t* Vt, const uint16_t* dY, int N,
                           const uint16_t* Ut, int M, int r, DropMask drop, float* dA, float* dB, bool f16,
-                          hipStream_t st);
+                          hipStream_t st, const uint32_t* mbits = nullptr);
 
 // The fragment-tiled copy of act[M][R] (row pitch R elements, R % 8 == 0)
 // alone, for products whose adapter kernels do not run (r == 0); eo: the

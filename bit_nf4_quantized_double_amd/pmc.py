@@ -32,11 +32,11 @@ KERNELS = {
     "gemm_dx_7b": ("k_gemm_nf4<true, qlora::Bf16>", ["gemm.hip", "gemm_args.h", "nf4_lut.h", "common.h",
                                                     "dropout.h"]),
     # the adapter passes of the same layer steps
-    "rowpass_x_7b": ("k_rowpass<true, 1, qlora::Bf16>", ["adapter.hip", "gemm_args.h", "nf4_lut.h", "common.h",
+    "rowpass_x_7b": ("k_rowpass<true, 1, qlora::Bf16, false>", ["adapter.hip", "gemm_args.h", "nf4_lut.h", "common.h",
                                                          "dropout.h"]),
-    "rowpass_dy_7b": ("k_rowpass<false, 1, qlora::Bf16>", ["adapter.hip", "gemm_args.h", "nf4_lut.h", "common.h",
+    "rowpass_dy_7b": ("k_rowpass<false, 1, qlora::Bf16, false>", ["adapter.hip", "gemm_args.h", "nf4_lut.h", "common.h",
                                                            "dropout.h"]),
-    "colpass_7b": ("k_colpass<1, qlora::Bf16>", ["adapter.hip", "gemm_args.h", "nf4_lut.h", "common.h",
+    "colpass_7b": ("k_colpass<1, qlora::Bf16, false>", ["adapter.hip", "gemm_args.h", "nf4_lut.h", "common.h",
                                                  "dropout.h"]),
 }
 COPY_KERNEL = "neg_kernel"  # torch.neg over PMC_COPY_BYTES of fp32 (bench.py --pmc-pass)

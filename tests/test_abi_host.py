@@ -155,11 +155,12 @@ def test_workspace_sizes(L):
     # 32 chunks of 128 (64 row blocks x 4 splits fill the 256 compute units
     # a host without a GPU assumes)
     assert ws(1, 2048, 4096, 4096, 16) == _tiled(2048, 4096) + 4 * 2048 * 16 * 4
-    # backward: U~ and V~ slots, the tiled dY, and one region for the larger
+    # backward: U~ and V~ slots, the tiled dY, one region for the larger
     # of the row-pass partials of a U~ recompute (4 splits over k_in) and of
-    # V~ (4 splits over n_out)
+    # V~ (4 splits over n_out), and the keep mask of X as bits (one bit per
+    # element of the 2048 x 4096 adapter input, used under dropout)
     b = ws(2, 2048, 11008, 4096, 16)
-    assert b == 2 * 2048 * 16 * 2 + _tiled(2048, 11008) + 4 * 2048 * 16 * 4
+    assert b == 2 * 2048 * 16 * 2 + _tiled(2048, 11008) + 4 * 2048 * 16 * 4 + 2048 * 4096 // 8
     assert ws(2, 2048, 4096, 4096, 0) == _tiled(2048, 4096)  # the tiled dY only
     assert ws(9, 1, 1, 64, 1) == 0
     # few output tiles: optional room for a reduction split, also with r = 0
